@@ -1,0 +1,81 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds no attention arithmetic: it only draws Gaussian tensors from a
+CPU ``torch.Generator`` so that the GPU path and the fp64 oracle see identical
+bytes.  The shapes are those of the workloads the Sparse Transformer pages
+describe: 12,288-long byte / pixel sequences (64x64x3 images, enwik8 contexts)
+and 65,536-sample audio.  The values are i.i.d. N(0, 1) stand-ins for the
+projected activations; the datasets themselves are not used.
+
+Recipe (identical on every machine): ``torch.Generator().manual_seed(seed)``,
+draws in the order q, k, v, dO, each ``randn(B, H, T, D)`` in fp32, multiplied
+by ``scale`` and then rounded to the compute dtype (round-to-nearest-even for
+bf16).  The oracle receives these stored values widened exactly to fp64.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+STRIDED, FIXED, FIXED_R1, DENSE = 0, 1, 2, 3
+PATTERN_NAMES = {STRIDED: "strided", FIXED: "fixed", FIXED_R1: "fixed_r1", DENSE: "dense"}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention problem: pattern, shapes, dtype and the passes it runs."""
+
+    name: str
+    pattern: int
+    B: int
+    H: int
+    T: int
+    D: int
+    l: int
+    c: int
+    dtype: str  # "bf16" or "f32"
+    backward: bool
+    seed: int
+    scale: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+# The five workloads of the hot path.  Seeds are 1000 + position.
+WORKLOADS = [
+    Workload("strided_T256_f32_fwd", STRIDED, 1, 2, 256, 32, 16, 0, "f32", False, 1000,
+             note="head0 = previous 16 positions, head1 = every 16th earlier position"),
+    Workload("fixed_T1024_bf16_fwd", FIXED, 2, 4, 1024, 64, 32, 4, "bf16", False, 1001, 0.5,
+             note="c = 4 summary positions at the end of each 32-block, alternating heads"),
+    Workload("strided_T12288_bf16_fwd", STRIDED, 1, 16, 12288, 64, 128, 0, "bf16", False, 1002,
+             note="64x64x3 pixel-order sequence, 8 local + 8 strided heads"),
+    Workload("fixed_T12288_bf16_fwdbwd", FIXED, 4, 8, 12288, 64, 128, 8, "bf16", True, 1003,
+             note="enwik8-length context, c = 8, forward + recompute backward"),
+    Workload("strided_T65536_bf16_fwdbwd", STRIDED, 1, 8, 65536, 64, 256, 0, "bf16", True, 1004,
+             note="audio-length sequence, 4 local + 4 strided heads"),
+]
+WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def draw(B: int, H: int, T: int, D: int, *, dtype: torch.dtype, seed: int,
+         scale: float = 1.0, n: int = 3) -> list[torch.Tensor]:
+    """Return ``n`` CPU tensors [B, H, T, D] (q, k, v[, dO]) drawn from ``seed``."""
+    g = torch.Generator().manual_seed(int(seed))
+    out = []
+    for _ in range(n):
+        x = torch.randn(B, H, T, D, generator=g, dtype=torch.float32)
+        if scale != 1.0:
+            x = x * scale
+        out.append(x.to(dtype).contiguous())
+    return out
+
+
+def draw_workload(w: Workload, *, n: int | None = None) -> list[torch.Tensor]:
+    """q, k, v (and dO when the workload has a backward) for one workload, on the CPU."""
+    if n is None:
+        n = 4 if w.backward else 3
+    return draw(w.B, w.H, w.T, w.D, dtype=w.torch_dtype, seed=w.seed, scale=w.scale, n=n)

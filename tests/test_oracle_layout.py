@@ -1,0 +1,80 @@
+"""Pins for the oracle's block LUT derivation (CPU only).
+
+``oracle.block_layout`` counts enumerated (query, key) pairs per block.  Here the
+same counts come from a dense boolean matrix in kernel coordinates, built with
+the membership predicate and summed block-wise by a reshape, and the maps are
+checked to be bijections onto the positions they claim.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import DENSE, FIXED, FIXED_R1, STRIDED
+
+
+def brute_force_counts(pattern, kind, T, l, c, bs):
+    rows, keys = oracle.kernel_maps(pattern, kind, T, l, c, bs)
+    n_qb = -(-len(rows) // bs)
+    n_kb = -(-len(keys) // bs)
+    rp = np.full(n_qb * bs, -1)
+    rp[:len(rows)] = rows
+    kp = np.full(n_kb * bs, -1)
+    kp[:len(keys)] = keys
+    M = oracle.in_key_set(pattern, kind, rp[:, None], kp[None, :], l, c)
+    M &= (rp[:, None] >= 0) & (kp[None, :] >= 0)
+    return M.reshape(n_qb, bs, n_kb, bs).sum(axis=(1, 3))
+
+
+CASES = [
+    (STRIDED, 256, 16, 0, 16), (STRIDED, 256, 16, 0, 64), (STRIDED, 250, 16, 0, 32),
+    (STRIDED, 300, 7, 0, 16), (STRIDED, 100, 128, 0, 64),
+    (FIXED, 1024, 32, 4, 64), (FIXED, 250, 16, 3, 16), (FIXED, 333, 20, 20, 32),
+    (FIXED, 60, 64, 4, 64), (FIXED_R1, 250, 16, 3, 16), (FIXED_R1, 256, 32, 4, 64),
+    (DENSE, 200, 16, 0, 64),
+]
+
+
+@pytest.mark.parametrize("pattern,T,l,c,bs", CASES)
+def test_lut_matches_dense_block_sums(pattern, T, l, c, bs):
+    for kind in (0, 1):
+        lay = oracle.block_layout(pattern, kind, T, l, c, bs)
+        counts = brute_force_counts(pattern, kind, T, l, c, bs)
+        qb, kb = np.nonzero(counts)
+        assert lay["nnz"] == len(qb)
+        rp = lay["row_ptr"]
+        for q in range(lay["n_qb"]):
+            sel = qb == q
+            assert lay["col_idx"][rp[q]:rp[q + 1]].tolist() == kb[sel].tolist()
+            full = (counts[q, kb[sel]] == bs * bs).astype(np.uint8)
+            assert lay["flags"][rp[q]:rp[q + 1]].tolist() == full.tolist()
+        cp = lay["col_ptr"]
+        for k in range(lay["n_kb"]):
+            sel = kb == k
+            assert lay["row_idx"][cp[k]:cp[k + 1]].tolist() == sorted(qb[sel].tolist())
+        assert lay["pair_count"] == oracle.pair_count(pattern, kind, T, l, c)
+
+
+@pytest.mark.parametrize("pattern,T,l,c,bs", CASES)
+def test_maps_are_bijections(pattern, T, l, c, bs):
+    for kind in (0, 1):
+        rows, keys = oracle.kernel_maps(pattern, kind, T, l, c, bs)
+        real_rows = rows[rows >= 0]
+        assert sorted(real_rows.tolist()) == list(range(T))
+        real_keys = keys[keys >= 0]
+        assert len(set(real_keys.tolist())) == real_keys.size
+        attended = set()
+        for t in range(T):
+            attended |= set(oracle.key_set(pattern, kind, t, T, l, c).tolist())
+        assert attended <= set(real_keys.tolist())
+        if pattern == FIXED and kind == 1:
+            nb = -(-T // l)
+            expect = [b * l + o for b in range(nb - 1) for o in range(l - c, l)]
+            assert real_keys.tolist() == expect
+        if pattern == STRIDED and kind == 1:
+            # within a class the run is in increasing position order, l apart
+            n_pad = len(rows) // min(l, T)
+            assert n_pad % bs == 0
+            for r in range(min(l, T)):
+                run = rows[r * n_pad:(r + 1) * n_pad]
+                run = run[run >= 0]
+                assert run.tolist() == list(range(r, T, l))
