@@ -1,0 +1,16 @@
+"""Factorized sparse causal self-attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libst.so`` (hand-written HIP kernels behind the C ABI of
+``include/st.h``); this package is its thin Python binding.  Importing the
+package does not load the library; the first call does, and raises if it has
+not been built (``python -m factorized_sparse_self_amd.build``).
+"""
+from ._lib import (EXPORTED, ST_DENSE, ST_FIXED, ST_FIXED_R1, ST_STRIDED, StError, lib,
+                   sparse_attention, st_block_size, st_layout_build, st_release,
+                   st_sparse_attn_bwd, st_sparse_attn_fwd)
+
+__all__ = [
+    "EXPORTED", "ST_STRIDED", "ST_FIXED", "ST_FIXED_R1", "ST_DENSE", "StError", "lib",
+    "sparse_attention", "st_block_size", "st_layout_build", "st_release",
+    "st_sparse_attn_bwd", "st_sparse_attn_fwd",
+]

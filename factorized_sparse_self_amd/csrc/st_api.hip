@@ -1,0 +1,376 @@
+// C ABI of libst: argument checks, the per-device plan cache (block LUTs of
+// both head kinds plus the work schedules), the backward workspace, and the
+// kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/st.h"
+#include "st_internal.hpp"
+#include "st_kernels.hpp"
+
+namespace st {
+
+namespace {
+
+// A key block of the dK/dV pass is split so that no work item walks more than
+// this many row blocks (fp32 partials are then summed by the reduce kernel).
+constexpr int kDkdvSplit = 32;
+
+struct PlanKey {
+  int device, pattern, T, l, c, B, H;
+  bool operator<(const PlanKey& o) const {
+    return std::tie(device, pattern, T, l, c, B, H) <
+           std::tie(o.device, o.pattern, o.T, o.l, o.c, o.B, o.H);
+  }
+};
+
+struct Plan {
+  void* dmem = nullptr;  // single device allocation holding everything below
+  KindDev* kinds = nullptr;
+  int2* row_items = nullptr;  // forward and dq
+  DkdvItem* dkdv_items = nullptr;
+  ReduceItem* red_items = nullptr;
+  int n_row_items = 0, n_dkdv_items = 0, n_red_items = 0, n_slots = 0;
+  ~Plan() {
+    if (dmem) (void)hipFree(dmem);
+  }
+};
+
+struct Workspace {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_mutex;
+std::map<PlanKey, std::unique_ptr<Plan>> g_plans;
+std::map<int, Workspace> g_workspace;
+
+int hip_fail(const char* what, hipError_t e) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return ST_ERR_HIP;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Host image of a plan: byte blob plus the offsets of its parts.
+struct Blob {
+  std::vector<unsigned char> bytes;
+  size_t add(const void* src, size_t n) {
+    const size_t off = align_up(bytes.size(), 256);
+    bytes.resize(off + std::max<size_t>(n, 1));
+    if (n) std::memcpy(bytes.data() + off, src, n);
+    return off;
+  }
+};
+
+int build_plan(const PlanKey& key, Plan* plan) {
+  st_layout lay;
+  lay.pattern = key.pattern;
+  lay.T = key.T;
+  lay.l = key.l;
+  lay.c = key.c;
+  for (int kind = 0; kind < 2; ++kind) {
+    make_geometry(key.pattern, kind, key.T, key.l, key.c, &lay.kind[kind].geo);
+    build_kind(lay.kind[kind]);
+  }
+  const int BH = key.B * key.H;
+
+  // Row-block items (forward and dq): every row block of every head, the
+  // longest (most key blocks) first so the tail of the grid is short.
+  struct RowItem {
+    int qb, bh, cost;
+  };
+  std::vector<RowItem> rows;
+  for (int bh = 0; bh < BH; ++bh) {
+    const KindLayout& L = lay.kind[(bh % key.H) & 1];
+    for (int qb = 0; qb < L.n_qb; ++qb)
+      rows.push_back({qb, bh, L.row_ptr[qb + 1] - L.row_ptr[qb] + 1});
+  }
+  std::stable_sort(rows.begin(), rows.end(),
+                   [](const RowItem& x, const RowItem& y) { return x.cost > y.cost; });
+  std::vector<int2> row_items(rows.size());
+  for (size_t i = 0; i < rows.size(); ++i) row_items[i] = make_int2(rows[i].qb, rows[i].bh);
+
+  // dK/dV items: every key block of every head, split when long.
+  std::vector<DkdvItem> dkdv;
+  std::vector<ReduceItem> red;
+  int slots = 0;
+  for (int bh = 0; bh < BH; ++bh) {
+    const KindLayout& L = lay.kind[(bh % key.H) & 1];
+    for (int kb = 0; kb < L.n_kb; ++kb) {
+      const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1], n = e1 - e0;
+      const int nsplit = std::max(1, (n + kDkdvSplit - 1) / kDkdvSplit);
+      if (nsplit == 1) {
+        dkdv.push_back({kb, bh, e0, e1, -1, 0, 0, 0});
+        continue;
+      }
+      const int chunk = (n + nsplit - 1) / nsplit;
+      int used = 0;
+      for (int s = 0; s < nsplit; ++s) {
+        const int a = e0 + s * chunk, b = std::min(e1, a + chunk);
+        dkdv.push_back({kb, bh, a, b, slots + s, 0, 0, 0});
+        ++used;
+      }
+      red.push_back({kb, bh, slots, used});
+      slots += used;
+    }
+  }
+  std::stable_sort(dkdv.begin(), dkdv.end(),
+                   [](const DkdvItem& x, const DkdvItem& y) { return x.e1 - x.e0 > y.e1 - y.e0; });
+
+  Blob blob;
+  KindDev kinds_host[2];
+  size_t off_kinds = blob.add(kinds_host, sizeof(kinds_host));
+  size_t offs[2][6];
+  for (int kind = 0; kind < 2; ++kind) {
+    const KindLayout& L = lay.kind[kind];
+    offs[kind][0] = blob.add(L.row_ptr.data(), L.row_ptr.size() * 4);
+    offs[kind][1] = blob.add(L.col_idx.data(), L.col_idx.size() * 4);
+    offs[kind][2] = blob.add(L.flags.data(), L.flags.size());
+    offs[kind][3] = blob.add(L.col_ptr.data(), L.col_ptr.size() * 4);
+    offs[kind][4] = blob.add(L.row_idx.data(), L.row_idx.size() * 4);
+    offs[kind][5] = blob.add(L.csc_flags.data(), L.csc_flags.size());
+  }
+  const size_t off_rows = blob.add(row_items.data(), row_items.size() * sizeof(int2));
+  const size_t off_dkdv = blob.add(dkdv.data(), dkdv.size() * sizeof(DkdvItem));
+  const size_t off_red = blob.add(red.data(), red.size() * sizeof(ReduceItem));
+
+  hipError_t e = hipMalloc(&plan->dmem, blob.bytes.size());
+  if (e != hipSuccess) {
+    plan->dmem = nullptr;
+    set_error(std::string("plan allocation: ") + hipGetErrorString(e));
+    return ST_ERR_NOMEM;
+  }
+  unsigned char* dbase = (unsigned char*)plan->dmem;
+  for (int kind = 0; kind < 2; ++kind) {
+    const KindLayout& L = lay.kind[kind];
+    KindDev& k = kinds_host[kind];
+    k.geo = L.geo;
+    k.row_ptr = (const int32_t*)(dbase + offs[kind][0]);
+    k.col_idx = (const int32_t*)(dbase + offs[kind][1]);
+    k.flags = (const uint8_t*)(dbase + offs[kind][2]);
+    k.col_ptr = (const int32_t*)(dbase + offs[kind][3]);
+    k.row_idx = (const int32_t*)(dbase + offs[kind][4]);
+    k.csc_flags = (const uint8_t*)(dbase + offs[kind][5]);
+  }
+  std::memcpy(blob.bytes.data() + off_kinds, kinds_host, sizeof(kinds_host));
+  e = hipMemcpy(plan->dmem, blob.bytes.data(), blob.bytes.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail("plan upload", e);
+  plan->kinds = (KindDev*)(dbase + off_kinds);
+  plan->row_items = (int2*)(dbase + off_rows);
+  plan->dkdv_items = (DkdvItem*)(dbase + off_dkdv);
+  plan->red_items = (ReduceItem*)(dbase + off_red);
+  plan->n_row_items = (int)row_items.size();
+  plan->n_dkdv_items = (int)dkdv.size();
+  plan->n_red_items = (int)red.size();
+  plan->n_slots = slots;
+  return ST_OK;
+}
+
+// Caller holds g_mutex.
+int get_plan(const PlanKey& key, Plan** out) {
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) {
+    *out = it->second.get();
+    return ST_OK;
+  }
+  std::unique_ptr<Plan> plan(new Plan);
+  const int rc = build_plan(key, plan.get());
+  if (rc != ST_OK) return rc;
+  *out = plan.get();
+  g_plans[key] = std::move(plan);
+  return ST_OK;
+}
+
+// Caller holds g_mutex.
+int get_workspace(int device, size_t bytes, void** out) {
+  Workspace& w = g_workspace[device];
+  if (w.bytes < bytes) {
+    if (w.p) (void)hipFree(w.p);
+    w.p = nullptr;
+    w.bytes = 0;
+    const hipError_t e = hipMalloc(&w.p, bytes);
+    if (e != hipSuccess) {
+      w.p = nullptr;
+      set_error(std::string("workspace allocation: ") + hipGetErrorString(e));
+      return ST_ERR_NOMEM;
+    }
+    w.bytes = bytes;
+  }
+  *out = w.p;
+  return ST_OK;
+}
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, int H, int T, int D,
+                    int pattern, int l, int c) {
+  for (int i = 0; i < n_ptrs; ++i)
+    if (!aligned16(ptrs[i])) {
+      set_error(std::string(fn) + ": tensor pointer " + std::to_string(i) +
+                " is null or not 16-byte aligned");
+      return ST_ERR_INVALID;
+    }
+  if (B < 1 || H < 1 || (int64_t)B * H > (1 << 20)) {
+    set_error(std::string(fn) + ": need B >= 1, H >= 1, B*H <= 2^20");
+    return ST_ERR_INVALID;
+  }
+  const std::string why = check_pattern_args(pattern, T, l, c);
+  if (!why.empty()) {
+    set_error(std::string(fn) + ": " + why);
+    return ST_ERR_INVALID;
+  }
+  if (D != 32 && D != 64) {
+    set_error(std::string(fn) + ": head dimension D must be 32 or 64, got " + std::to_string(D));
+    return ST_ERR_UNSUPPORTED;
+  }
+  Geometry g;
+  make_geometry(pattern, 1, T, l, c, &g);
+  const int64_t blocks = ((int64_t)std::max(g.n_rows, T) + kBlock - 1) / kBlock;
+  if (blocks * B * H >= (int64_t)1 << 31) {
+    set_error(std::string(fn) + ": too many work items for one launch");
+    return ST_ERR_UNSUPPORTED;
+  }
+  return ST_OK;
+}
+
+template <typename TE>
+int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
+  const void* ptrs[] = {q, k, v, out, lse};
+  int rc = check_attn_args(fn, ptrs, 5, B, H, T, D, pattern, l, c);
+  if (rc != ST_OK) return rc;
+  if (pattern != ST_FIXED && pattern != ST_FIXED_R1) c = 0;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  std::lock_guard<std::mutex> lock(g_mutex);
+  Plan* plan = nullptr;
+  rc = get_plan({device, pattern, T, l, c, B, H}, &plan);
+  if (rc != ST_OK) return rc;
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.H = H;
+  a.T = T;
+  a.kinds = plan->kinds;
+  a.items = plan->row_items;
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipStream_t s = (hipStream_t)stream;
+  e = (D == 32) ? launch_fwd<TE, 32>(a, plan->n_row_items, s) : launch_fwd<TE, 64>(a, plan->n_row_items, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ST_OK;
+}
+
+template <typename TE>
+int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const void* out,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H, int T,
+             int D, int pattern, int l, int c, void* stream) {
+  const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
+  int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c);
+  if (rc != ST_OK) return rc;
+  if (pattern != ST_FIXED && pattern != ST_FIXED_R1) c = 0;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  std::lock_guard<std::mutex> lock(g_mutex);
+  Plan* plan = nullptr;
+  rc = get_plan({device, pattern, T, l, c, B, H}, &plan);
+  if (rc != ST_OK) return rc;
+  const size_t delta_bytes = align_up((size_t)B * H * T * sizeof(float), 256);
+  const size_t partial_bytes = (size_t)plan->n_slots * 2 * kBlock * D * sizeof(float);
+  void* ws = nullptr;
+  rc = get_workspace(device, delta_bytes + partial_bytes, &ws);
+  if (rc != ST_OK) return rc;
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)ws;
+  a.partial = (float*)((unsigned char*)ws + delta_bytes);
+  a.BH = B * H;
+  a.H = H;
+  a.T = T;
+  a.kinds = plan->kinds;
+  a.dq_items = plan->row_items;
+  a.dkdv_items = plan->dkdv_items;
+  a.red_items = plan->red_items;
+  a.scale = (float)(1.0 / std::sqrt((double)D));
+  a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipStream_t s = (hipStream_t)stream;
+  e = (D == 32) ? launch_bwd<TE, 32>(a, plan->n_row_items, plan->n_dkdv_items, plan->n_red_items, s)
+                : launch_bwd<TE, 64>(a, plan->n_row_items, plan->n_dkdv_items, plan->n_red_items, s);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ST_OK;
+}
+
+}  // namespace
+}  // namespace st
+
+using namespace st;
+
+extern "C" {
+
+int st_sparse_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int H, int T, int D, int pattern, int l, int c, void* stream) {
+  return attn_fwd<bf16>("st_sparse_attn_fwd", q, k, v, out, lse, B, H, T, D, pattern, l, c, stream);
+}
+
+int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
+  return attn_fwd<float>("st_sparse_attn_fwd_f32", q, k, v, out, lse, B, H, T, D, pattern, l, c,
+                         stream);
+}
+
+int st_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                       int H, int T, int D, int pattern, int l, int c, void* stream) {
+  return attn_bwd<bf16>("st_sparse_attn_bwd", q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D,
+                        pattern, l, c, stream);
+}
+
+int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
+  return attn_bwd<float>("st_sparse_attn_bwd_f32", q, k, v, out, lse, dout, dq, dk, dv, B, H, T,
+                         D, pattern, l, c, stream);
+}
+
+void st_release(void) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  int current = 0;
+  const bool have_device = hipGetDevice(&current) == hipSuccess;
+  for (auto& kv : g_plans) {
+    if (have_device) (void)hipSetDevice(kv.first.device);
+    kv.second.reset();
+  }
+  g_plans.clear();
+  for (auto& kv : g_workspace) {
+    if (kv.second.p) {
+      if (have_device) (void)hipSetDevice(kv.first);
+      (void)hipFree(kv.second.p);
+    }
+  }
+  g_workspace.clear();
+  if (have_device) (void)hipSetDevice(current);
+}
+
+}  // extern "C"

@@ -1,0 +1,530 @@
+// Recompute backward of sparse attention for gfx950.
+//
+// The attention weights are not kept from the forward; they are rebuilt from
+// q, k and the row log-sum-exp when the gradients need them (nlp-lineage,
+// "The idea", recomputation).  For L = <dO, O>:
+//   p_tj = exp(s_tj - lse_t),  Delta_t = dO_t . O_t,
+//   dp_tj = dO_t . v_j,        ds_tj = p_tj (dp_tj - Delta_t),
+//   dq_t = sum_j ds_tj k_j / sqrt(D),  dk_j = sum_t ds_tj q_t / sqrt(D),
+//   dv_j = sum_t p_tj dO_t.
+// Kernels (one stream, in order):
+//   pre   Delta for every row; zero dk / dv at positions no query attends
+//   dq    per row block over the CSR (no cross-item reduction)
+//   dkdv  per key block over the CSC; key blocks with many row blocks are
+//         split, each split writing fp32 partials
+//   red   sums the partials of split key blocks
+#include "st_device.hpp"
+#include "st_kernels.hpp"
+
+namespace st {
+
+namespace {
+
+template <typename TE, int D>
+struct BwdLds {
+  static constexpr bool BF = IsBf16<TE>::value;
+  static constexpr int RP = BF ? D + 8 : D + 2;       // row-major pitch
+  static constexpr int TP = kBlock + 8;               // transposed pitch (bf16 only)
+  static constexpr int R_ELEMS = kBlock * RP;
+  static constexpr int T_ELEMS = BF ? D * TP : 1;
+};
+
+// Load rows (2*pr, 2*pr+1), 8-element chunk ch of a bf16 tensor into the
+// row-major copy and (optionally) the transposed copy.
+template <int D>
+__device__ __forceinline__ void stage_pair_bf16(const bf16* __restrict__ src, int p0, int p1, int pr,
+                                                int ch, bf16* rows, bf16* trans) {
+  using L = BwdLds<bf16, D>;
+  uint4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+  if (p0 >= 0) x0 = *(const uint4*)(src + (size_t)p0 * D + ch * 8);
+  if (p1 >= 0) x1 = *(const uint4*)(src + (size_t)p1 * D + ch * 8);
+  *(uint4*)(rows + (2 * pr) * L::RP + ch * 8) = x0;
+  *(uint4*)(rows + (2 * pr + 1) * L::RP + ch * 8) = x1;
+  if (trans) {
+    const uint32_t a[4] = {x0.x, x0.y, x0.z, x0.w};
+    const uint32_t b[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
+      const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
+      *(uint32_t*)(trans + (ch * 8 + 2 * w) * L::TP + 2 * pr) = lo;
+      *(uint32_t*)(trans + (ch * 8 + 2 * w + 1) * L::TP + 2 * pr) = hi;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_row_f32(const float* __restrict__ src, int p, int r, int ch,
+                                              float* rows) {
+  using L = BwdLds<float, D>;
+  float4 x = {0.f, 0.f, 0.f, 0.f};
+  if (p >= 0) x = *(const float4*)(src + (size_t)p * D + ch * 4);
+  float* d = rows + r * L::RP + ch * 4;
+  *(float2*)d = make_float2(x.x, x.y);
+  *(float2*)(d + 2) = make_float2(x.z, x.w);
+}
+
+// ---------------------------------------------------------------------------
+// pre: Delta_t = sum_d dO_t,d O_t,d; zero dk / dv where no query attends.
+// ---------------------------------------------------------------------------
+template <typename TE, int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
+  constexpr int VEC = 16 / sizeof(TE);  // elements per 16-byte chunk
+  constexpr int TPR = D / VEC;          // threads per row (power of two)
+  const int64_t row = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / TPR;
+  const int ch = threadIdx.x % TPR;
+  const int64_t n_rows = (int64_t)a.BH * a.T;
+  const bool valid = row < n_rows;
+  float part = 0.f;
+  if (valid) {
+    const TE* o = (const TE*)a.o + row * D + ch * VEC;
+    const TE* g = (const TE*)a.dout + row * D + ch * VEC;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) part += (float)o[i] * (float)g[i];
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) part += xor_shfl(part, m);
+  if (!valid) return;
+  if (ch == 0) a.delta[row] = part;
+  const int bh = (int)(row / a.T), t = (int)(row - (int64_t)bh * a.T);
+  const Geometry& g = a.kinds[(bh % a.H) & 1].geo;
+  if (!position_is_key(g, t)) {
+    const uint4 z = {0, 0, 0, 0};
+    *(uint4*)((TE*)a.dk + row * D + ch * VEC) = z;
+    *(uint4*)((TE*)a.dv + row * D + ch * VEC) = z;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq: per row block; 4 waves x 16 rows; loop over the CSR key blocks.
+// ---------------------------------------------------------------------------
+template <typename TE, int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+  using L = BwdLds<TE, D>;
+  constexpr bool BF = L::BF;
+  constexpr int NQ = BF ? D / 32 : D / 4;
+  constexpr int ND = D / 16;
+  __shared__ __attribute__((aligned(16))) TE Ks[L::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) TE Vs[L::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) TE Kt[L::T_ELEMS];
+
+  const int2 item = a.dq_items[blockIdx.x];
+  const int qb = item.x, bh = item.y;
+  const KindDev kd = a.kinds[(bh % a.H) & 1];
+  const Geometry& g = kd.geo;
+  const size_t base = (size_t)bh * a.T * D;
+  const TE* __restrict__ Qg = (const TE*)a.q + base;
+  const TE* __restrict__ Kg = (const TE*)a.k + base;
+  const TE* __restrict__ Vg = (const TE*)a.v + base;
+  const TE* __restrict__ Gg = (const TE*)a.dout + base;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int R = qb * kBlock + wave * 16 + li;
+  const int t = row_position(g, R);
+  int lo = 1, hi = 0;
+  if (t >= 0) row_interval(g, R, t, lo, hi);
+  const int wlo = wave_min(lo <= hi ? lo : 0x7fffffff);
+  const int whi = wave_max(lo <= hi ? hi : -1);
+  const bool wave_active = whi >= 0;
+  float lse2 = 0.f, delta = 0.f;
+  if (t >= 0 && lo <= hi) {
+    lse2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
+    delta = a.delta[(size_t)bh * a.T + t];
+  }
+
+  typedef typename std::conditional<BF, bf16x8, float>::type Op;
+  Op qop[NQ], gop[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    if constexpr (BF) {
+      uint4 rq = {0, 0, 0, 0}, rg = {0, 0, 0, 0};
+      if (t >= 0) {
+        rq = *(const uint4*)(Qg + (size_t)t * D + 32 * s + 8 * lg);
+        rg = *(const uint4*)(Gg + (size_t)t * D + 32 * s + 8 * lg);
+      }
+      qop[s] = __builtin_bit_cast(bf16x8, rq);
+      gop[s] = __builtin_bit_cast(bf16x8, rg);
+    } else {
+      qop[s] = (t >= 0) ? (float)Qg[(size_t)t * D + 4 * s + lg] : 0.f;
+      gop[s] = (t >= 0) ? (float)Gg[(size_t)t * D + 4 * s + lg] : 0.f;
+    }
+  }
+  f32x4 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.sl2;
+
+  const int e0 = kd.row_ptr[qb], e1 = kd.row_ptr[qb + 1];
+  for (int e = e0; e < e1; ++e) {
+    const int kb = kd.col_idx[e];
+    const bool full = kd.flags[e] != 0;
+    __syncthreads();
+    if constexpr (BF) {
+      constexpr int CH = D / 8;
+      for (int u = tid; u < (kBlock / 2) * CH; u += kThreads) {
+        const int pr = u / CH, ch = u - pr * CH;
+        const int p0 = key_position(g, kb * kBlock + 2 * pr);
+        const int p1 = key_position(g, kb * kBlock + 2 * pr + 1);
+        stage_pair_bf16<D>(Kg, p0, p1, pr, ch, Ks, Kt);
+        stage_pair_bf16<D>(Vg, p0, p1, pr, ch, Vs, nullptr);
+      }
+    } else {
+      constexpr int CH = D / 4;
+      for (int u = tid; u < kBlock * CH; u += kThreads) {
+        const int r = u / CH, ch = u - r * CH;
+        const int p = key_position(g, kb * kBlock + r);
+        stage_row_f32<D>((const float*)Kg, p, r, ch, (float*)Ks);
+        stage_row_f32<D>((const float*)Vg, p, r, ch, (float*)Vs);
+      }
+    }
+    __syncthreads();
+    if (!wave_active) continue;
+
+    const int k0 = kb * kBlock;
+    bool need[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      need[b] = full || (k0 + 16 * b <= whi && k0 + 16 * b + 15 >= wlo);
+
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      s[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (!need[b]) continue;
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        if constexpr (BF) {
+          const bf16x8 ak = *(const bf16x8*)(Ks + (16 * b + li) * L::RP + 32 * k + 8 * lg);
+          const bf16x8 av = *(const bf16x8*)(Vs + (16 * b + li) * L::RP + 32 * k + 8 * lg);
+          s[b] = mfma_bf16(ak, qop[k], s[b]);
+          dp[b] = mfma_bf16(av, gop[k], dp[b]);
+        } else {
+          const float ak = ((const float*)Ks)[(16 * b + li) * L::RP + 4 * k + lg];
+          const float av = ((const float*)Vs)[(16 * b + li) * L::RP + 4 * k + lg];
+          s[b] = mfma_f32(ak, qop[k], s[b]);
+          dp[b] = mfma_f32(av, gop[k], dp[b]);
+        }
+      }
+    }
+    // ds = p * (dp - Delta), p rebuilt from lse; zero outside the row's run
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int Kk = k0 + 16 * b + 4 * lg + i;
+        const bool in = full || (Kk >= lo && Kk <= hi);
+        const float p = in ? fast_exp2(fmaf(s[b][i], sl2, -lse2)) : 0.f;
+        s[b][i] = p * (dp[b][i] - delta);
+      }
+    // dq^T += K^T ds^T
+    if constexpr (BF) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (!need[2 * kk] && !need[2 * kk + 1]) continue;
+        const bf16x8 bs = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const bf16* row = Kt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
+          acc[d] = mfma_bf16(concat(*(const bf16x4*)row, *(const bf16x4*)(row + 16)), bs, acc[d]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (!need[b]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const float ak = ((const float*)Ks)[(16 * b + 4 * lg + i) * L::RP + 16 * d + li];
+            acc[d] = mfma_f32(ak, s[b][i], acc[d]);
+          }
+      }
+    }
+  }
+  if (t < 0) return;
+  TE* dq = (TE*)a.dq + base + (size_t)t * D;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const f32x4 o = acc[d] * a.scale;
+    if constexpr (BF) {
+      *(bf16x4*)(dq + 16 * d + 4 * lg) = to_bf16x4(o);
+    } else {
+      *(float4*)(dq + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dkdv: per key block (or a split of its row blocks); 4 waves x 16 keys.
+// ---------------------------------------------------------------------------
+template <typename TE, int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+  using L = BwdLds<TE, D>;
+  constexpr bool BF = L::BF;
+  constexpr int NQ = BF ? D / 32 : D / 4;
+  constexpr int ND = D / 16;
+  __shared__ __attribute__((aligned(16))) TE Qs[L::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) TE Gs[L::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) TE Qt[L::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) TE Gt[L::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) float lse2s[kBlock];
+  __shared__ __attribute__((aligned(16))) float dels[kBlock];
+  __shared__ __attribute__((aligned(16))) int los[kBlock];
+  __shared__ __attribute__((aligned(16))) int his[kBlock];
+
+  const DkdvItem item = a.dkdv_items[blockIdx.x];
+  const int kb = item.kb, bh = item.bh;
+  const KindDev kd = a.kinds[(bh % a.H) & 1];
+  const Geometry& g = kd.geo;
+  const size_t base = (size_t)bh * a.T * D;
+  const TE* __restrict__ Qg = (const TE*)a.q + base;
+  const TE* __restrict__ Kg = (const TE*)a.k + base;
+  const TE* __restrict__ Vg = (const TE*)a.v + base;
+  const TE* __restrict__ Gg = (const TE*)a.dout + base;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int Kw0 = kb * kBlock + wave * 16;  // first key of this wave
+  const int Kl = Kw0 + li;                  // this lane's key
+  const int kp = key_position(g, Kl);
+
+  typedef typename std::conditional<BF, bf16x8, float>::type Op;
+  Op kop[NQ], vop[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    if constexpr (BF) {
+      uint4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
+      if (kp >= 0) {
+        rk = *(const uint4*)(Kg + (size_t)kp * D + 32 * s + 8 * lg);
+        rv = *(const uint4*)(Vg + (size_t)kp * D + 32 * s + 8 * lg);
+      }
+      kop[s] = __builtin_bit_cast(bf16x8, rk);
+      vop[s] = __builtin_bit_cast(bf16x8, rv);
+    } else {
+      kop[s] = (kp >= 0) ? (float)Kg[(size_t)kp * D + 4 * s + lg] : 0.f;
+      vop[s] = (kp >= 0) ? (float)Vg[(size_t)kp * D + 4 * s + lg] : 0.f;
+    }
+  }
+  f32x4 dk[ND], dv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    dk[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    dv[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.sl2;
+
+  for (int e = item.e0; e < item.e1; ++e) {
+    const int qb = kd.row_idx[e];
+    const bool full = kd.csc_flags[e] != 0;
+    __syncthreads();
+    if constexpr (BF) {
+      constexpr int CH = D / 8;
+      for (int u = tid; u < (kBlock / 2) * CH; u += kThreads) {
+        const int pr = u / CH, ch = u - pr * CH;
+        const int p0 = row_position(g, qb * kBlock + 2 * pr);
+        const int p1 = row_position(g, qb * kBlock + 2 * pr + 1);
+        stage_pair_bf16<D>(Qg, p0, p1, pr, ch, Qs, Qt);
+        stage_pair_bf16<D>(Gg, p0, p1, pr, ch, Gs, Gt);
+      }
+    } else {
+      constexpr int CH = D / 4;
+      for (int u = tid; u < kBlock * CH; u += kThreads) {
+        const int r = u / CH, ch = u - r * CH;
+        const int p = row_position(g, qb * kBlock + r);
+        stage_row_f32<D>((const float*)Qg, p, r, ch, (float*)Qs);
+        stage_row_f32<D>((const float*)Gg, p, r, ch, (float*)Gs);
+      }
+    }
+    if (tid < kBlock) {
+      const int R = qb * kBlock + tid;
+      const int t = row_position(g, R);
+      int lo = 1, hi = 0;
+      float l2 = 0.f, de = 0.f;
+      if (t >= 0) {
+        row_interval(g, R, t, lo, hi);
+        if (lo <= hi) {
+          l2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
+          de = a.delta[(size_t)bh * a.T + t];
+        }
+      }
+      los[tid] = lo;
+      his[tid] = hi;
+      lse2s[tid] = l2;
+      dels[tid] = de;
+    }
+    __syncthreads();
+
+    // which 16-row blocks have a row whose run meets this wave's 16 keys
+    const int rlo = los[lane], rhi = his[lane];
+    const uint64_t hit = __ballot(rlo <= rhi && rlo <= Kw0 + 15 && rhi >= Kw0);
+    bool need[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) need[b] = full || ((hit >> (16 * b)) & 0xffffull) != 0;
+    if (!full && hit == 0) continue;
+
+    // S = Q K^T and dP = dO V^T: lane holds rows 16b + 4lg + i of key Kl
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      s[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (!need[b]) continue;
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        if constexpr (BF) {
+          const bf16x8 aq = *(const bf16x8*)(Qs + (16 * b + li) * L::RP + 32 * k + 8 * lg);
+          const bf16x8 ag = *(const bf16x8*)(Gs + (16 * b + li) * L::RP + 32 * k + 8 * lg);
+          s[b] = mfma_bf16(aq, kop[k], s[b]);
+          dp[b] = mfma_bf16(ag, vop[k], dp[b]);
+        } else {
+          const float aq = ((const float*)Qs)[(16 * b + li) * L::RP + 4 * k + lg];
+          const float ag = ((const float*)Gs)[(16 * b + li) * L::RP + 4 * k + lg];
+          s[b] = mfma_f32(aq, kop[k], s[b]);
+          dp[b] = mfma_f32(ag, vop[k], dp[b]);
+        }
+      }
+    }
+    // p and ds for each (row 16b + 4lg + i, key Kl)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r0 = 16 * b + 4 * lg;
+      const float4 l2 = *(const float4*)(lse2s + r0);
+      const float4 de = *(const float4*)(dels + r0);
+      const int4 lo4 = *(const int4*)(los + r0);
+      const int4 hi4 = *(const int4*)(his + r0);
+      const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float dea[4] = {de.x, de.y, de.z, de.w};
+      const int loa[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+      const int hia[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = full || (Kl >= loa[i] && Kl <= hia[i]);
+        const float p = in ? fast_exp2(fmaf(s[b][i], sl2, -l2a[i])) : 0.f;
+        s[b][i] = p;
+        dp[b][i] = p * (dp[b][i] - dea[i]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS
+    if constexpr (BF) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (!need[2 * kk] && !need[2 * kk + 1]) continue;
+        const bf16x8 bp = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
+        const bf16x8 bd = pack_b_operand(dp[2 * kk], dp[2 * kk + 1]);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const bf16* rg = Gt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
+          const bf16* rq = Qt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
+          dv[d] = mfma_bf16(concat(*(const bf16x4*)rg, *(const bf16x4*)(rg + 16)), bp, dv[d]);
+          dk[d] = mfma_bf16(concat(*(const bf16x4*)rq, *(const bf16x4*)(rq + 16)), bd, dk[d]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (!need[b]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const int off = (16 * b + 4 * lg + i) * L::RP + 16 * d + li;
+            dv[d] = mfma_f32(((const float*)Gs)[off], s[b][i], dv[d]);
+            dk[d] = mfma_f32(((const float*)Qs)[off], dp[b][i], dk[d]);
+          }
+      }
+    }
+  }
+
+  if (item.slot < 0) {
+    if (kp < 0) return;
+    TE* dkp = (TE*)a.dk + base + (size_t)kp * D;
+    TE* dvp = (TE*)a.dv + base + (size_t)kp * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 x = dk[d] * a.scale;
+      if constexpr (BF) {
+        *(bf16x4*)(dkp + 16 * d + 4 * lg) = to_bf16x4(x);
+        *(bf16x4*)(dvp + 16 * d + 4 * lg) = to_bf16x4(dv[d]);
+      } else {
+        *(float4*)(dkp + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
+        *(float4*)(dvp + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
+      }
+    }
+  } else {
+    float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
+    float* pv = pk + kBlock * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 x = dk[d] * a.scale;
+      *(float4*)(pk + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
+      *(float4*)(pv + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// red: sum the fp32 partials of a split key block and store dk / dv.
+// ---------------------------------------------------------------------------
+template <typename TE, int D>
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
+  const ReduceItem item = a.red_items[blockIdx.x];
+  const KindDev kd = a.kinds[(item.bh % a.H) & 1];
+  const size_t base = (size_t)item.bh * a.T * D;
+  constexpr int CH = D / 4;
+  for (int u = threadIdx.x; u < 2 * kBlock * CH; u += kThreads) {
+    const int which = u / (kBlock * CH);  // 0 = dk, 1 = dv
+    const int r = (u / CH) % kBlock, ch = u % CH;
+    const int kp = key_position(kd.geo, item.kb * kBlock + r);
+    if (kp < 0) continue;
+    float4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < item.nsplit; ++j) {
+      const float4 x = *(const float4*)(a.partial + ((size_t)(item.slot0 + j) * 2 + which) * kBlock * D +
+                                        r * D + ch * 4);
+      s.x += x.x;
+      s.y += x.y;
+      s.z += x.z;
+      s.w += x.w;
+    }
+    TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
+    if constexpr (IsBf16<TE>::value) {
+      *(bf16x4*)dst = to_bf16x4((f32x4){s.x, s.y, s.z, s.w});
+    } else {
+      *(float4*)dst = s;
+    }
+  }
+}
+
+}  // namespace
+
+template <typename TE, int D>
+hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStream_t stream) {
+  constexpr int TPR = D / (16 / sizeof(TE));
+  const int64_t rows = (int64_t)a.BH * a.T;
+  const int64_t pre_blocks = (rows * TPR + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (n_dq > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (n_dkdv > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (n_red > 0) {
+    hipLaunchKernelGGL((bwd_reduce_kernel<TE, D>), dim3(n_red), dim3(kThreads), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+template hipError_t launch_bwd<bf16, 32>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<float, 32>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<float, 64>(const BwdArgs&, int, int, int, hipStream_t);
+
+}  // namespace st

@@ -1,0 +1,62 @@
+// Kernel argument blocks and launchers (host <-> device interface of libst).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "st_device.hpp"
+
+namespace st {
+
+// Work item of the dK/dV pass: key block kb of head bh, CSC entries [e0, e1).
+// slot >= 0: the key block is split over several items and this one writes
+// fp32 partial sums to workspace slot `slot`; slot < 0: write dk / dv directly.
+struct DkdvItem {
+  int kb, bh, e0, e1, slot, pad0, pad1, pad2;
+};
+
+// Reduction of a split key block: partial slots [slot0, slot0 + nsplit).
+struct ReduceItem {
+  int kb, bh, slot0, nsplit;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int H, T;
+  const KindDev* kinds;  // [2], device memory
+  const int2* items;     // {row block, batch*H + head}
+  float sl2;             // log2(e) / sqrt(D)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;    // [B*H*T] workspace: rowsum(dout * out)
+  float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
+  int BH, H, T;
+  const KindDev* kinds;
+  const int2* dq_items;
+  const DkdvItem* dkdv_items;
+  const ReduceItem* red_items;
+  float sl2;    // log2(e) / sqrt(D)
+  float scale;  // 1 / sqrt(D)
+};
+
+template <typename TE, int D>
+hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream);
+
+template <typename TE, int D>
+hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStream_t stream);
+
+}  // namespace st

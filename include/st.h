@@ -1,0 +1,179 @@
+/*
+ * st.h -- C ABI of libst.so: factorized sparse causal self-attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (nlp-lineage milestone page on the Sparse Transformer,
+ * "The notation"; llm-arch-kb "Sparse Transformer", §2 Derivation):
+ *
+ *   out[b,h,t,:] = sum_{j in S_h(t)} softmax_j( q[b,h,t,:] . k[b,h,j,:] / sqrt(D) ) v[b,h,j,:]
+ *
+ * where the softmax normalises over S_h(t) only (keys outside the set carry
+ * no probability mass) and S_h(t) is one half of a factorized pattern:
+ * head h uses sub-pattern (h mod 2), "kind 0" or "kind 1".
+ *
+ *   ST_STRIDED (llm-arch-kb §2, Pattern A -- strided; nlp-lineage "The idea"):
+ *     kind 0: the last l positions, t included:  max(0, t-l+1) <= j <= t
+ *     kind 1: every l-th position back from t:   j <= t and (t - j) mod l == 0
+ *   ST_FIXED (llm-arch-kb §2, Pattern B -- fixed; nlp-lineage "The idea"):
+ *     kind 0: t's own l-block up to t:           l*floor(t/l) <= j <= t
+ *     kind 1: the c summary positions at the end of every *earlier* block:
+ *             floor(j/l) < floor(t/l) and (j mod l) >= l - c
+ *   ST_FIXED_R1: as ST_FIXED, but kind 1 also admits the own block's summary
+ *     positions j <= t (the reading of the llm-arch-kb §3 mask sketch).
+ *   ST_DENSE: full causal attention, S(t) = {j <= t}, for both kinds (the
+ *     dense comparator of nlp-lineage "The notation").
+ *
+ * Conventions (readings where the pages are silent):
+ *   - positions are 0-based; T need not be a multiple of l;
+ *   - a row with an empty key set (ST_FIXED kind 1, first block) gets
+ *     out = 0 and lse = -inf, and contributes nothing to any gradient;
+ *   - lse[b,h,t] = ln sum_{j in S(t)} exp(q_t . k_j / sqrt(D)), fp32;
+ *   - keys that no query attends get dk = dv = 0.
+ *
+ * Layout.  q, k, v, out, dout, dq, dk, dv are dense row-major [B, H, T, D]
+ * (D fastest); lse is [B, H, T] fp32.  The unsuffixed entry points take and
+ * return bf16 (bfloat16, round-to-nearest-even on output) with fp32
+ * arithmetic inside; the _f32 entry points take and return fp32.
+ *
+ * Ownership.  All tensor pointers are device pointers owned by the caller;
+ * the library never frees them or keeps them past the call.  The library owns
+ * a per-device cache of block LUTs and work schedules and a per-device
+ * backward workspace, both grown on demand and freed by st_release().
+ *
+ * Asynchrony.  The attention entry points enqueue kernels on `stream` (a
+ * hipStream_t; NULL means the default stream) and return without waiting.
+ * A call that has to build a LUT or grow the workspace performs blocking
+ * host-to-device copies or allocations first.  Backward calls that overlap in
+ * time on one device share the workspace and race; serialise them.
+ *
+ * Errors.  Every entry point returns ST_OK (0) or a negative st_status; no
+ * C++ exception crosses the ABI.  The message of the last failure on the
+ * calling thread is available from st_last_error().
+ */
+#ifndef ST_H
+#define ST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum st_status {
+  ST_OK = 0,
+  ST_ERR_INVALID = -1,     /* bad argument: null/misaligned pointer, size out of range */
+  ST_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (e.g. D not 32 or 64) */
+  ST_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  ST_ERR_NOMEM = -4        /* host or device allocation failed */
+} st_status;
+
+typedef enum st_pattern {
+  ST_STRIDED = 0,
+  ST_FIXED = 1,
+  ST_FIXED_R1 = 2,
+  ST_DENSE = 3
+} st_pattern;
+
+/* ---------------------------------------------------------------------------
+ * Block layout (host only; no GPU needed).
+ *
+ * The pages precompute each query's key indices and run the attention as a
+ * block-sparse product over non-empty blocks (llm-arch-kb "Sparse
+ * Transformer", §2 "Per-layer cost" and §3 Reference implementation).  The
+ * library does so in kernel coordinates, per head kind:
+ *   kernel row R  holds query position row_pos[R] (-1 = padding),
+ *   kernel key K  holds key   position key_pos[K] (-1 = padding),
+ * with block size st_block_size() for both.  The maps:
+ *   - identity for ST_STRIDED kind 0, ST_FIXED / ST_FIXED_R1 kind 0, ST_DENSE;
+ *   - ST_STRIDED kind 1, residue-major: position m*l + r is row and key
+ *     r*n_pad + m, n = ceil(T/l), n_pad = n rounded up to a multiple of the
+ *     block size; classes r < min(l, T);
+ *   - ST_FIXED kind 1, compact summary keys: key b*c + o holds position
+ *     b*l + (l-c) + o for blocks b < ceil(T/l) - 1 (ST_FIXED_R1: all blocks,
+ *     positions >= T are padding); rows are the identity.
+ * In these coordinates every row attends one contiguous run of kernel keys.
+ * A (row block, key block) pair is listed when it holds at least one
+ * attended pair; its flag is 1 (FULL) when all block*block pairs are
+ * attended, else 0 (PARTIAL).  The CSR lists pairs sorted by (row block,
+ * key block); the CSC by (key block, row block).
+ * ------------------------------------------------------------------------- */
+typedef struct st_layout st_layout; /* opaque, owned by the library */
+
+enum {
+  ST_DIM_BLOCK = 0,   /* block size (rows and keys)                    */
+  ST_DIM_ROWS = 1,    /* kernel rows, padding included                 */
+  ST_DIM_KEYS = 2,    /* kernel keys, padding included                 */
+  ST_DIM_QBLOCKS = 3, /* ceil(rows / block): CSR row_ptr has this + 1  */
+  ST_DIM_KBLOCKS = 4, /* ceil(keys / block): CSC col_ptr has this + 1  */
+  ST_DIM_NNZ = 5,     /* listed block pairs                            */
+  ST_DIM_COUNT = 6
+};
+
+/* Build the layouts of both head kinds of `pattern` for sequence length T,
+ * stride l (>= 1) and summary count c (1 <= c <= l for the fixed patterns,
+ * ignored otherwise).  1 <= T <= 2^24.  On success *out owns the result;
+ * release it with st_layout_free().  Returns ST_ERR_INVALID on bad
+ * arguments, ST_ERR_NOMEM on allocation failure. */
+int st_layout_build(int pattern, int T, int l, int c, st_layout** out);
+
+/* dims[ST_DIM_COUNT] of head kind 0 or 1. */
+int st_layout_dims(const st_layout* lay, int kind, int32_t* dims);
+
+/* Total attended (query, key) pairs of one head of this kind, sum_t |S(t)|. */
+int st_layout_pairs(const st_layout* lay, int kind, int64_t* pairs);
+
+/* Copy the coordinate maps: row_pos[ROWS], key_pos[KEYS] (caller buffers). */
+int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, int32_t* key_pos);
+
+/* Copy the CSR: row_ptr[QBLOCKS+1], col_idx[NNZ], flags[NNZ] (caller buffers). */
+int st_layout_csr(const st_layout* lay, int kind, int32_t* row_ptr, int32_t* col_idx,
+                  uint8_t* flags);
+
+/* Copy the CSC: col_ptr[KBLOCKS+1], row_idx[NNZ], flags[NNZ] (caller buffers). */
+int st_layout_csc(const st_layout* lay, int kind, int32_t* col_ptr, int32_t* row_idx,
+                  uint8_t* flags);
+
+void st_layout_free(st_layout* lay);
+
+/* ---------------------------------------------------------------------------
+ * Attention.  Shapes: 1 <= B, 1 <= H, B*H <= 2^20, 1 <= T <= 2^24,
+ * D in {32, 64}; pattern, l and c as for st_layout_build.  Every pointer must
+ * be non-null and 16-byte aligned, and the tensors must not overlap (except
+ * that inputs may alias one another).
+ * ------------------------------------------------------------------------- */
+
+/* Forward (llm-arch-kb §2 "Sparse attention as an unnormalized form";
+ * nlp-lineage "The notation").  Reads q, k, v; writes out [B,H,T,D] and
+ * lse [B,H,T].  bf16 in / out, fp32 arithmetic. */
+int st_sparse_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+
+/* Backward of L = <dout, out> with the attention weights recomputed from q,
+ * k and lse instead of being stored (nlp-lineage "The idea", recomputation).
+ * `out` and `lse` must be what st_sparse_attn_fwd returned for the same
+ * q, k, v.  Writes dq, dk, dv [B,H,T,D].  bf16 in / out, fp32 arithmetic. */
+int st_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+
+/* fp32 twins: same arguments, fp32 tensors. */
+int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Utilities.
+ * ------------------------------------------------------------------------- */
+int st_block_size(void);                 /* block size of the LUTs (64)              */
+const char* st_status_string(int status); /* static text for a status code           */
+const char* st_last_error(void);         /* last failure message on this thread       */
+void st_release(void);                   /* free LUT caches and workspaces (all GPUs) */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ST_H */

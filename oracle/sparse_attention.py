@@ -133,11 +133,16 @@ def _attend_row(qt: np.ndarray, Ks: np.ndarray, Vs: np.ndarray, scale: float):
     return p @ Vs, lse, p
 
 
-def forward_rows(q, k, v, pattern, l, c, rows=None):
+def _heads(H, heads):
+    return range(H) if heads is None else [int(h) for h in heads]
+
+
+def forward_rows(q, k, v, pattern, l, c, rows=None, heads=None):
     """Attention output and row log-sum-exp for the given query positions.
 
     q, k, v: float64 arrays [B, H, T, D].  ``rows`` is an iterable of query
-    positions (all positions when None).  Returns (O [B, H, R, D],
+    positions (all positions when None); ``heads`` restricts the heads that
+    are computed (the others stay 0 / -inf).  Returns (O [B, H, R, D],
     lse [B, H, R]).  Empty key sets give O = 0, lse = -inf (reading R-empty).
     """
     B, H, T, D = q.shape
@@ -145,7 +150,7 @@ def forward_rows(q, k, v, pattern, l, c, rows=None):
     scale = 1.0 / math.sqrt(D)
     O = np.zeros((B, H, len(rows), D), dtype=np.float64)
     lse = np.full((B, H, len(rows)), -np.inf, dtype=np.float64)
-    for h in range(H):
+    for h in _heads(H, heads):
         kind = head_kind(h)
         for ri, t in enumerate(rows):
             S = key_set(pattern, kind, int(t), T, l, c)
@@ -198,13 +203,13 @@ def backward(q, k, v, dO, pattern, l, c):
     return dq, dk, dv
 
 
-def backward_dq_rows(q, k, v, dO, pattern, l, c, rows):
+def backward_dq_rows(q, k, v, dO, pattern, l, c, rows, heads=None):
     """dq at the given query positions only: float64 [B, H, R, D]."""
     B, H, T, D = q.shape
     scale = 1.0 / math.sqrt(D)
     rows = np.asarray(rows, dtype=np.int64)
     dq = np.zeros((B, H, len(rows), D), dtype=np.float64)
-    for h in range(H):
+    for h in _heads(H, heads):
         kind = head_kind(h)
         for ri, t in enumerate(rows):
             S = key_set(pattern, kind, int(t), T, l, c)
@@ -219,7 +224,7 @@ def backward_dq_rows(q, k, v, dO, pattern, l, c, rows):
     return dq
 
 
-def backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys):
+def backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys, heads=None):
     """dk, dv at the given key positions only: two float64 arrays [B, H, K, D].
 
     Every query that attends a sampled key is recomputed in full (its own key
@@ -230,7 +235,7 @@ def backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys):
     keys = np.asarray(keys, dtype=np.int64)
     dk = np.zeros((B, H, len(keys), D), dtype=np.float64)
     dv = np.zeros((B, H, len(keys), D), dtype=np.float64)
-    for h in range(H):
+    for h in _heads(H, heads):
         kind = head_kind(h)
         for ki, j in enumerate(keys):
             for t in queries_of_key(pattern, kind, int(j), T, l, c):

@@ -1,0 +1,79 @@
+"""The C-ABI library loads and exports every entry point include/st.h declares.
+
+Host only: argument errors are raised by the library's own checks before any
+HIP call, so they can be exercised without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "st.h")
+LIB = os.path.join(ROOT, "factorized_sparse_self_amd", "libst.so")
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libst.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(st_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("st_layout_build", "st_sparse_attn_fwd", "st_sparse_attn_bwd", "st_sparse_attn_fwd_f32",
+              "st_sparse_attn_bwd_f32", "st_layout_csr", "st_layout_csc", "st_layout_maps"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    from factorized_sparse_self_amd import EXPORTED
+    assert sorted(EXPORTED) == declared_functions()
+
+
+def test_status_strings_and_block_size():
+    from factorized_sparse_self_amd import lib
+    L = lib()
+    assert L.st_block_size() == 64
+    assert L.st_status_string(0) == b"ok"
+    assert L.st_status_string(-2) == b"unsupported configuration"
+
+
+def _call_fwd(name, ptr, B=1, H=2, T=64, D=64, pattern=0, l=8, c=0):
+    from factorized_sparse_self_amd import lib
+    return getattr(lib(), name)(ptr, ptr, ptr, ptr, ptr, B, H, T, D, pattern, l, c, None)
+
+
+@pytest.mark.parametrize("name", ["st_sparse_attn_fwd", "st_sparse_attn_fwd_f32"])
+def test_attention_argument_errors_without_gpu(name):
+    from factorized_sparse_self_amd import lib
+    fake = 1 << 20  # aligned, never dereferenced: every case fails the checks first
+    assert _call_fwd(name, None) == -1
+    assert _call_fwd(name, fake + 8) == -1          # misaligned
+    assert _call_fwd(name, fake, B=0) == -1
+    assert _call_fwd(name, fake, T=0) == -1
+    assert _call_fwd(name, fake, pattern=7) == -1
+    assert _call_fwd(name, fake, pattern=1, c=0) == -1
+    assert _call_fwd(name, fake, pattern=1, l=4, c=5) == -1
+    assert _call_fwd(name, fake, D=48) == -2
+    assert _call_fwd(name, fake, D=128) == -2
+    assert b"D must be 32 or 64" in lib().st_last_error()
+
+
+def test_backward_argument_errors_without_gpu():
+    from factorized_sparse_self_amd import lib
+    L = lib()
+    fake = 1 << 20
+    args = [fake] * 9
+    assert L.st_sparse_attn_bwd(*args, 1, 2, 64, 48, 0, 8, 0, None) == -2
+    args[5] = None
+    assert L.st_sparse_attn_bwd(*args, 1, 2, 64, 64, 0, 8, 0, None) == -1
+    assert b"pointer 5" in L.st_last_error()
