@@ -7,6 +7,8 @@
 //   dp_tj = dO_t . v_j,        ds_tj = p_tj (dp_tj - Delta_t),
 //   dq_t = sum_j ds_tj k_j / sqrt(D),  dk_j = sum_t ds_tj q_t / sqrt(D),
 //   dv_j = sum_t p_tj dO_t.
+// P and dS enter the dV, dK and dQ products as bf16 hi + lo pairs (about 16
+// significant bits), so those sums are not limited by bf16's 8-bit rounding.
 // Kernels (one stream, in order):
 //   pre   Delta for every row; zero dk / dv at positions no query attends
 //   dq    per row block over the CSR (no cross-item reduction)
@@ -223,11 +225,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-        const bf16x8 bs = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
+        bf16x8 bs_hi, bs_lo;
+        split_b_operand(s[2 * kk], s[2 * kk + 1], bs_hi, bs_lo);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           const bf16* row = Kt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
-          acc[d] = mfma_bf16(concat(*(const bf16x4*)row, *(const bf16x4*)(row + 16)), bs, acc[d]);
+          const bf16x8 ak = concat(*(const bf16x4*)row, *(const bf16x4*)(row + 16));
+          acc[d] = mfma_bf16(ak, bs_hi, acc[d]);
+          acc[d] = mfma_bf16(ak, bs_lo, acc[d]);
         }
       }
     } else {
@@ -412,14 +417,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-        const bf16x8 bp = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
-        const bf16x8 bd = pack_b_operand(dp[2 * kk], dp[2 * kk + 1]);
+        bf16x8 bp_hi, bp_lo, bd_hi, bd_lo;
+        split_b_operand(s[2 * kk], s[2 * kk + 1], bp_hi, bp_lo);
+        split_b_operand(dp[2 * kk], dp[2 * kk + 1], bd_hi, bd_lo);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           const bf16* rg = Gt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
           const bf16* rq = Qt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
-          dv[d] = mfma_bf16(concat(*(const bf16x4*)rg, *(const bf16x4*)(rg + 16)), bp, dv[d]);
-          dk[d] = mfma_bf16(concat(*(const bf16x4*)rq, *(const bf16x4*)(rq + 16)), bd, dk[d]);
+          const bf16x8 ag = concat(*(const bf16x4*)rg, *(const bf16x4*)(rg + 16));
+          const bf16x8 aq = concat(*(const bf16x4*)rq, *(const bf16x4*)(rq + 16));
+          dv[d] = mfma_bf16(ag, bp_hi, dv[d]);
+          dv[d] = mfma_bf16(ag, bp_lo, dv[d]);
+          dk[d] = mfma_bf16(aq, bd_hi, dk[d]);
+          dk[d] = mfma_bf16(aq, bd_lo, dk[d]);
         }
       }
     } else {
