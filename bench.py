@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the factorized sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+st_sparse_attn_fwd followed by st_sparse_attn_bwd (Delta preprocess, dq,
+dk/dv and the split reduction), with the block LUTs and schedules already
+cached (their one-off build time is reported separately).  The default
+workload is the fixed pattern at T = 12288 with forward + recompute backward
+(B=4, H=8, l=128, c=8, D=64, bf16), the configuration the headline metric
+(useful fwd+bwd TFLOP/s and tokens/s at T=12288) is quoted on.
+
+Output: one JSON line.  ``value`` is useful TFLOP/s: 14*D*nnz FLOP per step
+(forward 4*D*nnz: QK^T and PV; backward 10*D*nnz: S recomputed, dP, dV, dQ,
+dK) over the step time, nnz = sum over heads of |S(t)|; masked or skipped
+work is never counted.  ``roofline`` describes the kernel with the largest
+time per step, timed with HIP events on its launch stream inside the timed
+region; ``cpu_baseline`` times the fp64 oracle on the host on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MI355X_HBM_GBS = 8000.0        # HBM3E peak, GB/s
+MI355X_BF16_TFLOPS = 2500.0    # dense bf16 MFMA peak, TFLOP/s
+MI355X_FP32_TFLOPS = 157.3     # dense fp32 MFMA peak, TFLOP/s
+
+
+# ---------------------------------------------------------------------------
+# Work accounting (closed forms per head kind)
+# ---------------------------------------------------------------------------
+
+def active_rows(pattern, kind, T, l, c):
+    """Query rows whose key set is non-empty."""
+    from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1
+    if pattern == ST_FIXED and kind == 1:
+        return max(0, T - l)
+    if pattern == ST_FIXED_R1 and kind == 1:
+        return max(0, T - (l - c))
+    return T
+
+
+def attended_keys(pattern, kind, T, l, c):
+    """Key positions some query attends."""
+    from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1
+    nb = -(-T // l)
+    if pattern == ST_FIXED and kind == 1:
+        return (nb - 1) * c
+    if pattern == ST_FIXED_R1 and kind == 1:
+        return sum(1 for b in range(nb) for o in range(c) if b * l + l - c + o < T)
+    return T
+
+
+def accounting(w):
+    """Per-kernel algorithmic bytes and useful FLOP for one step of workload w."""
+    from factorized_sparse_self_amd import st_layout_build
+    lay = st_layout_build(w.pattern, w.T, w.l, w.c)
+    E = 2 if w.dtype == "bf16" else 4
+    row = w.D * E
+    by = {"fwd": 0, "bwd_pre": 0, "bwd_dq": 0, "bwd_dkdv": 0, "bwd_reduce": 0}
+    pairs_total = 0
+    for h in range(w.H):
+        kind = h % 2
+        pairs = lay[kind]["pairs"]
+        rows = active_rows(w.pattern, kind, w.T, w.l, w.c)
+        keys = attended_keys(w.pattern, kind, w.T, w.l, w.c)
+        pairs_total += w.B * pairs
+        # forward: read q (active rows), k and v (attended keys); write out and lse (every row)
+        by["fwd"] += w.B * (rows * row + 2 * keys * row + w.T * (row + 4))
+        # preprocess: read out and dout, write Delta; zero dk and dv where no query attends
+        by["bwd_pre"] += w.B * (w.T * (2 * row + 4) + 2 * (w.T - keys) * row)
+        # dq: read q, dout, lse, Delta (active rows), k and v (keys); write dq (every row)
+        by["bwd_dq"] += w.B * (rows * (2 * row + 8) + 2 * keys * row + w.T * row)
+        # dk/dv: read q, dout, lse, Delta (active rows), k and v (keys); write dk and dv (keys)
+        by["bwd_dkdv"] += w.B * (rows * (2 * row + 8) + 4 * keys * row)
+    fl = {"fwd": 4 * w.D * pairs_total, "bwd_pre": 0, "bwd_dq": 6 * w.D * pairs_total,
+          "bwd_dkdv": 8 * w.D * pairs_total, "bwd_reduce": 0}
+    useful = (4 if not w.backward else 14) * w.D * pairs_total
+    return {"bytes": by, "flops": fl, "useful_flops": useful, "pairs": pairs_total,
+            "pairs_per_kind": [lay[0]["pairs"], lay[1]["pairs"]]}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def _oracle_unit(args):
+    wname, b, h0 = args
+    import torch
+    import oracle
+    from factorized_sparse_self_amd import inputs
+    w = inputs.WORKLOAD_BY_NAME[wname]
+    tensors = inputs.draw_workload(w)
+    arrs = [x[b:b + 1, h0:h0 + 2].to(torch.float64).numpy() for x in tensors]
+    t0 = time.perf_counter()
+    if w.backward:
+        oracle.backward(arrs[0], arrs[1], arrs[2], arrs[3], w.pattern, w.l, w.c)
+    else:
+        oracle.forward(arrs[0], arrs[1], arrs[2], w.pattern, w.l, w.c)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, acct, units):
+    """Time the oracle on `units` (batch, head-pair) slices, one worker process each."""
+    from factorized_sparse_self_amd import inputs  # noqa: F401
+    pairs = acct["pairs_per_kind"]
+    jobs = []
+    for b in range(w.B):
+        for h0 in range(0, w.H - 1, 2):
+            jobs.append((w.name, b, h0))
+    jobs = jobs[:units]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(jobs)) as pool:
+        per_unit = pool.map(_oracle_unit, jobs)
+    wall = time.perf_counter() - t0
+    flop_per_pair = (14 if w.backward else 4) * w.D
+    flops = len(jobs) * (pairs[0] + pairs[1]) * flop_per_pair
+    busy = max(per_unit)
+    return {
+        "value": flops / busy / 1e12, "unit": "TFLOP/s", "cores": len(jobs), "kind": "oracle",
+        "sample": (f"{len(jobs)} of {w.B * (w.H // 2)} (batch, head-pair) slices of {w.name}: "
+                   f"batch {jobs[0][1]}, heads {jobs[0][2]}-{jobs[-1][2] + 1}, full T={w.T}, "
+                   f"{'forward + backward' if w.backward else 'forward'}, fp64 numpy, one process "
+                   f"per slice; value = sampled useful FLOP / slowest slice time"),
+        "seconds_per_slice": [round(x, 3) for x in per_unit], "wall_s": round(wall, 3),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from committed rocprofv3 counter summaries
+# ---------------------------------------------------------------------------
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in ("st_fwd.hip", "st_bwd.hip", "st_device.hpp", "st_kernels.hpp", "st_geometry.hpp"):
+        with open(os.path.join(ROOT, "factorized_sparse_self_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/, or None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fixed_T12288_bf16_fwdbwd")
+    ap.add_argument("--cpu-units", type=int, default=8,
+                    help="(batch, head-pair) slices the oracle baseline times, one process each")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the sparse attention path is built and timed on a single "
+              "MI355X; runs on more than one GPU are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from factorized_sparse_self_amd import (inputs, st_sparse_attn_bwd, st_sparse_attn_fwd,
+                                            st_timing_enable, st_timing_read, st_timing_reset,
+                                            KERNEL_NAMES, st_layout_build)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = inputs.WORKLOAD_BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    st_layout_build(w.pattern, w.T, w.l, w.c)
+    layout_ms = (time.perf_counter() - t0) * 1e3
+    acct = accounting(w)
+
+    tensors = [x.to(dev) for x in inputs.draw_workload(w)]
+    q, k, v = tensors[:3]
+    do = tensors[3] if w.backward else None
+    out = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.T, dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        st_sparse_attn_fwd(q, k, v, w.pattern, w.l, w.c, out=out, lse=lse)
+        if w.backward:
+            st_sparse_attn_bwd(q, k, v, out, lse, do, w.pattern, w.l, w.c, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    st_timing_reset()
+    st_timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    st_timing_enable(False)
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kernels = {}
+    for name in KERNEL_NAMES:
+        n, tot = st_timing_read(name)
+        if n:
+            kernels[name] = {"launches_per_step": n / args.steps, "avg_ms": tot / n,
+                             "ms_per_step": tot / args.steps}
+
+    useful_tflops = acct["useful_flops"] / (ms_per_step * 1e-3) / 1e12
+    tokens_per_s = w.B * w.T / (ms_per_step * 1e-3)
+    dom = max(kernels, key=lambda k_: kernels[k_]["ms_per_step"])
+    dur_s = kernels[dom]["avg_ms"] * 1e-3
+    dom_bytes = acct["bytes"][dom]
+    dom_flops = acct["flops"][dom]
+    peak_flops = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
+    ridge = peak_flops * 1e12 / (MI355X_HBM_GBS * 1e9)
+    ai = dom_flops / dom_bytes if dom_bytes else float("inf")
+    if ai < ridge:
+        achieved, peak, unit, bound = dom_bytes / dur_s / 1e9, MI355X_HBM_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = dom_flops / dur_s / 1e12, peak_flops, "TFLOP/s", "mfma"
+    roofline = {
+        "kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+        "frac": round(achieved / peak, 4), "traffic": measured_traffic(dom, w.name),
+        "algorithmic_bytes": dom_bytes, "useful_flops": dom_flops, "avg_ms": round(kernels[dom]["avg_ms"], 4),
+        "useful_tflops": round(dom_flops / dur_s / 1e12, 2),
+        "mfma_frac": round(dom_flops / dur_s / 1e12 / peak_flops, 4),
+    }
+
+    result = {
+        "metric": "sparse-attn fwd+bwd useful TFLOP/s & tokens/s at T=12288, % of bf16 MFMA peak",
+        "value": round(useful_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pattern": inputs.PATTERN_NAMES[w.pattern], "B": w.B, "H": w.H,
+                   "T": w.T, "D": w.D, "l": w.l, "c": w.c, "passes": "fwd+bwd" if w.backward else "fwd",
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "pct_bf16_mfma_peak": round(100 * useful_tflops / MI355X_BF16_TFLOPS, 3),
+        "useful_gflop_per_step": round(acct["useful_flops"] / 1e9, 3),
+        "nnz_pairs": acct["pairs"],
+        "kernels": {k_: {kk: round(vv, 5) for kk, vv in v_.items()} for k_, v_ in kernels.items()},
+        "layout_build_ms": round(layout_ms, 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, acct, args.cpu_units)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,9 @@ _SIG = {
     "st_sparse_attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "st_sparse_attn_bwd": (_I, [_P] * 9 + [_I] * 7 + [_P]),
     "st_sparse_attn_bwd_f32": (_I, [_P] * 9 + [_I] * 7 + [_P]),
+    "st_timing_enable": (_I, [_I]),
+    "st_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
+    "st_timing_reset": (None, []),
     "st_block_size": (_I, []),
     "st_status_string": (ctypes.c_char_p, [_I]),
     "st_last_error": (ctypes.c_char_p, []),
@@ -121,6 +124,25 @@ def st_block_size() -> int:
 
 def st_release() -> None:
     lib().st_release()
+
+
+KERNEL_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce")
+
+
+def st_timing_enable(on: bool) -> None:
+    _check("st_timing_enable", lib().st_timing_enable(1 if on else 0))
+
+
+def st_timing_reset() -> None:
+    lib().st_timing_reset()
+
+
+def st_timing_read(kernel: str) -> tuple[int, float]:
+    """(launches, summed milliseconds) of one kernel since the last reset."""
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    _check("st_timing_read", lib().st_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 # ---------------------------------------------------------------------------

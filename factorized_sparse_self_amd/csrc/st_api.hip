@@ -322,7 +322,74 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   return ST_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Launch timing: event pairs recorded around each launch while enabled.
+// ---------------------------------------------------------------------------
+struct TimingRecord {
+  int kid;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_timing_mutex;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_timing_records;
+std::vector<hipEvent_t> g_event_pool;
+TimingRecord g_open[KID_COUNT];
+bool g_is_open[KID_COUNT] = {};
+int64_t g_launches[KID_COUNT] = {};
+double g_total_ms[KID_COUNT] = {};
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Fold completed records into the per-kernel totals (caller holds the mutex).
+int drain_records() {
+  for (const TimingRecord& r : g_timing_records) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail("st_timing_read", e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail("st_timing_read", e);
+    g_launches[r.kid] += 1;
+    g_total_ms[r.kid] += ms;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_timing_records.clear();
+  return ST_OK;
+}
+
 }  // namespace
+
+const char* const kKernelNames[KID_COUNT] = {"fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce"};
+
+void timing_begin(int kid, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_timing_mutex);
+  g_is_open[kid] = false;
+  if (!g_timing_on) return;
+  TimingRecord r{kid, take_event(), take_event()};
+  if (!r.start || !r.stop) return;
+  if (hipEventRecord(r.start, stream) != hipSuccess) return;
+  g_open[kid] = r;
+  g_is_open[kid] = true;
+}
+
+void timing_end(int kid, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_timing_mutex);
+  if (!g_is_open[kid]) return;
+  g_is_open[kid] = false;
+  if (hipEventRecord(g_open[kid].stop, stream) != hipSuccess) return;
+  g_timing_records.push_back(g_open[kid]);
+}
+
 }  // namespace st
 
 using namespace st;
@@ -352,6 +419,41 @@ int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const vo
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_bwd<float>("st_sparse_attn_bwd_f32", q, k, v, out, lse, dout, dq, dk, dv, B, H, T,
                          D, pattern, l, c, stream);
+}
+
+int st_timing_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_timing_mutex);
+  g_timing_on = on != 0;
+  return ST_OK;
+}
+
+int st_timing_read(const char* kernel, int64_t* launches, double* total_ms) {
+  if (!kernel || !launches || !total_ms) {
+    set_error("st_timing_read: null argument");
+    return ST_ERR_INVALID;
+  }
+  int kid = -1;
+  for (int i = 0; i < KID_COUNT; ++i)
+    if (std::string(kernel) == kKernelNames[i]) kid = i;
+  if (kid < 0) {
+    set_error(std::string("st_timing_read: unknown kernel ") + kernel);
+    return ST_ERR_INVALID;
+  }
+  std::lock_guard<std::mutex> lock(g_timing_mutex);
+  const int rc = drain_records();
+  if (rc != ST_OK) return rc;
+  *launches = g_launches[kid];
+  *total_ms = g_total_ms[kid];
+  return ST_OK;
+}
+
+void st_timing_reset(void) {
+  std::lock_guard<std::mutex> lock(g_timing_mutex);
+  (void)drain_records();
+  for (int i = 0; i < KID_COUNT; ++i) {
+    g_launches[i] = 0;
+    g_total_ms[i] = 0.0;
+  }
 }
 
 void st_release(void) {

@@ -514,20 +514,31 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   constexpr int TPR = D / (16 / sizeof(TE));
   const int64_t rows = (int64_t)a.BH * a.T;
   const int64_t pre_blocks = (rows * TPR + kThreads - 1) / kThreads;
+  timing_begin(KID_PRE, stream);
   hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
   hipError_t err = hipGetLastError();
+  timing_end(KID_PRE, stream);
   if (err != hipSuccess) return err;
   if (n_dq > 0) {
+    timing_begin(KID_DQ, stream);
     hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = hipGetLastError();
+    timing_end(KID_DQ, stream);
+    if (err != hipSuccess) return err;
   }
   if (n_dkdv > 0) {
+    timing_begin(KID_DKDV, stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = hipGetLastError();
+    timing_end(KID_DKDV, stream);
+    if (err != hipSuccess) return err;
   }
   if (n_red > 0) {
+    timing_begin(KID_RED, stream);
     hipLaunchKernelGGL((bwd_reduce_kernel<TE, D>), dim3(n_red), dim3(kThreads), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = hipGetLastError();
+    timing_end(KID_RED, stream);
+    if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }

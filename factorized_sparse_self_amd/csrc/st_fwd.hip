@@ -252,8 +252,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 template <typename TE, int D>
 hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
+  timing_begin(KID_FWD, stream);
   hipLaunchKernelGGL((fwd_kernel<TE, D>), dim3(n_items), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  timing_end(KID_FWD, stream);
+  return err;
 }
 
 template hipError_t launch_fwd<bf16, 32>(const FwdArgs&, int, hipStream_t);

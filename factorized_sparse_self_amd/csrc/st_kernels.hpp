@@ -53,6 +53,14 @@ struct BwdArgs {
   float scale;  // 1 / sqrt(D)
 };
 
+// Kernel ids for the optional launch timing (names in kKernelNames).
+enum KernelId : int { KID_FWD = 0, KID_PRE, KID_DQ, KID_DKDV, KID_RED, KID_COUNT };
+extern const char* const kKernelNames[KID_COUNT];
+
+// Record timing events around a launch when timing is enabled (no-op otherwise).
+void timing_begin(int kid, hipStream_t stream);
+void timing_end(int kid, hipStream_t stream);
+
 template <typename TE, int D>
 hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream);
 

@@ -165,6 +165,19 @@ int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const vo
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Kernel timing (diagnostics; not part of the computation).  While enabled,
+ * every kernel the library launches is bracketed by two HIP events recorded
+ * on its launch stream.  st_timing_read() waits for those events and returns,
+ * for one kernel, the number of launches and their summed duration in
+ * milliseconds since the last st_timing_reset().  Kernel names: "fwd",
+ * "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce".  Unknown names give
+ * ST_ERR_INVALID; a failing event call gives ST_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+int st_timing_enable(int on);
+int st_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+void st_timing_reset(void);
+
+/* ---------------------------------------------------------------------------
  * Utilities.
  * ------------------------------------------------------------------------- */
 int st_block_size(void);                 /* block size of the LUTs (64)              */
