@@ -24,6 +24,12 @@ COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax reads them with VALU, and the
+    # AGPR form would copy every fragment across register files
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # no NaN inputs are assumed (infinities are kept: masked logits are -inf),
+    # which drops the NaN-quieting copies IEEE mode adds around every max
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 

@@ -72,6 +72,41 @@ struct Blob {
   }
 };
 
+// Workgroup i of a launch is dispatched to XCD (i mod kXcds); each XCD has its
+// own L2.  Items are grouped by the inputs they share, groups are assigned to
+// XCDs longest-first (balancing total cost), each XCD's queue runs longest
+// first, and queue x fills workgroup ids x, x + kXcds, ...  Short queues are
+// padded with -1 (an empty item).
+constexpr int kXcds = 8;
+// Aim for at least this many groups so that every XCD gets several.
+constexpr int kMinGroups = 64;
+
+std::vector<int> xcd_order(const std::vector<int64_t>& cost, const std::vector<int64_t>& group) {
+  const size_t n = cost.size();
+  std::map<int64_t, int64_t> gcost;
+  for (size_t i = 0; i < n; ++i) gcost[group[i]] += cost[i];
+  std::vector<std::pair<int64_t, int64_t>> gs(gcost.begin(), gcost.end());  // (group, cost)
+  std::stable_sort(gs.begin(), gs.end(), [](const auto& x, const auto& y) { return x.second > y.second; });
+  std::map<int64_t, int> gxcd;
+  int64_t load[kXcds] = {};
+  for (const auto& gc : gs) {
+    const int x = (int)(std::min_element(load, load + kXcds) - load);
+    gxcd[gc.first] = x;
+    load[x] += gc.second;
+  }
+  std::vector<std::vector<int>> q(kXcds);
+  for (size_t i = 0; i < n; ++i) q[gxcd[group[i]]].push_back((int)i);
+  size_t maxlen = 0;
+  for (auto& v : q) {
+    std::stable_sort(v.begin(), v.end(), [&](int x, int y) { return cost[x] > cost[y]; });
+    maxlen = std::max(maxlen, v.size());
+  }
+  std::vector<int> order(kXcds * maxlen, -1);
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t j = 0; j < q[x].size(); ++j) order[j * kXcds + x] = q[x][j];
+  return order;
+}
+
 int build_plan(const PlanKey& key, Plan* plan) {
   st_layout lay;
   lay.pattern = key.pattern;
@@ -83,54 +118,67 @@ int build_plan(const PlanKey& key, Plan* plan) {
     build_kind(lay.kind[kind]);
   }
   const int BH = key.B * key.H;
+  const int chunks_per_head = std::max(1, (kMinGroups + BH - 1) / BH);
+  int chunk[2];
+  for (int kind = 0; kind < 2; ++kind)
+    chunk[kind] = std::max(1, (lay.kind[kind].n_qb + chunks_per_head - 1) / chunks_per_head);
 
-  // Row-block items (forward and dq): every row block of every head, the
-  // longest (most key blocks) first so the tail of the grid is short.
-  struct RowItem {
-    int qb, bh, cost;
-  };
-  std::vector<RowItem> rows;
+  // Row-block items (forward and dq): every row block of every head; cost =
+  // key blocks visited + 1; grouped by (head, range of row blocks).
+  std::vector<int2> rows;
+  std::vector<int64_t> rcost, rgroup;
   for (int bh = 0; bh < BH; ++bh) {
-    const KindLayout& L = lay.kind[(bh % key.H) & 1];
-    for (int qb = 0; qb < L.n_qb; ++qb)
-      rows.push_back({qb, bh, L.row_ptr[qb + 1] - L.row_ptr[qb] + 1});
+    const int kind = (bh % key.H) & 1;
+    const KindLayout& L = lay.kind[kind];
+    for (int qb = 0; qb < L.n_qb; ++qb) {
+      rows.push_back(make_int2(qb, bh));
+      rcost.push_back(L.row_ptr[qb + 1] - L.row_ptr[qb] + 1);
+      rgroup.push_back((int64_t)bh * 65536 + qb / chunk[kind]);
+    }
   }
-  std::stable_sort(rows.begin(), rows.end(),
-                   [](const RowItem& x, const RowItem& y) { return x.cost > y.cost; });
-  std::vector<int2> row_items(rows.size());
-  for (size_t i = 0; i < rows.size(); ++i) row_items[i] = make_int2(rows[i].qb, rows[i].bh);
+  std::vector<int2> row_items;
+  for (int i : xcd_order(rcost, rgroup)) row_items.push_back(i < 0 ? make_int2(-1, -1) : rows[i]);
 
-  // dK/dV items: every key block of every head, split when long.
+  // dK/dV items: every key block of every head.  A key block whose row-block
+  // list is longer than kDkdvSplit is split at row-block multiples of
+  // kDkdvSplit, so that the splits of different key blocks read the same row
+  // blocks; grouped by (head, first row block read).
   std::vector<DkdvItem> dkdv;
+  std::vector<int64_t> dcost, dgroup;
   std::vector<ReduceItem> red;
   int slots = 0;
   for (int bh = 0; bh < BH; ++bh) {
-    const KindLayout& L = lay.kind[(bh % key.H) & 1];
+    const int kind = (bh % key.H) & 1;
+    const KindLayout& L = lay.kind[kind];
     for (int kb = 0; kb < L.n_kb; ++kb) {
-      const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1], n = e1 - e0;
-      const int nsplit = std::max(1, (n + kDkdvSplit - 1) / kDkdvSplit);
-      if (nsplit == 1) {
+      const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
+      const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
+      if (e1 - e0 <= kDkdvSplit) {
         dkdv.push_back({kb, bh, e0, e1, -1, 0, 0, 0});
+        dcost.push_back(e1 - e0 + 1);
+        dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
         continue;
       }
-      const int chunk = (n + nsplit - 1) / nsplit;
-      int used = 0;
-      for (int s = 0; s < nsplit; ++s) {
-        const int a = e0 + s * chunk, b = std::min(e1, a + chunk);
-        dkdv.push_back({kb, bh, a, b, slots + s, 0, 0, 0});
-        ++used;
+      const int slot0 = slots;
+      for (int a = e0; a < e1;) {
+        const int range = L.row_idx[a] / kDkdvSplit;
+        int b = a;
+        while (b < e1 && L.row_idx[b] / kDkdvSplit == range) ++b;
+        dkdv.push_back({kb, bh, a, b, slots++, 0, 0, 0});
+        dcost.push_back(b - a + 1);
+        dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);
+        a = b;
       }
-      red.push_back({kb, bh, slots, used});
-      slots += used;
+      red.push_back({kb, bh, slot0, slots - slot0});
     }
   }
-  std::stable_sort(dkdv.begin(), dkdv.end(),
-                   [](const DkdvItem& x, const DkdvItem& y) { return x.e1 - x.e0 > y.e1 - y.e0; });
-
+  std::vector<DkdvItem> dkdv_items;
+  for (int i : xcd_order(dcost, dgroup))
+    dkdv_items.push_back(i < 0 ? DkdvItem{-1, -1, 0, 0, -1, 0, 0, 0} : dkdv[i]);
   Blob blob;
   KindDev kinds_host[2];
   size_t off_kinds = blob.add(kinds_host, sizeof(kinds_host));
-  size_t offs[2][6];
+  size_t offs[2][8];
   for (int kind = 0; kind < 2; ++kind) {
     const KindLayout& L = lay.kind[kind];
     offs[kind][0] = blob.add(L.row_ptr.data(), L.row_ptr.size() * 4);
@@ -139,9 +187,14 @@ int build_plan(const PlanKey& key, Plan* plan) {
     offs[kind][3] = blob.add(L.col_ptr.data(), L.col_ptr.size() * 4);
     offs[kind][4] = blob.add(L.row_idx.data(), L.row_idx.size() * 4);
     offs[kind][5] = blob.add(L.csc_flags.data(), L.csc_flags.size());
+    std::vector<uint32_t> csr(L.col_idx.size()), csc(L.row_idx.size());
+    for (size_t e = 0; e < csr.size(); ++e) csr[e] = (uint32_t)L.col_idx[e] | (L.flags[e] ? kFullBit : 0u);
+    for (size_t e = 0; e < csc.size(); ++e) csc[e] = (uint32_t)L.row_idx[e] | (L.csc_flags[e] ? kFullBit : 0u);
+    offs[kind][6] = blob.add(csr.data(), csr.size() * 4);
+    offs[kind][7] = blob.add(csc.data(), csc.size() * 4);
   }
   const size_t off_rows = blob.add(row_items.data(), row_items.size() * sizeof(int2));
-  const size_t off_dkdv = blob.add(dkdv.data(), dkdv.size() * sizeof(DkdvItem));
+  const size_t off_dkdv = blob.add(dkdv_items.data(), dkdv_items.size() * sizeof(DkdvItem));
   const size_t off_red = blob.add(red.data(), red.size() * sizeof(ReduceItem));
 
   hipError_t e = hipMalloc(&plan->dmem, blob.bytes.size());
@@ -161,6 +214,8 @@ int build_plan(const PlanKey& key, Plan* plan) {
     k.col_ptr = (const int32_t*)(dbase + offs[kind][3]);
     k.row_idx = (const int32_t*)(dbase + offs[kind][4]);
     k.csc_flags = (const uint8_t*)(dbase + offs[kind][5]);
+    k.csr_entry = (const uint32_t*)(dbase + offs[kind][6]);
+    k.csc_entry = (const uint32_t*)(dbase + offs[kind][7]);
   }
   std::memcpy(blob.bytes.data() + off_kinds, kinds_host, sizeof(kinds_host));
   e = hipMemcpy(plan->dmem, blob.bytes.data(), blob.bytes.size(), hipMemcpyHostToDevice);
@@ -170,7 +225,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   plan->dkdv_items = (DkdvItem*)(dbase + off_dkdv);
   plan->red_items = (ReduceItem*)(dbase + off_red);
   plan->n_row_items = (int)row_items.size();
-  plan->n_dkdv_items = (int)dkdv.size();
+  plan->n_dkdv_items = (int)dkdv_items.size();
   plan->n_red_items = (int)red.size();
   plan->n_slots = slots;
   return ST_OK;

@@ -15,6 +15,8 @@
 //   dkdv  per key block over the CSC; key blocks with many row blocks are
 //         split, each split writing fp32 partials
 //   red   sums the partials of split key blocks
+#include <type_traits>
+
 #include "st_device.hpp"
 #include "st_kernels.hpp"
 
@@ -110,9 +112,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) TE Vs[L::R_ELEMS];
   __shared__ __attribute__((aligned(16))) TE Kt[L::T_ELEMS];
 
-  const int2 item = a.dq_items[blockIdx.x];
+  const int2 item = load_uniform(&a.dq_items[blockIdx.x]);
+  if (item.x < 0) return;  // schedule padding
   const int qb = item.x, bh = item.y;
-  const KindDev kd = a.kinds[(bh % a.H) & 1];
+  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
   const Geometry& g = kd.geo;
   const size_t base = (size_t)bh * a.T * D;
   const TE* __restrict__ Qg = (const TE*)a.q + base;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
 
-  const int e0 = kd.row_ptr[qb], e1 = kd.row_ptr[qb + 1];
+  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
   for (int e = e0; e < e1; ++e) {
     const int kb = kd.col_idx[e];
     const bool full = kd.flags[e] != 0;
@@ -280,9 +283,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) int los[kBlock];
   __shared__ __attribute__((aligned(16))) int his[kBlock];
 
-  const DkdvItem item = a.dkdv_items[blockIdx.x];
+  const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
+  if (item.kb < 0) return;  // schedule padding
   const int kb = item.kb, bh = item.bh;
-  const KindDev kd = a.kinds[(bh % a.H) & 1];
+  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
   const Geometry& g = kd.geo;
   const size_t base = (size_t)bh * a.T * D;
   const TE* __restrict__ Qg = (const TE*)a.q + base;
@@ -476,12 +480,338 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 dq and dk/dv.  As in the forward: the streamed blocks (K and V for dq;
+// Q and dO with their lse, Delta and key runs for dk/dv) are staged row-major
+// in double-buffered LDS with the next block's buffer loads in flight (padding
+// rows read as zeros); FULL blocks run without masks; every transposed MFMA
+// operand (K^T, Q^T, dO^T) comes from LDS transpose reads.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
+  constexpr int P = D + 16, NQ = D / 32, ND = D / 16, CH = D / 8;  // pitch as in the forward
+  constexpr int NLD = kBlock * CH / kThreads;
+  constexpr int RSTEP = kThreads / CH;
+  static_assert(NLD >= 1 && kBlock * CH % kThreads == 0, "staging layout");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * P];
+
+  const int2 item = load_uniform(&a.dq_items[blockIdx.x]);
+  if (item.x < 0) return;  // schedule padding
+  const int qb = item.x, bh = item.y;
+  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
+  const Geometry& g = kd.geo;
+  const size_t base = (size_t)bh * a.T * D;
+  const uint32_t head_bytes = (uint32_t)a.T * D * 2;
+  const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
+  const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
+  const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
+  const Rsrc rg = make_rsrc((const bf16*)a.dout + base, head_bytes);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int t = block_position(g, false, qb, wave * 16 + li);
+  int lo = 1, hi = 0;
+  if (t >= 0) row_interval(g, qb * kBlock + wave * 16 + li, t, lo, hi);
+  const bool row_live = lo <= hi;
+  const int wlo = uniform(wave_min(row_live ? lo : 0x7fffffff));
+  const int whi = uniform(wave_max(row_live ? hi : -1));
+  const int mlo = row_live ? lo : -(1 << 30);
+  const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
+  float lse2 = 0.f, delta = 0.f;
+  if (row_live) {
+    lse2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
+    delta = a.delta[(size_t)bh * a.T + t];
+  }
+  bf16x8 qop[NQ], gop[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const uint32_t off = t >= 0 ? (uint32_t)(t * D + 32 * s + 8 * lg) * 2 : kOutOfRange;
+    qop[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    gop[s] = __builtin_bit_cast(bf16x8, buf_load16(rg, off));
+  }
+  f32x4 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.sl2;
+
+  uint4 kr[NLD], vr[NLD];
+  const int srow = tid / CH, sch = tid % CH;
+  const StageRows<NLD, RSTEP> stage(g, true, srow);
+  auto gload = [&](int kb) {
+    int p[NLD];
+    stage.positions(g, true, kb, p);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t off = p[i] >= 0 ? (uint32_t)(p[i] * D + sch * 8) * 2 : kOutOfRange;
+      kr[i] = buf_load16(rk, off);
+      vr[i] = buf_load16(rv, off);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int off = (srow + i * RSTEP) * P + sch * 8;
+      *(uint4*)(&Ks[buf][off]) = kr[i];
+      *(uint4*)(&Vs[buf][off]) = vr[i];
+    }
+  };
+
+  auto block = [&](auto full_c, const bf16* Kb, const bf16* Vb, int kb) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int k0 = kb * kBlock;
+    bool need[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) need[b] = FULL || (k0 + 16 * b <= whi && k0 + 16 * b + 15 >= wlo);
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      s[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (!need[b]) continue;
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        s[b] = mfma_bf16(*(const bf16x8*)(Kb + (16 * b + li) * P + 32 * k + 8 * lg), qop[k], s[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(Vb + (16 * b + li) * P + 32 * k + 8 * lg), gop[k], dp[b]);
+      }
+    }
+    const int m0 = k0 + 4 * lg - mlo;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = fast_exp2(fmaf(s[b][i], sl2, -lse2));
+        if (!FULL && (uint32_t)(m0 + 16 * b + i) > mspan) p = 0.f;
+        s[b][i] = p * (dp[b][i] - delta);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (!need[2 * kk] && !need[2 * kk + 1]) continue;
+      bf16x8 hi8, lo8;
+      split_b_operand(s[2 * kk], s[2 * kk + 1], hi8, lo8);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const bf16x8 ak = tr_a_operand(Kb, P, 32 * kk, 16 * d, li, lg);
+        acc[d] = mfma_bf16(ak, hi8, acc[d]);
+        acc[d] = mfma_bf16(ak, lo8, acc[d]);
+      }
+    }
+  };
+
+  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
+  if (e0 < e1) gload((int)(as_const(kd.csr_entry)[e0] & ~kFullBit));
+  for (int e = e0, buf = 0; e < e1; ++e, buf ^= 1) {
+    const uint32_t entry = as_const(kd.csr_entry)[e];
+    const int kb = (int)(entry & ~kFullBit);
+    const bool full = (entry & kFullBit) != 0;
+    lstore(buf);
+    __syncthreads();
+    if (e + 1 < e1) gload((int)(as_const(kd.csr_entry)[e + 1] & ~kFullBit));
+    if (whi < 0) continue;
+    if (full)
+      block(std::true_type(), Ks[buf], Vs[buf], kb);
+    else
+      block(std::false_type(), Ks[buf], Vs[buf], kb);
+  }
+  if (t < 0) return;
+  bf16* dq = (bf16*)a.dq + base + (size_t)t * D;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) *(bf16x4*)(dq + 16 * d + 4 * lg) = to_bf16x4(acc[d] * a.scale);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int P = D + 16, NQ = D / 32, ND = D / 16, CH = D / 8;  // pitch as in the forward
+  constexpr int NLD = kBlock * CH / kThreads;
+  constexpr int RSTEP = kThreads / CH;
+  static_assert(NLD >= 1 && kBlock * CH % kThreads == 0, "staging layout");
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][kBlock * P];
+  __shared__ __attribute__((aligned(16))) bf16 Gs[2][kBlock * P];
+  __shared__ __attribute__((aligned(16))) float lse2s[2][kBlock];
+  __shared__ __attribute__((aligned(16))) float dels[2][kBlock];
+  __shared__ __attribute__((aligned(16))) int los[2][kBlock];     // masking base of each row
+  __shared__ __attribute__((aligned(16))) int spans[2][kBlock];   // masking span (unsigned)
+
+  const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
+  if (item.kb < 0) return;  // schedule padding
+  const int kb = item.kb, bh = item.bh;
+  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
+  const Geometry& g = kd.geo;
+  const size_t base = (size_t)bh * a.T * D;
+  const uint32_t head_bytes = (uint32_t)a.T * D * 2;
+  const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
+  const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
+  const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
+  const Rsrc rg = make_rsrc((const bf16*)a.dout + base, head_bytes);
+  const Rsrc rl = make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4);
+  const Rsrc rd = make_rsrc(a.delta + (size_t)bh * a.T, (uint32_t)a.T * 4);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int Kw0 = kb * kBlock + wave * 16;
+  const int Kl = Kw0 + li;
+  const int kp = block_position(g, true, kb, wave * 16 + li);
+  bf16x8 kop[NQ], vop[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const uint32_t off = kp >= 0 ? (uint32_t)(kp * D + 32 * s + 8 * lg) * 2 : kOutOfRange;
+    kop[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+    vop[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+  }
+  f32x4 dk[ND], dv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) dk[d] = dv[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.sl2;
+
+  uint4 qr[NLD], gr[NLD];
+  float sc_l2 = 0.f, sc_de = 0.f;
+  int sc_lo = 0, sc_span = 0;
+  const int srow = tid / CH, sch = tid % CH;
+  const StageRows<NLD, RSTEP> stage(g, false, srow);
+  const StageRows<1, kBlock> stage_row(g, false, tid & (kBlock - 1));
+  auto gload = [&](int qb) {
+    int p[NLD];
+    stage.positions(g, false, qb, p);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t off = p[i] >= 0 ? (uint32_t)(p[i] * D + sch * 8) * 2 : kOutOfRange;
+      qr[i] = buf_load16(rq, off);
+      gr[i] = buf_load16(rg, off);
+    }
+    if (tid < kBlock) {
+      int tp[1];
+      stage_row.positions(g, false, qb, tp);
+      const int t = tp[0];
+      int lo = 1, hi = 0;
+      if (t >= 0) row_interval(g, qb * kBlock + tid, t, lo, hi);
+      const bool live = lo <= hi;
+      sc_lo = live ? lo : -(1 << 30);
+      sc_span = live ? hi - lo : 0;
+      const uint32_t off = live ? (uint32_t)t * 4 : kOutOfRange;
+      sc_l2 = buf_load_f32(rl, off);
+      sc_de = buf_load_f32(rd, off);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int off = (srow + i * RSTEP) * P + sch * 8;
+      *(uint4*)(&Qs[buf][off]) = qr[i];
+      *(uint4*)(&Gs[buf][off]) = gr[i];
+    }
+    if (tid < kBlock) {
+      lse2s[buf][tid] = sc_l2 * kLog2e;
+      dels[buf][tid] = sc_de;
+      los[buf][tid] = sc_lo;
+      spans[buf][tid] = sc_span;
+    }
+  };
+
+  auto block = [&](auto full_c, int buf) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const bf16* Qb = Qs[buf];
+    const bf16* Gb = Gs[buf];
+    bool need[4] = {true, true, true, true};
+    if (!FULL) {
+      // which 16-row blocks hold a row whose key run meets this wave's 16 keys
+      const int rlo = los[buf][lane];
+      const uint32_t rspan = (uint32_t)spans[buf][lane];
+      const bool meets = rlo <= Kw0 + 15 && (int64_t)rlo + rspan >= Kw0 && rlo > -(1 << 30);
+      const uint64_t hit = __ballot(meets);
+      if (hit == 0) return;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) need[b] = ((hit >> (16 * b)) & 0xffffull) != 0;
+    }
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      s[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (!need[b]) continue;
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        s[b] = mfma_bf16(*(const bf16x8*)(Qb + (16 * b + li) * P + 32 * k + 8 * lg), kop[k], s[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(Gb + (16 * b + li) * P + 32 * k + 8 * lg), vop[k], dp[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r0 = 16 * b + 4 * lg;
+      const float4 l2 = *(const float4*)(&lse2s[buf][r0]);
+      const float4 de = *(const float4*)(&dels[buf][r0]);
+      const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float dea[4] = {de.x, de.y, de.z, de.w};
+      int loa[4] = {0, 0, 0, 0}, spa[4] = {0, 0, 0, 0};
+      if (!FULL) {
+        const int4 lo4 = *(const int4*)(&los[buf][r0]);
+        const int4 sp4 = *(const int4*)(&spans[buf][r0]);
+        loa[0] = lo4.x; loa[1] = lo4.y; loa[2] = lo4.z; loa[3] = lo4.w;
+        spa[0] = sp4.x; spa[1] = sp4.y; spa[2] = sp4.z; spa[3] = sp4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = fast_exp2(fmaf(s[b][i], sl2, -l2a[i]));
+        if (!FULL && (uint32_t)(Kl - loa[i]) > (uint32_t)spa[i]) p = 0.f;
+        s[b][i] = p;
+        dp[b][i] = p * (dp[b][i] - dea[i]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (!need[2 * kk] && !need[2 * kk + 1]) continue;
+      bf16x8 p_hi, p_lo, d_hi, d_lo;
+      split_b_operand(s[2 * kk], s[2 * kk + 1], p_hi, p_lo);
+      split_b_operand(dp[2 * kk], dp[2 * kk + 1], d_hi, d_lo);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const bf16x8 ag = tr_a_operand(Gb, P, 32 * kk, 16 * d, li, lg);
+        const bf16x8 aq = tr_a_operand(Qb, P, 32 * kk, 16 * d, li, lg);
+        dv[d] = mfma_bf16(ag, p_hi, dv[d]);
+        dv[d] = mfma_bf16(ag, p_lo, dv[d]);
+        dk[d] = mfma_bf16(aq, d_hi, dk[d]);
+        dk[d] = mfma_bf16(aq, d_lo, dk[d]);
+      }
+    }
+  };
+
+  if (item.e0 < item.e1) gload((int)(as_const(kd.csc_entry)[item.e0] & ~kFullBit));
+  for (int e = item.e0, buf = 0; e < item.e1; ++e, buf ^= 1) {
+    const bool full = (as_const(kd.csc_entry)[e] & kFullBit) != 0;
+    lstore(buf);
+    __syncthreads();
+    if (e + 1 < item.e1) gload((int)(as_const(kd.csc_entry)[e + 1] & ~kFullBit));
+    if (full)
+      block(std::true_type(), buf);
+    else
+      block(std::false_type(), buf);
+  }
+
+  if (item.slot < 0) {
+    if (kp < 0) return;
+    bf16* dkp = (bf16*)a.dk + base + (size_t)kp * D;
+    bf16* dvp = (bf16*)a.dv + base + (size_t)kp * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      *(bf16x4*)(dkp + 16 * d + 4 * lg) = to_bf16x4(dk[d] * a.scale);
+      *(bf16x4*)(dvp + 16 * d + 4 * lg) = to_bf16x4(dv[d]);
+    }
+  } else {
+    float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
+    float* pv = pk + kBlock * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 x = dk[d] * a.scale;
+      *(float4*)(pk + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
+      *(float4*)(pv + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // red: sum the fp32 partials of a split key block and store dk / dv.
 // ---------------------------------------------------------------------------
 template <typename TE, int D>
 __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
-  const ReduceItem item = a.red_items[blockIdx.x];
-  const KindDev kd = a.kinds[(item.bh % a.H) & 1];
+  const ReduceItem item = load_uniform(&a.red_items[blockIdx.x]);
+  if (item.kb < 0) return;  // schedule padding
+  const KindDev kd = load_uniform(&a.kinds[(item.bh % a.H) & 1]);
   const size_t base = (size_t)item.bh * a.T * D;
   constexpr int CH = D / 4;
   for (int u = threadIdx.x; u < 2 * kBlock * CH; u += kThreads) {
@@ -521,14 +851,20 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   if (err != hipSuccess) return err;
   if (n_dq > 0) {
     timing_begin(KID_DQ, stream);
-    hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
+    if constexpr (IsBf16<TE>::value)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
     timing_end(KID_DQ, stream);
     if (err != hipSuccess) return err;
   }
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+    if constexpr (IsBf16<TE>::value)
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
     timing_end(KID_DKDV, stream);
     if (err != hipSuccess) return err;

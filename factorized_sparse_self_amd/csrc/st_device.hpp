@@ -94,6 +94,100 @@ __device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
   return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes that
+// share lg, lane i receives element (i mod 4) of the 8-byte chunks addressed by
+// lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12.  If lane j addresses row
+// r0 + j/4, columns c0 + 4*(j mod 4) of a row-major tile, lane i therefore gets
+// column c0 + i of rows r0 .. r0 + 3: the transposed operand an MFMA needs,
+// read from a tile stored untransposed.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// A operand (rows c0 + li, 32 k-slots) of an MFMA whose k index runs over the
+// rows of a row-major LDS tile X[row][col] with pitch `pitch`: k-slots
+// 8*lg + e map to rows r0 + 4*lg + e (e < 4) and r0 + 16 + 4*lg + e - 4, the
+// same slot order as pack_b_operand() gives a pair of C fragments.
+__device__ __forceinline__ bf16x8 tr_a_operand(const bf16* X, int pitch, int r0, int c0, int li, int lg) {
+  const bf16* p = X + (r0 + 4 * lg + (li >> 2)) * pitch + c0 + 4 * (li & 3);
+  return concat(lds_read_tr(p), lds_read_tr(p + 16 * pitch));
+}
+
+__device__ __forceinline__ bool wave_any(bool v) { return __ballot(v) != 0ull; }
+
+// Read-only tables (LUTs, schedules) are read through the constant address
+// space: a uniform load from it is a scalar load, so values such as a block
+// index or its FULL flag stay in scalar registers and branches on them are
+// scalar branches.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ __forceinline__ cptr<T> as_const(const T* p) {
+  return (cptr<T>)p;
+}
+
+// The rows a thread stages from every 64-block: rows srow + i*RSTEP.  Their
+// per-row address parts are computed once; per block only the uniform block
+// part is added (or, for a summary map whose c does not divide the block,
+// the position is computed directly).
+template <int NLD, int RSTEP>
+struct StageRows {
+  int row[NLD], off[NLD];
+  bool split;
+  __device__ __forceinline__ StageRows(const Geometry& g, bool keys, int srow) {
+    split = split_position_ok(g, keys);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      row[i] = srow + i * RSTEP;
+      off[i] = split ? row_part(g, keys, row[i]).off : 0;
+    }
+  }
+  __device__ __forceinline__ void positions(const Geometry& g, bool keys, int blk, int (&p)[NLD]) const {
+    if (split) {
+      const BlockPart bp = block_part(g, keys, blk);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int q = bp.base + off[i];
+        p[i] = (row[i] < bp.limit && q < g.T) ? q : -1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) p[i] = block_position(g, keys, blk, row[i]);
+    }
+  }
+};
+
+// Load a (trivially copyable) struct from a read-only table with scalar loads.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "dword-sized struct");
+  struct Words {
+    uint32_t w[sizeof(T) / 4];
+  } tmp;
+  const cptr<uint32_t> q = (cptr<uint32_t>)p;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) tmp.w[i] = q[i];
+  return __builtin_bit_cast(T, tmp);
+}
+
+// Make a wave-uniform value explicit (scalar register).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Buffer resource over `bytes` bytes from `base` (bytes < 2^31).  Loads whose
+// offset lies outside the buffer return zeros, so padding rows need no branch.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
 __device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ int xor_shfl(int v, int m) { return __shfl_xor(v, m, 64); }
 
@@ -118,7 +212,11 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
-// One head kind on the device: geometry plus its LUT.
+// One head kind on the device: geometry plus its LUT.  Besides the byte flags,
+// each CSR / CSC entry is also packed as one dword, block index | FULL << 31,
+// so that a kernel reads both with one scalar load (a byte read would come
+// back in a vector register and make the FULL branch look divergent).
+constexpr uint32_t kFullBit = 0x80000000u;
 struct KindDev {
   Geometry geo;
   const int32_t* row_ptr;
@@ -127,6 +225,8 @@ struct KindDev {
   const int32_t* col_ptr;
   const int32_t* row_idx;
   const uint8_t* csc_flags;
+  const uint32_t* csr_entry;  // col_idx | flags << 31
+  const uint32_t* csc_entry;  // row_idx | csc_flags << 31
 };
 
 }  // namespace st

@@ -14,6 +14,8 @@
 // MFMA so each lane holds 16 logits of its own query; the online softmax keeps
 // the running max / sum in registers (cross-lane only over the 4 lanes of a
 // query); O^T += V^T P^T runs on MFMA with P packed to bf16 in registers.
+#include <type_traits>
+
 #include "st_device.hpp"
 #include "st_kernels.hpp"
 
@@ -94,10 +96,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TE Ks[L::K_ELEMS];
   __shared__ __attribute__((aligned(16))) TE Vs[L::V_ELEMS];
 
-  const int2 item = a.items[blockIdx.x];
+  const int2 item = load_uniform(&a.items[blockIdx.x]);
+  if (item.x < 0) return;  // schedule padding
   const int qb = item.x, bh = item.y;
   const int h = bh % a.H;
-  const KindDev kd = a.kinds[h & 1];
+  const KindDev kd = load_uniform(&a.kinds[h & 1]);
   const Geometry& g = kd.geo;
   const size_t base = (size_t)bh * a.T * D;
   const TE* __restrict__ Q = (const TE*)a.q + base;
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.sl2;
 
-  const int e0 = kd.row_ptr[qb], e1 = kd.row_ptr[qb + 1];
+  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
   for (int e = e0; e < e1; ++e) {
     const int kb = kd.col_idx[e];
     const bool full = kd.flags[e] != 0;
@@ -247,13 +250,185 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     a.lse[(size_t)bh * a.T + t] = lsum > 0.f ? (m_run * sl2 + fast_log2(lsum)) * kLn2 : -INFINITY;
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 forward.
+//  * K and V blocks are staged row-major in double-buffered LDS; the next
+//    block's global loads are issued before the current block is computed, so
+//    one barrier per block separates staging from use.  Loads go through
+//    buffer descriptors: padding rows get an out-of-range offset and read as
+//    zeros, with no branch.
+//  * FULL blocks take a straight path (no masks, no sub-block tests); PARTIAL
+//    blocks skip 16-key sub-blocks the wave does not need and mask the rest
+//    with one unsigned compare per logit.
+//  * The V^T operand of the P.V product comes from LDS transpose reads.
+//  * Online softmax: the row sum is fp32 (lse must be the log of the exact
+//    sum: the backward rebuilds P from it).  The running max is only raised
+//    when a logit exceeds it by more than 2^8 in exp2 units; blocks where no
+//    lane of the wave needs that skip the cross-lane max and the rescale.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
+  // LDS row pitch (elements): rows stay 16-byte aligned (a misaligned 128-bit
+  // LDS access is split by the hardware); a 32-byte pad keeps the transpose
+  // reads of four consecutive rows on disjoint banks
+  constexpr int P = D + 16;
+  constexpr int NQ = D / 32;                   // MFMA k-steps over D
+  constexpr int ND = D / 16;                   // 16-wide output column blocks
+  constexpr int CH = D / 8;                    // 16-byte chunks per row
+  constexpr int NLD = kBlock * CH / kThreads;  // chunks per thread per tensor
+  constexpr int RSTEP = kThreads / CH;         // rows between a thread's chunks
+  static_assert(NLD >= 1 && kBlock * CH % kThreads == 0, "staging layout");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * P];
+
+  const int2 item = load_uniform(&a.items[blockIdx.x]);
+  if (item.x < 0) return;  // schedule padding
+  const int qb = item.x, bh = item.y;
+  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
+  const Geometry& g = kd.geo;
+  const size_t base = (size_t)bh * a.T * D;
+  const uint32_t head_bytes = (uint32_t)a.T * D * 2;
+  const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
+  const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
+  const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int t = block_position(g, false, qb, wave * 16 + li);
+  int lo = 1, hi = 0;
+  if (t >= 0) row_interval(g, qb * kBlock + wave * 16 + li, t, lo, hi);
+  const bool row_live = lo <= hi;
+  const int wlo = uniform(wave_min(row_live ? lo : 0x7fffffff));
+  const int whi = uniform(wave_max(row_live ? hi : -1));
+  // logit of kernel key K is masked when (unsigned)(K - mlo) > mspan
+  const int mlo = row_live ? lo : -(1 << 30);
+  const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
+
+  bf16x8 qop[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s)
+    qop[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, t >= 0 ? (uint32_t)(t * D + 32 * s + 8 * lg) * 2 : kOutOfRange));
+
+  f32x4 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.sl2;
+  const float headroom = 8.0f / sl2;  // raw-logit growth allowed before a rescale
+  float m_run = -INFINITY, l_run = 0.f;
+
+  uint4 kr[NLD], vr[NLD];
+  const int srow = tid / CH, sch = tid % CH;
+  const StageRows<NLD, RSTEP> stage(g, true, srow);
+  auto gload = [&](int kb) {
+    int p[NLD];
+    stage.positions(g, true, kb, p);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t off = p[i] >= 0 ? (uint32_t)(p[i] * D + sch * 8) * 2 : kOutOfRange;
+      kr[i] = buf_load16(rk, off);
+      vr[i] = buf_load16(rv, off);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int off = (srow + i * RSTEP) * P + sch * 8;
+      *(uint4*)(&Ks[buf][off]) = kr[i];
+      *(uint4*)(&Vs[buf][off]) = vr[i];
+    }
+  };
+
+  auto block = [&](auto full_c, const bf16* Kb, const bf16* Vb, int kb) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int k0 = kb * kBlock;
+    bool need[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) need[b] = FULL || (k0 + 16 * b <= whi && k0 + 16 * b + 15 >= wlo);
+    f32x4 s[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      s[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (!need[b]) continue;
+#pragma unroll
+      for (int k = 0; k < NQ; ++k)
+        s[b] = mfma_bf16(*(const bf16x8*)(Kb + (16 * b + li) * P + 32 * k + 8 * lg), qop[k], s[b]);
+    }
+    if (!FULL) {
+      const int m0 = k0 + 4 * lg - mlo;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((uint32_t)(m0 + 16 * b + i) > mspan) s[b][i] = -INFINITY;
+    }
+    float lm = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) lm = fmaxf(fmaxf(lm, fmaxf(s[b][0], s[b][1])), fmaxf(s[b][2], s[b][3]));
+    if (wave_any(lm > m_run + headroom)) {
+      const float mt = group4_max(lm);
+      const bool raise = mt > m_run + headroom;
+      // raising rows scale by exp2((old - new) max), 0 when the old max is -inf;
+      // the others keep their sums (factor exactly 1, never -inf - -inf)
+      const float alpha = raise ? fast_exp2((m_run - mt) * sl2) : 1.f;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+      l_run *= alpha;
+      m_run = raise ? mt : m_run;
+    }
+    const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[b][i] = fast_exp2(fmaf(s[b][i], sl2, -mb));
+        l_run += s[b][i];
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (!need[2 * kk] && !need[2 * kk + 1]) continue;
+      const bf16x8 pb = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] = mfma_bf16(tr_a_operand(Vb, P, 32 * kk, 16 * d, li, lg), pb, acc[d]);
+    }
+  };
+
+  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
+  if (e0 < e1) gload((int)(as_const(kd.csr_entry)[e0] & ~kFullBit));
+  for (int e = e0, buf = 0; e < e1; ++e, buf ^= 1) {
+    const uint32_t entry = as_const(kd.csr_entry)[e];
+    const int kb = (int)(entry & ~kFullBit);
+    const bool full = (entry & kFullBit) != 0;
+    lstore(buf);
+    __syncthreads();
+    if (e + 1 < e1) gload((int)(as_const(kd.csr_entry)[e + 1] & ~kFullBit));
+    if (whi < 0) continue;  // no live row in this wave
+    if (full)
+      block(std::true_type(), Ks[buf], Vs[buf], kb);
+    else
+      block(std::false_type(), Ks[buf], Vs[buf], kb);
+  }
+
+  const float lsum = group4_sum(l_run);
+  if (t < 0) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  bf16* O = (bf16*)a.o + base + (size_t)t * D;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(acc[d] * inv);
+  if (lg == 0)
+    a.lse[(size_t)bh * a.T + t] = lsum > 0.f ? (m_run * sl2 + fast_log2(lsum)) * kLn2 : -INFINITY;
+}
+
 }  // namespace
 
 template <typename TE, int D>
 hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   timing_begin(KID_FWD, stream);
-  hipLaunchKernelGGL((fwd_kernel<TE, D>), dim3(n_items), dim3(kThreads), 0, stream, a);
+  if constexpr (IsBf16<TE>::value)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(n_items), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<TE, D>), dim3(n_items), dim3(kThreads), 0, stream, a);
   const hipError_t err = hipGetLastError();
   timing_end(KID_FWD, stream);
   return err;

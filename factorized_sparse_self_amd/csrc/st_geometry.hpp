@@ -39,6 +39,21 @@ enum KindCode : int {
 
 constexpr int kBlock = 64;  // LUT block size, rows and keys
 
+// Division of a non-negative int by a fixed divisor as multiply-shift
+// (Granlund and Montgomery, 1994): with s = 31 + ceil(log2 d) and
+// m = ceil(2^s / d) (< 2^32), m*d - 2^s < d <= 2^(s-31), so
+// floor(n*m / 2^s) == floor(n / d) for every 0 <= n < 2^31.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t lg = 0;
+  while ((1ull << lg) < d) ++lg;
+  const uint32_t s = 31 + lg;
+  return {(uint32_t)(((1ull << s) + d - 1) / d), s};
+}
+ST_HD int fdiv(int n, FastDiv f) { return (int)(((uint64_t)(uint32_t)n * f.mul) >> f.shift); }
+
 struct Geometry {
   int code;    // KindCode
   int T, l, c;
@@ -46,6 +61,7 @@ struct Geometry {
   int n_keys;  // kernel keys, padding included
   int n_pad;   // K_STRIDE: class length rounded up to kBlock
   int n_cls;   // K_STRIDE: number of residue classes, min(l, T)
+  FastDiv div_l, div_c, div_pad;  // division by l, c (>= 1) and n_pad (>= 1)
 };
 
 ST_HD int imin(int a, int b) { return a < b ? a : b; }
@@ -55,7 +71,7 @@ ST_HD int imax(int a, int b) { return a > b ? a : b; }
 ST_HD int row_position(const Geometry& g, int R) {
   if (R < 0 || R >= g.n_rows) return -1;
   if (g.code == K_STRIDE) {
-    const int r = R / g.n_pad;
+    const int r = fdiv(R, g.div_pad);
     const int m = R - r * g.n_pad;
     const int64_t p = (int64_t)m * g.l + r;
     return p < g.T ? (int)p : -1;
@@ -67,13 +83,13 @@ ST_HD int row_position(const Geometry& g, int R) {
 ST_HD int key_position(const Geometry& g, int K) {
   if (K < 0 || K >= g.n_keys) return -1;
   if (g.code == K_STRIDE) {
-    const int r = K / g.n_pad;
+    const int r = fdiv(K, g.div_pad);
     const int m = K - r * g.n_pad;
     const int64_t p = (int64_t)m * g.l + r;
     return p < g.T ? (int)p : -1;
   }
   if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
-    const int b = K / g.c;
+    const int b = fdiv(K, g.div_c);
     const int o = K - b * g.c;
     const int64_t p = (int64_t)b * g.l + (g.l - g.c) + o;
     return p < g.T ? (int)p : -1;
@@ -81,10 +97,63 @@ ST_HD int key_position(const Geometry& g, int K) {
   return K;
 }
 
+// Position held by row i (0 <= i < kBlock) of 64-block `blk` of the kernel rows
+// (keys == false) or kernel keys (keys == true); -1 for padding.  The branch on
+// the kind is uniform; only the compact summary map divides, by multiply-shift.
+ST_HD int block_position(const Geometry& g, bool keys, int blk, int i) {
+  if (g.code == K_STRIDE) {
+    const int nblk = g.n_pad / kBlock;  // blocks per residue class
+    const int cls = blk / nblk;
+    const int m = (blk - cls * nblk) * kBlock + i;
+    const int p = m * g.l + cls;
+    return (cls < g.n_cls && p < g.T) ? p : -1;
+  }
+  const int R = blk * kBlock + i;
+  if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) {
+    if (R >= g.n_keys) return -1;
+    const int q = fdiv(R, g.div_c);
+    const int p = q * g.l + (g.l - g.c) + (R - q * g.c);
+    return p < g.T ? p : -1;
+  }
+  return R < g.T ? R : -1;
+}
+
+// block_position() split into a part that depends only on the block (uniform)
+// and a part that depends only on the row offset i (per thread, fixed for a
+// kernel's staging rows): position = base + off, valid iff i < limit and
+// position < T.  Available when the map allows it: always for the identity and
+// residue-major maps, and for the compact summary map when c divides kBlock.
+struct RowPart {
+  int off;
+};
+struct BlockPart {
+  int base, limit;
+};
+ST_HD bool split_position_ok(const Geometry& g, bool keys) {
+  return !(keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) || (kBlock % g.c) == 0;
+}
+ST_HD RowPart row_part(const Geometry& g, bool keys, int i) {
+  if (g.code == K_STRIDE) return {i * g.l};
+  if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1))
+    return {(i / g.c) * g.l + (g.l - g.c) + i % g.c};
+  return {i};
+}
+ST_HD BlockPart block_part(const Geometry& g, bool keys, int blk) {
+  if (g.code == K_STRIDE) {
+    const int nblk = g.n_pad / kBlock;
+    const int cls = blk / nblk;
+    const int m0 = (blk - cls * nblk) * kBlock;
+    return {m0 * g.l + cls, cls < g.n_cls ? kBlock : 0};
+  }
+  if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1))
+    return {blk * (kBlock / g.c) * g.l, g.n_keys - blk * kBlock};
+  return {blk * kBlock, kBlock};
+}
+
 // True when position t of this kind is some kernel key (else nobody attends it).
 ST_HD bool position_is_key(const Geometry& g, int t) {
   if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
-    const int b = t / g.l;
+    const int b = fdiv(t, g.div_l);
     const int off = t - b * g.l;
     if (off < g.l - g.c) return false;
     return g.code == K_SUMMARY_R1 || (int64_t)(b + 1) * g.c <= g.n_keys;
@@ -101,19 +170,19 @@ ST_HD void row_interval(const Geometry& g, int R, int t, int& lo, int& hi) {
       hi = t;
       break;
     case K_STRIDE:
-      lo = (R / g.n_pad) * g.n_pad;
+      lo = fdiv(R, g.div_pad) * g.n_pad;
       hi = R;
       break;
     case K_BLOCK:
-      lo = (t / g.l) * g.l;
+      lo = fdiv(t, g.div_l) * g.l;
       hi = t;
       break;
     case K_SUMMARY:
       lo = 0;
-      hi = g.c * (t / g.l) - 1;
+      hi = g.c * fdiv(t, g.div_l) - 1;
       break;
     case K_SUMMARY_R1: {
-      const int b = t / g.l;
+      const int b = fdiv(t, g.div_l);
       const int off = t - b * g.l;
       lo = 0;
       hi = g.c * b + imax(0, off - (g.l - g.c) + 1) - 1;

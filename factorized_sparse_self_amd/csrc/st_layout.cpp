@@ -52,6 +52,9 @@ bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g) {
   } else if (g->code == K_SUMMARY_R1) {
     g->n_keys = nb * c;
   }
+  g->div_l = make_fastdiv((uint32_t)l);
+  g->div_c = make_fastdiv(c > 0 ? (uint32_t)c : 1u);
+  g->div_pad = make_fastdiv(g->n_pad > 0 ? (uint32_t)g->n_pad : 1u);
   return true;
 }
 
