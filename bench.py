@@ -78,10 +78,17 @@ def accounting(w):
         pairs_total += w.B * pairs
         # forward: read q (active rows), k and v (attended keys); write out and lse (every row)
         by["fwd"] += w.B * (rows * row + 2 * keys * row + w.T * (row + 4))
-        # preprocess: read out and dout, write Delta; zero dk and dv where no query attends
-        by["bwd_pre"] += w.B * (w.T * (2 * row + 4) + 2 * (w.T - keys) * row)
+        # Delta and the zero fill: read out and dout, write Delta; zero dk and dv where no
+        # query attends (a kernel of its own for fp32; folded into dq for bf16, whose dq
+        # then reads out instead of Delta)
+        pre = w.T * (2 * row + 4) + 2 * (w.T - keys) * row
         # dq: read q, dout, lse, Delta (active rows), k and v (keys); write dq (every row)
-        by["bwd_dq"] += w.B * (rows * (2 * row + 8) + 2 * keys * row + w.T * row)
+        dq = rows * (2 * row + 8) + 2 * keys * row + w.T * row
+        if w.dtype == "bf16":
+            by["bwd_dq"] += w.B * (dq + w.T * (row + 4) + 2 * (w.T - keys) * row)
+        else:
+            by["bwd_pre"] += w.B * pre
+            by["bwd_dq"] += w.B * dq
         # dk/dv: read q, dout, lse, Delta (active rows), k and v (keys); write dk and dv (keys)
         by["bwd_dkdv"] += w.B * (rows * (2 * row + 8) + 4 * keys * row)
     fl = {"fwd": 4 * w.D * pairs_total, "bwd_pre": 0, "bwd_dq": 6 * w.D * pairs_total,

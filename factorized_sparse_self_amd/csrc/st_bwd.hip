@@ -11,6 +11,7 @@
 // significant bits), so those sums are not limited by bf16's 8-bit rounding.
 // Kernels (one stream, in order):
 //   pre   Delta for every row; zero dk / dv at positions no query attends
+//         (fp32 only: the bf16 dq kernel does both for its own rows)
 //   dq    per row block over the CSR (no cross-item reduction)
 //   dkdv  per key block over the CSC; key blocks with many row blocks are
 //         split, each split writing fp32 partials
@@ -517,17 +518,39 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   const int whi = uniform(wave_max(row_live ? hi : -1));
   const int mlo = row_live ? lo : -(1 << 30);
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
-  float lse2 = 0.f, delta = 0.f;
-  if (row_live) {
-    lse2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
-    delta = a.delta[(size_t)bh * a.T + t];
-  }
+  // Delta_t = dO_t . O_t: each of the row's four lanes holds a quarter of the
+  // row of dO (the MFMA operand) and loads the same quarter of O
+  const Rsrc ro = make_rsrc((const bf16*)a.o + base, head_bytes);
   bf16x8 qop[NQ], gop[NQ];
+  float dpart = 0.f;
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
     const uint32_t off = t >= 0 ? (uint32_t)(t * D + 32 * s + 8 * lg) * 2 : kOutOfRange;
     qop[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
     gop[s] = __builtin_bit_cast(bf16x8, buf_load16(rg, off));
+    const bf16x8 o8 = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dpart = fmaf((float)gop[s][i], (float)o8[i], dpart);
+  }
+  const float delta_row = group4_sum(dpart);
+  if (t >= 0 && lg == 0) a.delta[(size_t)bh * a.T + t] = delta_row;
+  float lse2 = 0.f, delta = 0.f;
+  if (row_live) {
+    lse2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
+    delta = delta_row;
+  }
+  // keys nobody attends (positions outside a summary head's key map) get
+  // dk = dv = 0; the row positions of this block cover every such position
+  if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
+    for (int u = tid; u < kBlock * CH; u += kThreads) {
+      const int r = u / CH, ch = u % CH;
+      const int tp = block_position(g, false, qb, r);
+      if (tp >= 0 && !position_is_key(g, tp)) {
+        const uint4 z = {0, 0, 0, 0};
+        *(uint4*)((bf16*)a.dk + base + (size_t)tp * D + ch * 8) = z;
+        *(uint4*)((bf16*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+      }
+    }
   }
   f32x4 acc[ND];
 #pragma unroll
@@ -809,31 +832,32 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <typename TE, int D>
 __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
-  const ReduceItem item = load_uniform(&a.red_items[blockIdx.x]);
+  // kParts workgroups per split key block, one float4 of dk or dv per thread
+  constexpr int CH = D / 4;
+  constexpr int kParts = 2 * kBlock * CH / kThreads;
+  const ReduceItem item = load_uniform(&a.red_items[blockIdx.x / kParts]);
   if (item.kb < 0) return;  // schedule padding
   const KindDev kd = load_uniform(&a.kinds[(item.bh % a.H) & 1]);
   const size_t base = (size_t)item.bh * a.T * D;
-  constexpr int CH = D / 4;
-  for (int u = threadIdx.x; u < 2 * kBlock * CH; u += kThreads) {
-    const int which = u / (kBlock * CH);  // 0 = dk, 1 = dv
-    const int r = (u / CH) % kBlock, ch = u % CH;
-    const int kp = key_position(kd.geo, item.kb * kBlock + r);
-    if (kp < 0) continue;
-    float4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < item.nsplit; ++j) {
-      const float4 x = *(const float4*)(a.partial + ((size_t)(item.slot0 + j) * 2 + which) * kBlock * D +
-                                        r * D + ch * 4);
-      s.x += x.x;
-      s.y += x.y;
-      s.z += x.z;
-      s.w += x.w;
-    }
-    TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
-    if constexpr (IsBf16<TE>::value) {
-      *(bf16x4*)dst = to_bf16x4((f32x4){s.x, s.y, s.z, s.w});
-    } else {
-      *(float4*)dst = s;
-    }
+  const int u = (blockIdx.x % kParts) * kThreads + threadIdx.x;
+  const int which = u / (kBlock * CH);  // 0 = dk, 1 = dv
+  const int r = (u / CH) % kBlock, ch = u % CH;
+  const int kp = block_position(kd.geo, true, item.kb, r);
+  if (kp < 0) return;
+  float4 s = {0.f, 0.f, 0.f, 0.f};
+  const float* src = a.partial + ((size_t)item.slot0 * 2 + which) * kBlock * D + r * D + ch * 4;
+  for (int j = 0; j < item.nsplit; ++j) {
+    const float4 x = *(const float4*)(src + (size_t)j * 2 * kBlock * D);
+    s.x += x.x;
+    s.y += x.y;
+    s.z += x.z;
+    s.w += x.w;
+  }
+  TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
+  if constexpr (IsBf16<TE>::value) {
+    *(bf16x4*)dst = to_bf16x4((f32x4){s.x, s.y, s.z, s.w});
+  } else {
+    *(float4*)dst = s;
   }
 }
 
@@ -844,11 +868,16 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   constexpr int TPR = D / (16 / sizeof(TE));
   const int64_t rows = (int64_t)a.BH * a.T;
   const int64_t pre_blocks = (rows * TPR + kThreads - 1) / kThreads;
-  timing_begin(KID_PRE, stream);
-  hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  timing_end(KID_PRE, stream);
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  // bf16: the dq kernel computes Delta and the zero fill itself; it runs
+  // before dk/dv, which reads Delta
+  if constexpr (!IsBf16<TE>::value) {
+    timing_begin(KID_PRE, stream);
+    hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
+    err = hipGetLastError();
+    timing_end(KID_PRE, stream);
+    if (err != hipSuccess) return err;
+  }
   if (n_dq > 0) {
     timing_begin(KID_DQ, stream);
     if constexpr (IsBf16<TE>::value)
@@ -871,7 +900,8 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   }
   if (n_red > 0) {
     timing_begin(KID_RED, stream);
-    hipLaunchKernelGGL((bwd_reduce_kernel<TE, D>), dim3(n_red), dim3(kThreads), 0, stream, a);
+    constexpr int kParts = 2 * kBlock * (D / 4) / kThreads;
+    hipLaunchKernelGGL((bwd_reduce_kernel<TE, D>), dim3(n_red * kParts), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
     timing_end(KID_RED, stream);
     if (err != hipSuccess) return err;
