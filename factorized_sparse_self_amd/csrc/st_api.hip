@@ -347,7 +347,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   const size_t delta_bytes = align_up((size_t)B * H * T * sizeof(float), 256);
   const size_t partial_bytes = (size_t)plan->n_slots * 2 * kBlock * D * sizeof(float);
   void* ws = nullptr;
-  rc = get_workspace(device, delta_bytes + partial_bytes, &ws);
+  rc = get_workspace(device, 2 * delta_bytes + partial_bytes, &ws);
   if (rc != ST_OK) return rc;
   BwdArgs a;
   a.q = q;
@@ -360,7 +360,8 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.dk = dk;
   a.dv = dv;
   a.delta = (float*)ws;
-  a.partial = (float*)((unsigned char*)ws + delta_bytes);
+  a.lse2 = (float*)((unsigned char*)ws + delta_bytes);
+  a.partial = (float*)((unsigned char*)ws + 2 * delta_bytes);
   a.BH = B * H;
   a.H = H;
   a.T = T;

@@ -20,10 +20,22 @@
 
 #include "st_device.hpp"
 #include "st_kernels.hpp"
+#include "st_stage.hpp"
 
 namespace st {
 
 namespace {
+
+// LDS ring stages of the bf16 dk/dv pass (row blocks in flight = stages - 1)
+#ifndef ST_DKDV_STAGES
+#define ST_DKDV_STAGES 2
+#endif
+constexpr int kDkdvStages = ST_DKDV_STAGES;
+// LDS ring stages of the bf16 dq pass
+#ifndef ST_DQ_STAGES
+#define ST_DQ_STAGES 2
+#endif
+constexpr int kDqStages = ST_DQ_STAGES;
 
 template <typename TE, int D>
 struct BwdLds {
@@ -482,19 +494,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 dq and dk/dv.  As in the forward: the streamed blocks (K and V for dq;
-// Q and dO with their lse, Delta and key runs for dk/dv) are staged row-major
-// in double-buffered LDS with the next block's buffer loads in flight (padding
-// rows read as zeros); FULL blocks run without masks; every transposed MFMA
-// operand (K^T, Q^T, dO^T) comes from LDS transpose reads.
+// Q and dO with their lse, Delta and key runs for dk/dv) go straight from
+// global memory into a ring of swizzled LDS stages (st_stage.hpp) with the
+// next blocks' loads in flight (padding rows read as zeros); FULL blocks run
+// without masks; every transposed MFMA operand (K^T, Q^T, dO^T) comes from
+// LDS transpose reads.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
-  constexpr int P = D + 16, NQ = D / 32, ND = D / 16, CH = D / 8;  // pitch as in the forward
-  constexpr int NLD = kBlock * CH / kThreads;
-  constexpr int RSTEP = kThreads / CH;
-  static_assert(NLD >= 1 && kBlock * CH % kThreads == 0, "staging layout");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * P];
+  using S = TileShape<D>;
+  constexpr int NQ = D / 32, ND = D / 16, CH = D / 8;
+  constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][S::BYTES];
 
   const int2 item = load_uniform(&a.dq_items[blockIdx.x]);
   if (item.x < 0) return;  // schedule padding
@@ -510,6 +521,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
+  const StageRows<S::NI, S::RPI> stage(g, true, 16 * wave + lane / S::CH);
+  const cptr<uint32_t> entries = as_const(kd.csr_entry);
+  auto issue = [&](int e, int stg) {
+    int p[S::NI];
+    stage.positions(g, true, (int)(entries[e] & ~kFullBit), p);
+    stage_rows<D>(rk, ring[stg][0], wave, lane, p);
+    stage_rows<D>(rv, ring[stg][1], wave, lane, p);
+  };
+  // The first NS-1 key blocks are in flight while the row's own operands load
+  // (those loads are younger, so the compiler's waits for them cover the ring's
+  // first blocks too, and no compiler wait lands inside the loop).
+  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (e0 + j < e1) issue(e0 + j, j);
+
   const int t = block_position(g, false, qb, wave * 16 + li);
   int lo = 1, hi = 0;
   if (t >= 0) row_interval(g, qb * kBlock + wave * 16 + li, t, lo, hi);
@@ -533,11 +560,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
     for (int i = 0; i < 8; ++i) dpart = fmaf((float)gop[s][i], (float)o8[i], dpart);
   }
   const float delta_row = group4_sum(dpart);
-  if (t >= 0 && lg == 0) a.delta[(size_t)bh * a.T + t] = delta_row;
   float lse2 = 0.f, delta = 0.f;
   if (row_live) {
-    lse2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
+    lse2 = buf_load_f32(make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4), (uint32_t)t * 4) * kLog2e;
     delta = delta_row;
+  }
+  // Delta and lse*log2(e) of every row, for the dk/dv pass that follows
+  if (t >= 0 && lg == 0) {
+    a.delta[(size_t)bh * a.T + t] = delta_row;
+    a.lse2[(size_t)bh * a.T + t] = lse2;
   }
   // keys nobody attends (positions outside a summary head's key map) get
   // dk = dv = 0; the row positions of this block cover every such position
@@ -552,34 +583,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
       }
     }
   }
+  // per-lane byte offsets of the MFMA operand reads inside a staged block
+  int a_off[NQ], t_off[ND];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) a_off[k] = S::phys(li, 4 * k + lg);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
   f32x4 acc[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
 
-  uint4 kr[NLD], vr[NLD];
-  const int srow = tid / CH, sch = tid % CH;
-  const StageRows<NLD, RSTEP> stage(g, true, srow);
-  auto gload = [&](int kb) {
-    int p[NLD];
-    stage.positions(g, true, kb, p);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const uint32_t off = p[i] >= 0 ? (uint32_t)(p[i] * D + sch * 8) * 2 : kOutOfRange;
-      kr[i] = buf_load16(rk, off);
-      vr[i] = buf_load16(rv, off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int off = (srow + i * RSTEP) * P + sch * 8;
-      *(uint4*)(&Ks[buf][off]) = kr[i];
-      *(uint4*)(&Vs[buf][off]) = vr[i];
-    }
-  };
-
-  auto block = [&](auto full_c, const bf16* Kb, const bf16* Vb, int kb) {
+  auto block = [&](auto full_c, const unsigned char* Kt, const unsigned char* Vt, int kb) {
     constexpr bool FULL = decltype(full_c)::value;
     const int k0 = kb * kBlock;
     bool need[4];
@@ -592,8 +607,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
       if (!need[b]) continue;
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        s[b] = mfma_bf16(*(const bf16x8*)(Kb + (16 * b + li) * P + 32 * k + 8 * lg), qop[k], s[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(Vb + (16 * b + li) * P + 32 * k + 8 * lg), gop[k], dp[b]);
+        s[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]), qop[k], s[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(Vt + 16 * b * S::RB + a_off[k]), gop[k], dp[b]);
       }
     }
     const int m0 = k0 + 4 * lg - mlo;
@@ -612,27 +627,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
       split_b_operand(s[2 * kk], s[2 * kk + 1], hi8, lo8);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const bf16x8 ak = tr_a_operand(Kb, P, 32 * kk, 16 * d, li, lg);
+        const unsigned char* r0 = Kt + 32 * kk * S::RB + t_off[d];
+        const bf16x8 ak = concat(lds_read_tr((const bf16*)r0), lds_read_tr((const bf16*)(r0 + 16 * S::RB)));
         acc[d] = mfma_bf16(ak, hi8, acc[d]);
         acc[d] = mfma_bf16(ak, lo8, acc[d]);
       }
     }
   };
 
-  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
-  if (e0 < e1) gload((int)(as_const(kd.csr_entry)[e0] & ~kFullBit));
-  for (int e = e0, buf = 0; e < e1; ++e, buf ^= 1) {
-    const uint32_t entry = as_const(kd.csr_entry)[e];
+  for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
+    const uint32_t entry = entries[e];
     const int kb = (int)(entry & ~kFullBit);
     const bool full = (entry & kFullBit) != 0;
-    lstore(buf);
+    wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
     __syncthreads();
-    if (e + 1 < e1) gload((int)(as_const(kd.csr_entry)[e + 1] & ~kFullBit));
+    if (e + NS - 1 < e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
     if (whi < 0) continue;
     if (full)
-      block(std::true_type(), Ks[buf], Vs[buf], kb);
+      block(std::true_type(), ring[stg][0], ring[stg][1], kb);
     else
-      block(std::false_type(), Ks[buf], Vs[buf], kb);
+      block(std::false_type(), ring[stg][0], ring[stg][1], kb);
   }
   if (t < 0) return;
   bf16* dq = (bf16*)a.dq + base + (size_t)t * D;
@@ -640,18 +654,27 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   for (int d = 0; d < ND; ++d) *(bf16x4*)(dq + 16 * d + 4 * lg) = to_bf16x4(acc[d] * a.scale);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int P = D + 16, NQ = D / 32, ND = D / 16, CH = D / 8;  // pitch as in the forward
-  constexpr int NLD = kBlock * CH / kThreads;
-  constexpr int RSTEP = kThreads / CH;
-  static_assert(NLD >= 1 && kBlock * CH % kThreads == 0, "staging layout");
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][kBlock * P];
-  __shared__ __attribute__((aligned(16))) bf16 Gs[2][kBlock * P];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][kBlock];
-  __shared__ __attribute__((aligned(16))) float dels[2][kBlock];
-  __shared__ __attribute__((aligned(16))) int los[2][kBlock];     // masking base of each row
-  __shared__ __attribute__((aligned(16))) int spans[2][kBlock];   // masking span (unsigned)
+// dk/dv: Q and dO blocks with their lse*log2(e) and Delta are staged by
+// direct global->LDS loads into a ring of NS stages (st_stage.hpp), so the
+// loads of NS-1 row blocks are in flight while one is computed; each row's
+// key run (for masks) is computed and stored next to them.
+// At most 168 VGPRs: three waves per SIMD (three workgroups per CU with the
+// two-stage ring) beat two waves with deeper prefetch; four waves would spill.
+template <int D, int NS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_bf16_kernel(
+    BwdArgs a) {
+  using S = TileShape<D>;
+  constexpr int NQ = D / 32, ND = D / 16;
+  constexpr int PER_TILE = 2 * S::NI + 2;  // loads per wave per row block: Q, dO, lse2, Delta
+  struct Stage {
+    unsigned char q[S::BYTES];
+    unsigned char g[S::BYTES];
+    float lse2[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 16)
+    float delta[4 * 64];
+    int lo[kBlock];       // masking base of each row
+    int span[kBlock];     // masking span (unsigned)
+  };
+  __shared__ __attribute__((aligned(16))) Stage ring[NS];
 
   const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
   if (item.kb < 0) return;  // schedule padding
@@ -664,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
   const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
   const Rsrc rg = make_rsrc((const bf16*)a.dout + base, head_bytes);
-  const Rsrc rl = make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4);
+  const Rsrc rl = make_rsrc(a.lse2 + (size_t)bh * a.T, (uint32_t)a.T * 4);
   const Rsrc rd = make_rsrc(a.delta + (size_t)bh * a.T, (uint32_t)a.T * 4);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -672,72 +695,47 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int Kw0 = kb * kBlock + wave * 16;
   const int Kl = Kw0 + li;
   const int kp = block_position(g, true, kb, wave * 16 + li);
-  bf16x8 kop[NQ], vop[NQ];
+  bf16x8 kop[NQ], vop[NQ];  // this wave's 16 keys as MFMA B operands (from LDS, first block)
+  int a_off[NQ], t_off[ND];
 #pragma unroll
-  for (int s = 0; s < NQ; ++s) {
-    const uint32_t off = kp >= 0 ? (uint32_t)(kp * D + 32 * s + 8 * lg) * 2 : kOutOfRange;
-    kop[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-    vop[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
-  }
+  for (int k = 0; k < NQ; ++k) a_off[k] = S::phys(li, 4 * k + lg);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
   f32x4 dk[ND], dv[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) dk[d] = dv[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
 
-  uint4 qr[NLD], gr[NLD];
-  float sc_l2 = 0.f, sc_de = 0.f;
-  int sc_lo = 0, sc_span = 0;
-  const int srow = tid / CH, sch = tid % CH;
-  const StageRows<NLD, RSTEP> stage(g, false, srow);
-  const StageRows<1, kBlock> stage_row(g, false, tid & (kBlock - 1));
-  auto gload = [&](int qb) {
-    int p[NLD];
+  const StageRows<S::NI, S::RPI> stage(g, false, 16 * wave + lane / S::CH);
+  const StageRows<1, kBlock> stage_own(g, false, 16 * wave + li);  // this lane's row, lanes 0..15
+  const cptr<uint32_t> entries = as_const(kd.csc_entry);
+  auto issue = [&](int e, int stg) {
+    const int qb = (int)(entries[e] & ~kFullBit);
+    int p[S::NI];
     stage.positions(g, false, qb, p);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const uint32_t off = p[i] >= 0 ? (uint32_t)(p[i] * D + sch * 8) * 2 : kOutOfRange;
-      qr[i] = buf_load16(rq, off);
-      gr[i] = buf_load16(rg, off);
-    }
-    if (tid < kBlock) {
-      int tp[1];
-      stage_row.positions(g, false, qb, tp);
-      const int t = tp[0];
-      int lo = 1, hi = 0;
-      if (t >= 0) row_interval(g, qb * kBlock + tid, t, lo, hi);
-      const bool live = lo <= hi;
-      sc_lo = live ? lo : -(1 << 30);
-      sc_span = live ? hi - lo : 0;
-      const uint32_t off = live ? (uint32_t)t * 4 : kOutOfRange;
-      sc_l2 = buf_load_f32(rl, off);
-      sc_de = buf_load_f32(rd, off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int off = (srow + i * RSTEP) * P + sch * 8;
-      *(uint4*)(&Qs[buf][off]) = qr[i];
-      *(uint4*)(&Gs[buf][off]) = gr[i];
-    }
-    if (tid < kBlock) {
-      lse2s[buf][tid] = sc_l2 * kLog2e;
-      dels[buf][tid] = sc_de;
-      los[buf][tid] = sc_lo;
-      spans[buf][tid] = sc_span;
+    stage_rows<D>(rq, ring[stg].q, wave, lane, p);
+    stage_rows<D>(rg, ring[stg].g, wave, lane, p);
+    int tp[1];
+    stage_own.positions(g, false, qb, tp);
+    int lo = 1, hi = 0;
+    if (tp[0] >= 0) row_interval(g, qb * kBlock + 16 * wave + li, tp[0], lo, hi);
+    const bool live = lo <= hi;
+    stage_row_values(rl, ring[stg].lse2, wave, lane, live ? tp[0] : -1);
+    stage_row_values(rd, ring[stg].delta, wave, lane, live ? tp[0] : -1);
+    if (lane < 16) {
+      ring[stg].lo[16 * wave + lane] = live ? lo : -(1 << 30);
+      ring[stg].span[16 * wave + lane] = live ? hi - lo : 0;
     }
   };
 
-  auto block = [&](auto full_c, int buf) {
+  auto block = [&](auto full_c, const Stage& st) {
     constexpr bool FULL = decltype(full_c)::value;
-    const bf16* Qb = Qs[buf];
-    const bf16* Gb = Gs[buf];
     bool need[4] = {true, true, true, true};
     if (!FULL) {
       // which 16-row blocks hold a row whose key run meets this wave's 16 keys
-      const int rlo = los[buf][lane];
-      const uint32_t rspan = (uint32_t)spans[buf][lane];
-      const bool meets = rlo <= Kw0 + 15 && (int64_t)rlo + rspan >= Kw0 && rlo > -(1 << 30);
+      const int rlo = st.lo[lane];
+      const uint32_t rspan = (uint32_t)st.span[lane];
+      const bool meets = rlo > -(1 << 30) && rlo <= Kw0 + 15 && (int64_t)rlo + rspan >= Kw0;
       const uint64_t hit = __ballot(meets);
       if (hit == 0) return;
 #pragma unroll
@@ -750,21 +748,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       if (!need[b]) continue;
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        s[b] = mfma_bf16(*(const bf16x8*)(Qb + (16 * b + li) * P + 32 * k + 8 * lg), kop[k], s[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(Gb + (16 * b + li) * P + 32 * k + 8 * lg), vop[k], dp[b]);
+        s[b] = mfma_bf16(*(const bf16x8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], s[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[b]);
       }
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int r0 = 16 * b + 4 * lg;
-      const float4 l2 = *(const float4*)(&lse2s[buf][r0]);
-      const float4 de = *(const float4*)(&dels[buf][r0]);
+      const int r0 = 16 * b + 4 * lg;  // rows r0 .. r0+3 of this lane's values
+      const float4 l2 = *(const float4*)(&st.lse2[64 * b + 4 * lg]);
+      const float4 de = *(const float4*)(&st.delta[64 * b + 4 * lg]);
       const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
       const float dea[4] = {de.x, de.y, de.z, de.w};
       int loa[4] = {0, 0, 0, 0}, spa[4] = {0, 0, 0, 0};
       if (!FULL) {
-        const int4 lo4 = *(const int4*)(&los[buf][r0]);
-        const int4 sp4 = *(const int4*)(&spans[buf][r0]);
+        const int4 lo4 = *(const int4*)(&st.lo[r0]);
+        const int4 sp4 = *(const int4*)(&st.span[r0]);
         loa[0] = lo4.x; loa[1] = lo4.y; loa[2] = lo4.z; loa[3] = lo4.w;
         spa[0] = sp4.x; spa[1] = sp4.y; spa[2] = sp4.z; spa[3] = sp4.w;
       }
@@ -784,8 +782,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       split_b_operand(dp[2 * kk], dp[2 * kk + 1], d_hi, d_lo);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const bf16x8 ag = tr_a_operand(Gb, P, 32 * kk, 16 * d, li, lg);
-        const bf16x8 aq = tr_a_operand(Qb, P, 32 * kk, 16 * d, li, lg);
+        const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
+        const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
+        const bf16x8 ag = concat(lds_read_tr((const bf16*)rg0), lds_read_tr((const bf16*)(rg0 + 16 * S::RB)));
+        const bf16x8 aq = concat(lds_read_tr((const bf16*)rq0), lds_read_tr((const bf16*)(rq0 + 16 * S::RB)));
         dv[d] = mfma_bf16(ag, p_hi, dv[d]);
         dv[d] = mfma_bf16(ag, p_lo, dv[d]);
         dk[d] = mfma_bf16(aq, d_hi, dk[d]);
@@ -794,16 +794,38 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
-  if (item.e0 < item.e1) gload((int)(as_const(kd.csc_entry)[item.e0] & ~kFullBit));
-  for (int e = item.e0, buf = 0; e < item.e1; ++e, buf ^= 1) {
-    const bool full = (as_const(kd.csc_entry)[e] & kFullBit) != 0;
-    lstore(buf);
+  // The key block's K and V rows go through the last ring stage (free until
+  // the first iteration refills it), ahead of the first NS-1 row blocks, so
+  // every global load of the kernel is a ring DMA.
+  if (item.e0 < item.e1) {
+    const StageRows<S::NI, S::RPI> kstage(g, true, 16 * wave + lane / S::CH);
+    int p[S::NI];
+    kstage.positions(g, true, kb, p);
+    stage_rows<D>(rk, ring[NS - 1].q, wave, lane, p);
+    stage_rows<D>(rv, ring[NS - 1].g, wave, lane, p);
+  }
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (item.e0 + j < item.e1) issue(item.e0 + j, j);
+  for (int e = item.e0, stg = 0; e < item.e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
+    const bool full = (entries[e] & kFullBit) != 0;
+    wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, item.e1 - 1 - e));
     __syncthreads();
-    if (e + 1 < item.e1) gload((int)(as_const(kd.csc_entry)[e + 1] & ~kFullBit));
+    if (e == item.e0) {
+      // this wave's 16 K/V rows (its own DMA, complete with the first block)
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        kop[k] = *(const bf16x8*)(ring[NS - 1].q + 16 * wave * S::RB + a_off[k]);
+        vop[k] = *(const bf16x8*)(ring[NS - 1].g + 16 * wave * S::RB + a_off[k]);
+      }
+      // the reads must land before the DMA below refills that stage
+      wait_lgkmcnt0();
+    }
+    if (e + NS - 1 < item.e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
     if (full)
-      block(std::true_type(), buf);
+      block(std::true_type(), ring[stg]);
     else
-      block(std::false_type(), buf);
+      block(std::false_type(), ring[stg]);
   }
 
   if (item.slot < 0) {
@@ -881,7 +903,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   if (n_dq > 0) {
     timing_begin(KID_DQ, stream);
     if constexpr (IsBf16<TE>::value)
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kDqStages>), dim3(n_dq), dim3(kThreads), 0, stream, a);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
@@ -891,7 +913,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
     if constexpr (IsBf16<TE>::value)
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kDkdvStages>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();

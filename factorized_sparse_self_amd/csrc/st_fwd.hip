@@ -18,10 +18,17 @@
 
 #include "st_device.hpp"
 #include "st_kernels.hpp"
+#include "st_stage.hpp"
 
 namespace st {
 
 namespace {
+
+// LDS ring stages of the bf16 forward (blocks in flight = stages - 1)
+#ifndef ST_FWD_STAGES
+#define ST_FWD_STAGES 2
+#endif
+constexpr int kFwdStages = ST_FWD_STAGES;
 
 template <typename TE, int D>
 struct FwdLds {
@@ -253,11 +260,10 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 forward.
-//  * K and V blocks are staged row-major in double-buffered LDS; the next
-//    block's global loads are issued before the current block is computed, so
-//    one barrier per block separates staging from use.  Loads go through
-//    buffer descriptors: padding rows get an out-of-range offset and read as
-//    zeros, with no branch.
+//  * K and V blocks are staged by direct global->LDS loads into a ring of NS
+//    LDS stages (st_stage.hpp): the loads of the next NS-1 blocks are in
+//    flight while a block is computed, and no registers hold them.  Padding
+//    rows read as zeros.  One barrier per block.
 //  * FULL blocks take a straight path (no masks, no sub-block tests); PARTIAL
 //    blocks skip 16-key sub-blocks the wave does not need and mask the rest
 //    with one unsigned compare per logit.
@@ -267,20 +273,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 //    when a logit exceeds it by more than 2^8 in exp2 units; blocks where no
 //    lane of the wave needs that skip the cross-lane max and the rescale.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
-  // LDS row pitch (elements): rows stay 16-byte aligned (a misaligned 128-bit
-  // LDS access is split by the hardware); a 32-byte pad keeps the transpose
-  // reads of four consecutive rows on disjoint banks
-  constexpr int P = D + 16;
-  constexpr int NQ = D / 32;                   // MFMA k-steps over D
-  constexpr int ND = D / 16;                   // 16-wide output column blocks
-  constexpr int CH = D / 8;                    // 16-byte chunks per row
-  constexpr int NLD = kBlock * CH / kThreads;  // chunks per thread per tensor
-  constexpr int RSTEP = kThreads / CH;         // rows between a thread's chunks
-  static_assert(NLD >= 1 && kBlock * CH % kThreads == 0, "staging layout");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * P];
+  using S = TileShape<D>;
+  constexpr int NQ = D / 32;                 // MFMA k-steps over D
+  constexpr int ND = D / 16;                 // 16-wide output column blocks
+  constexpr int PER_TILE = 2 * S::NI;        // loads per wave per block (K and V)
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][S::BYTES];
 
   const int2 item = load_uniform(&a.items[blockIdx.x]);
   if (item.x < 0) return;  // schedule padding
@@ -305,10 +304,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
   const int mlo = row_live ? lo : -(1 << 30);
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
 
-  bf16x8 qop[NQ];
+  bf16x8 qop[NQ];  // this wave's 16 query rows as MFMA B operands (from LDS, first block)
+
+  // per-lane byte offsets of the MFMA operand reads inside a staged block
+  int a_off[NQ], t_off[ND];
 #pragma unroll
-  for (int s = 0; s < NQ; ++s)
-    qop[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, t >= 0 ? (uint32_t)(t * D + 32 * s + 8 * lg) * 2 : kOutOfRange));
+  for (int k = 0; k < NQ; ++k) a_off[k] = S::phys(li, 4 * k + lg);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
 
   f32x4 acc[ND];
 #pragma unroll
@@ -317,29 +320,16 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
   const float headroom = 8.0f / sl2;  // raw-logit growth allowed before a rescale
   float m_run = -INFINITY, l_run = 0.f;
 
-  uint4 kr[NLD], vr[NLD];
-  const int srow = tid / CH, sch = tid % CH;
-  const StageRows<NLD, RSTEP> stage(g, true, srow);
-  auto gload = [&](int kb) {
-    int p[NLD];
-    stage.positions(g, true, kb, p);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const uint32_t off = p[i] >= 0 ? (uint32_t)(p[i] * D + sch * 8) * 2 : kOutOfRange;
-      kr[i] = buf_load16(rk, off);
-      vr[i] = buf_load16(rv, off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int off = (srow + i * RSTEP) * P + sch * 8;
-      *(uint4*)(&Ks[buf][off]) = kr[i];
-      *(uint4*)(&Vs[buf][off]) = vr[i];
-    }
+  const StageRows<S::NI, S::RPI> stage(g, true, 16 * wave + lane / S::CH);
+  const cptr<uint32_t> entries = as_const(kd.csr_entry);
+  auto issue = [&](int e, int stg) {
+    int p[S::NI];
+    stage.positions(g, true, (int)(entries[e] & ~kFullBit), p);
+    stage_rows<D>(rk, ring[stg][0], wave, lane, p);
+    stage_rows<D>(rv, ring[stg][1], wave, lane, p);
   };
 
-  auto block = [&](auto full_c, const bf16* Kb, const bf16* Vb, int kb) {
+  auto block = [&](auto full_c, const unsigned char* Kt, const unsigned char* Vt, int kb) {
     constexpr bool FULL = decltype(full_c)::value;
     const int k0 = kb * kBlock;
     bool need[4];
@@ -352,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
       if (!need[b]) continue;
 #pragma unroll
       for (int k = 0; k < NQ; ++k)
-        s[b] = mfma_bf16(*(const bf16x8*)(Kb + (16 * b + li) * P + 32 * k + 8 * lg), qop[k], s[b]);
+        s[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]), qop[k], s[b]);
     }
     if (!FULL) {
       const int m0 = k0 + 4 * lg - mlo;
@@ -389,24 +379,47 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
       if (!need[2 * kk] && !need[2 * kk + 1]) continue;
       const bf16x8 pb = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
 #pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] = mfma_bf16(tr_a_operand(Vb, P, 32 * kk, 16 * d, li, lg), pb, acc[d]);
+      for (int d = 0; d < ND; ++d) {
+        const unsigned char* r0 = Vt + 32 * kk * S::RB + t_off[d];
+        const bf16x8 av = concat(lds_read_tr((const bf16*)r0), lds_read_tr((const bf16*)(r0 + 16 * S::RB)));
+        acc[d] = mfma_bf16(av, pb, acc[d]);
+      }
     }
   };
 
-  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
-  if (e0 < e1) gload((int)(as_const(kd.csr_entry)[e0] & ~kFullBit));
-  for (int e = e0, buf = 0; e < e1; ++e, buf ^= 1) {
-    const uint32_t entry = as_const(kd.csr_entry)[e];
+  const cptr<int32_t> row_ptr = as_const(kd.row_ptr);
+  const int e0 = row_ptr[qb], e1 = row_ptr[qb + 1];
+  // The row block's Q rows go through the last ring stage (free until the
+  // first iteration refills it), ahead of the first NS-1 key blocks, so every
+  // global load of the loop is a ring DMA.
+  if (e0 < e1) {
+    const StageRows<S::NI, S::RPI> qstage(g, false, 16 * wave + lane / S::CH);
+    int p[S::NI];
+    qstage.positions(g, false, qb, p);
+    stage_rows<D>(rq, ring[NS - 1][0], wave, lane, p);
+  }
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (e0 + j < e1) issue(e0 + j, j);
+  for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
+    const uint32_t entry = entries[e];
     const int kb = (int)(entry & ~kFullBit);
     const bool full = (entry & kFullBit) != 0;
-    lstore(buf);
+    wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
     __syncthreads();
-    if (e + 1 < e1) gload((int)(as_const(kd.csr_entry)[e + 1] & ~kFullBit));
+    if (e == e0) {
+      // this wave's own DMA, complete with the first block
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) qop[k] = *(const bf16x8*)(ring[NS - 1][0] + 16 * wave * S::RB + a_off[k]);
+      // the reads must land before the DMA below refills that stage
+      wait_lgkmcnt0();
+    }
+    if (e + NS - 1 < e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
     if (whi < 0) continue;  // no live row in this wave
     if (full)
-      block(std::true_type(), Ks[buf], Vs[buf], kb);
+      block(std::true_type(), ring[stg][0], ring[stg][1], kb);
     else
-      block(std::false_type(), Ks[buf], Vs[buf], kb);
+      block(std::false_type(), ring[stg][0], ring[stg][1], kb);
   }
 
   const float lsum = group4_sum(l_run);
@@ -426,7 +439,7 @@ hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   timing_begin(KID_FWD, stream);
   if constexpr (IsBf16<TE>::value)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(n_items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdStages>), dim3(n_items), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((fwd_kernel<TE, D>), dim3(n_items), dim3(kThreads), 0, stream, a);
   const hipError_t err = hipGetLastError();

@@ -43,6 +43,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;    // [B*H*T] workspace: rowsum(dout * out)
+  float* lse2;     // [B*H*T] workspace: lse * log2(e) (bf16 path; written by dq)
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
   const KindDev* kinds;

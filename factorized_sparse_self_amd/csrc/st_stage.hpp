@@ -1,0 +1,127 @@
+// Direct global -> LDS staging of 64-row bf16 tiles for the gfx950 kernels.
+//
+// A tile holds 64 rows of D bf16 (row bytes RB = 2*D, no padding).  The 16-byte
+// chunk c of row r is stored at chunk c ^ (r mod CH), CH = D/8 chunks per row:
+// rows that an MFMA operand read touches at the same time land on different
+// banks, for both the row-operand reads and the LDS transpose reads.
+//
+// Loads use buffer_load ... lds (lds_dma): lane l of a wave writes its 16 bytes
+// to LDS base + 16*l, so one instruction fills 64/CH whole rows; the global chunk
+// a lane fetches is chosen so that the row it fills ends up swizzled.  An
+// out-of-range offset (padding row) writes zeros.  A wave stages its own 16
+// rows of every tile; a ring of LDS stages lets the loads of several tiles be
+// in flight (no registers hold them).
+#pragma once
+
+#include "st_device.hpp"
+
+namespace st {
+
+template <int D>
+struct TileShape {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int RB = D * 2;                 // bytes per row
+  static constexpr int BYTES = kBlock * RB;        // bytes per tile
+  static constexpr int RPI = 64 / CH;              // rows filled by one wave instruction
+  static constexpr int NI = 16 / RPI;              // instructions per wave per tile (16 rows)
+  static_assert(NI >= 1 && 16 % RPI == 0, "tile shape");
+  // byte offset of chunk c of row r inside a tile
+  __device__ static __forceinline__ int phys(int r, int c) { return r * RB + ((c ^ (r & (CH - 1))) << 4); }
+};
+
+// LDS byte address of a __shared__ pointer, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  typedef __attribute__((address_space(3))) const void* lds_ptr;
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr)p);
+}
+
+// One buffer_load ... lds of BYTES (16 or 4) per lane: lane l's bytes land at
+// LDS lds_base + BYTES*l.  Written as inline asm on purpose: the compiler's
+// wait-count insertion cannot tell the ring stages apart and would make every
+// LDS read wait for all DMA loads in flight, which serialises the ring; the
+// kernels order these loads with their own s_waitcnt vmcnt + barrier instead.
+// M0 carries the LDS base; it is saved and restored, and one wait state
+// separates the M0 write from the load that reads it.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(Rsrc r, uint32_t lds_base, uint32_t voff) {
+  uint32_t saved;
+  if constexpr (BYTES == 16) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(voff), "s"(r)
+        : "memory");
+  } else {
+    static_assert(BYTES == 4, "16- or 4-byte DMA");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(voff), "s"(r)
+        : "memory");
+  }
+}
+
+// Stage this wave's 16 rows (16*wave .. +15) of one 64-row tile of a [T, D]
+// bf16 tensor into `tile` (LDS).  pos[i] is the position held by tile row
+// 16*wave + i*RPI + lane/CH, or -1 for padding.
+template <int D>
+__device__ __forceinline__ void stage_rows(Rsrc src, unsigned char* tile, int wave, int lane,
+                                           const int (&pos)[TileShape<D>::NI]) {
+  using S = TileShape<D>;
+#pragma unroll
+  for (int i = 0; i < S::NI; ++i) {
+    const int r = 16 * wave + i * S::RPI + lane / S::CH;
+    const int lc = (lane % S::CH) ^ (r & (S::CH - 1));  // logical chunk this lane fetches
+    const uint32_t off = pos[i] >= 0 ? (uint32_t)(pos[i] * S::RB + lc * 16) : kOutOfRange;
+    lds_dma<16>(src, lds_address(tile + (16 * wave + i * S::RPI) * S::RB), off);
+  }
+}
+
+// Stage one fp32 value per row for this wave's 16 rows into `vals` (LDS):
+// row 16*wave + j lands at vals[64*wave + j]; lanes 16..63 write zeros into
+// the rest of the wave's 256-byte slot.
+__device__ __forceinline__ void stage_row_values(Rsrc src, float* vals, int wave, int lane, int pos) {
+  const uint32_t off = (lane < 16 && pos >= 0) ? (uint32_t)pos * 4 : kOutOfRange;
+  lds_dma<4>(src, lds_address(vals + 64 * wave), off);
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding
+// (loads complete in issue order).  n is a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] and [15:14]; expcnt[6:4] and lgkmcnt[11:8] left at their maximum
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Wait until this wave's LDS and scalar-memory operations have completed
+// (lgkmcnt 0; vmcnt and expcnt left at their maximum).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// wait_vmcnt<per_tile * k> for a runtime k in [0, KMAX].
+template <int PER_TILE, int KMAX>
+__device__ __forceinline__ void wait_tiles_left(int k) {
+  if constexpr (KMAX >= 3) {
+    if (k >= 3) {
+      wait_vmcnt<PER_TILE * 3>();
+      return;
+    }
+  }
+  if constexpr (KMAX >= 2) {
+    if (k == 2) {
+      wait_vmcnt<PER_TILE * 2>();
+      return;
+    }
+  }
+  if constexpr (KMAX >= 1) {
+    if (k == 1) {
+      wait_vmcnt<PER_TILE>();
+      return;
+    }
+  }
+  wait_vmcnt<0>();
+}
+
+}  // namespace st
