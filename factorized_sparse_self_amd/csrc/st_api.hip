@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -11,6 +12,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/st.h"
@@ -36,10 +38,11 @@ struct PlanKey {
 struct Plan {
   void* dmem = nullptr;  // single device allocation holding everything below
   KindDev* kinds = nullptr;
-  int2* row_items = nullptr;  // forward and dq
+  RowItem* row_items = nullptr;   // row blocks: fp32 forward, dq
+  RowItem* pair_items = nullptr;  // row-block pairs: bf16 forward
   DkdvItem* dkdv_items = nullptr;
   ReduceItem* red_items = nullptr;
-  int n_row_items = 0, n_dkdv_items = 0, n_red_items = 0, n_slots = 0;
+  int n_row_items = 0, n_pair_items = 0, n_dkdv_items = 0, n_red_items = 0, n_slots = 0;
   ~Plan() {
     if (dmem) (void)hipFree(dmem);
   }
@@ -125,19 +128,55 @@ int build_plan(const PlanKey& key, Plan* plan) {
 
   // Row-block items (forward and dq): every row block of every head; cost =
   // key blocks visited + 1; grouped by (head, range of row blocks).
-  std::vector<int2> rows;
+  std::vector<RowItem> rows;
   std::vector<int64_t> rcost, rgroup;
   for (int bh = 0; bh < BH; ++bh) {
     const int kind = (bh % key.H) & 1;
     const KindLayout& L = lay.kind[kind];
     for (int qb = 0; qb < L.n_qb; ++qb) {
-      rows.push_back(make_int2(qb, bh));
+      rows.push_back({qb, bh, kind, 0});
       rcost.push_back(L.row_ptr[qb + 1] - L.row_ptr[qb] + 1);
       rgroup.push_back((int64_t)bh * 65536 + qb / chunk[kind]);
     }
   }
-  std::vector<int2> row_items;
-  for (int i : xcd_order(rcost, rgroup)) row_items.push_back(i < 0 ? make_int2(-1, -1) : rows[i]);
+  std::vector<RowItem> row_items;
+  for (int i : xcd_order(rcost, rgroup)) row_items.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : rows[i]);
+
+  // Row-block pairs: the CSR rows of blocks 2p and 2p+1 merged (both ascending)
+  // into one list of key blocks with per-half visit / FULL bits.
+  std::vector<int32_t> pair_ptr[2];
+  std::vector<uint32_t> pair_entry[2];
+  for (int kind = 0; kind < 2; ++kind) {
+    const KindLayout& L = lay.kind[kind];
+    const int n_pairs = (L.n_qb + 1) / 2;
+    pair_ptr[kind].assign(n_pairs + 1, 0);
+    for (int pb = 0; pb < n_pairs; ++pb) {
+      int i0 = L.row_ptr[2 * pb], e0 = L.row_ptr[2 * pb + 1];
+      int i1 = 2 * pb + 1 < L.n_qb ? L.row_ptr[2 * pb + 1] : 0, e1 = 2 * pb + 1 < L.n_qb ? L.row_ptr[2 * pb + 2] : 0;
+      while (i0 < e0 || i1 < e1) {
+        const int k0 = i0 < e0 ? L.col_idx[i0] : INT_MAX, k1 = i1 < e1 ? L.col_idx[i1] : INT_MAX;
+        const int kb = std::min(k0, k1);
+        uint32_t bits = (uint32_t)kb;
+        if (k0 == kb) bits |= (kPairVisit | (L.flags[i0++] ? kPairFull : 0u)) << 28;
+        if (k1 == kb) bits |= (kPairVisit | (L.flags[i1++] ? kPairFull : 0u)) << 30;
+        pair_entry[kind].push_back(bits);
+      }
+      pair_ptr[kind][pb + 1] = (int32_t)pair_entry[kind].size();
+    }
+  }
+  std::vector<RowItem> pairs;
+  std::vector<int64_t> pcost, pgroup;
+  for (int bh = 0; bh < BH; ++bh) {
+    const int kind = (bh % key.H) & 1;
+    const int n_pairs = (int)pair_ptr[kind].size() - 1;
+    for (int pb = 0; pb < n_pairs; ++pb) {
+      pairs.push_back({pb, bh, kind, 0});
+      pcost.push_back(pair_ptr[kind][pb + 1] - pair_ptr[kind][pb] + 1);
+      pgroup.push_back((int64_t)bh * 65536 + 2 * pb / chunk[kind]);
+    }
+  }
+  std::vector<RowItem> pair_items;
+  for (int i : xcd_order(pcost, pgroup)) pair_items.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : pairs[i]);
 
   // dK/dV items: every key block of every head.  A key block whose row-block
   // list is longer than kDkdvSplit is split at row-block multiples of
@@ -154,7 +193,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
       const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
       const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
       if (e1 - e0 <= kDkdvSplit) {
-        dkdv.push_back({kb, bh, e0, e1, -1, 0, 0, 0});
+        dkdv.push_back({kb, bh, e0, e1, -1, kind, 0, 0});
         dcost.push_back(e1 - e0 + 1);
         dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
         continue;
@@ -164,12 +203,12 @@ int build_plan(const PlanKey& key, Plan* plan) {
         const int range = L.row_idx[a] / kDkdvSplit;
         int b = a;
         while (b < e1 && L.row_idx[b] / kDkdvSplit == range) ++b;
-        dkdv.push_back({kb, bh, a, b, slots++, 0, 0, 0});
+        dkdv.push_back({kb, bh, a, b, slots++, kind, 0, 0});
         dcost.push_back(b - a + 1);
         dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);
         a = b;
       }
-      red.push_back({kb, bh, slot0, slots - slot0});
+      red.push_back({kb, bh, slot0, slots - slot0, kind, 0, 0, 0});
     }
   }
   std::vector<DkdvItem> dkdv_items;
@@ -178,7 +217,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   Blob blob;
   KindDev kinds_host[2];
   size_t off_kinds = blob.add(kinds_host, sizeof(kinds_host));
-  size_t offs[2][8];
+  size_t offs[2][10];
   for (int kind = 0; kind < 2; ++kind) {
     const KindLayout& L = lay.kind[kind];
     offs[kind][0] = blob.add(L.row_ptr.data(), L.row_ptr.size() * 4);
@@ -192,8 +231,11 @@ int build_plan(const PlanKey& key, Plan* plan) {
     for (size_t e = 0; e < csc.size(); ++e) csc[e] = (uint32_t)L.row_idx[e] | (L.csc_flags[e] ? kFullBit : 0u);
     offs[kind][6] = blob.add(csr.data(), csr.size() * 4);
     offs[kind][7] = blob.add(csc.data(), csc.size() * 4);
+    offs[kind][8] = blob.add(pair_ptr[kind].data(), pair_ptr[kind].size() * 4);
+    offs[kind][9] = blob.add(pair_entry[kind].data(), pair_entry[kind].size() * 4);
   }
-  const size_t off_rows = blob.add(row_items.data(), row_items.size() * sizeof(int2));
+  const size_t off_rows = blob.add(row_items.data(), row_items.size() * sizeof(RowItem));
+  const size_t off_pairs = blob.add(pair_items.data(), pair_items.size() * sizeof(RowItem));
   const size_t off_dkdv = blob.add(dkdv_items.data(), dkdv_items.size() * sizeof(DkdvItem));
   const size_t off_red = blob.add(red.data(), red.size() * sizeof(ReduceItem));
 
@@ -216,15 +258,19 @@ int build_plan(const PlanKey& key, Plan* plan) {
     k.csc_flags = (const uint8_t*)(dbase + offs[kind][5]);
     k.csr_entry = (const uint32_t*)(dbase + offs[kind][6]);
     k.csc_entry = (const uint32_t*)(dbase + offs[kind][7]);
+    k.pair_ptr = (const int32_t*)(dbase + offs[kind][8]);
+    k.pair_entry = (const uint32_t*)(dbase + offs[kind][9]);
   }
   std::memcpy(blob.bytes.data() + off_kinds, kinds_host, sizeof(kinds_host));
   e = hipMemcpy(plan->dmem, blob.bytes.data(), blob.bytes.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail("plan upload", e);
   plan->kinds = (KindDev*)(dbase + off_kinds);
-  plan->row_items = (int2*)(dbase + off_rows);
+  plan->row_items = (RowItem*)(dbase + off_rows);
   plan->dkdv_items = (DkdvItem*)(dbase + off_dkdv);
   plan->red_items = (ReduceItem*)(dbase + off_red);
+  plan->pair_items = (RowItem*)(dbase + off_pairs);
   plan->n_row_items = (int)row_items.size();
+  plan->n_pair_items = (int)pair_items.size();
   plan->n_dkdv_items = (int)dkdv_items.size();
   plan->n_red_items = (int)red.size();
   plan->n_slots = slots;
@@ -321,10 +367,14 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   a.H = H;
   a.T = T;
   a.kinds = plan->kinds;
-  a.items = plan->row_items;
+  // bf16: one workgroup per pair of row blocks; fp32: per row block
+  const bool pairs = std::is_same<TE, bf16>::value;
+  a.items = pairs ? plan->pair_items : plan->row_items;
+  const int n_items = pairs ? plan->n_pair_items : plan->n_row_items;
   a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.pattern = pattern;
   hipStream_t s = (hipStream_t)stream;
-  e = (D == 32) ? launch_fwd<TE, 32>(a, plan->n_row_items, s) : launch_fwd<TE, 64>(a, plan->n_row_items, s);
+  e = (D == 32) ? launch_fwd<TE, 32>(a, n_items, s) : launch_fwd<TE, 64>(a, n_items, s);
   if (e != hipSuccess) return hip_fail(fn, e);
   return ST_OK;
 }
@@ -367,13 +417,15 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.T = T;
   a.kinds = plan->kinds;
   a.dq_items = plan->row_items;
+  const int n_dq = plan->n_row_items;
   a.dkdv_items = plan->dkdv_items;
   a.red_items = plan->red_items;
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.pattern = pattern;
   hipStream_t s = (hipStream_t)stream;
-  e = (D == 32) ? launch_bwd<TE, 32>(a, plan->n_row_items, plan->n_dkdv_items, plan->n_red_items, s)
-                : launch_bwd<TE, 64>(a, plan->n_row_items, plan->n_dkdv_items, plan->n_red_items, s);
+  e = (D == 32) ? launch_bwd<TE, 32>(a, n_dq, plan->n_dkdv_items, plan->n_red_items, s)
+                : launch_bwd<TE, 64>(a, n_dq, plan->n_dkdv_items, plan->n_red_items, s);
   if (e != hipSuccess) return hip_fail(fn, e);
   return ST_OK;
 }

@@ -125,10 +125,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) TE Vs[L::R_ELEMS];
   __shared__ __attribute__((aligned(16))) TE Kt[L::T_ELEMS];
 
-  const int2 item = load_uniform(&a.dq_items[blockIdx.x]);
-  if (item.x < 0) return;  // schedule padding
-  const int qb = item.x, bh = item.y;
-  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
+  const RowItem item = load_uniform(&a.dq_items[blockIdx.x]);
+  if (item.qb < 0) return;  // schedule padding
+  const int qb = item.qb, bh = item.bh;
+  const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const Geometry& g = kd.geo;
   const size_t base = (size_t)bh * a.T * D;
   const TE* __restrict__ Qg = (const TE*)a.q + base;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
   if (item.kb < 0) return;  // schedule padding
   const int kb = item.kb, bh = item.bh;
-  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
+  const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const Geometry& g = kd.geo;
   const size_t base = (size_t)bh * a.T * D;
   const TE* __restrict__ Qg = (const TE*)a.q + base;
@@ -500,18 +500,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 // without masks; every transposed MFMA operand (K^T, Q^T, dO^T) comes from
 // LDS transpose reads.
 // ---------------------------------------------------------------------------
-template <int D, int NS>
-__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
+template <int D, int NS, int KC>
+__device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int bh, int kind,
+                                                 unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
   constexpr int NQ = D / 32, ND = D / 16, CH = D / 8;
   constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
-  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][S::BYTES];
-
-  const int2 item = load_uniform(&a.dq_items[blockIdx.x]);
-  if (item.x < 0) return;  // schedule padding
-  const int qb = item.x, bh = item.y;
-  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
-  const Geometry& g = kd.geo;
+  const KindDev kd = load_uniform(&a.kinds[kind]);
+  const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
   const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
@@ -519,15 +515,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
   const Rsrc rg = make_rsrc((const bf16*)a.dout + base, head_bytes);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const StageRows<S::NI, S::RPI> stage(g, true, 16 * wave + lane / S::CH);
   const cptr<uint32_t> entries = as_const(kd.csr_entry);
+  // LDS address of this wave's 16 rows in stage 0's K tile (V follows at
+  // +BYTES, stage s at +s*STAGE)
+  constexpr uint32_t STAGE = 2 * S::BYTES;
+  const uint32_t lds_rows = lds_address(&ring[0][0][16 * wave * S::RB]);
   auto issue = [&](int e, int stg) {
     int p[S::NI];
     stage.positions(g, true, (int)(entries[e] & ~kFullBit), p);
-    stage_rows<D>(rk, ring[stg][0], wave, lane, p);
-    stage_rows<D>(rv, ring[stg][1], wave, lane, p);
+    stage_rows<D>(rk, lds_rows + stg * STAGE, lane, p);
+    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, lane, p);
   };
   // The first NS-1 key blocks are in flight while the row's own operands load
   // (those loads are younger, so the compiler's waits for them cover the ring's
@@ -541,8 +542,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   int lo = 1, hi = 0;
   if (t >= 0) row_interval(g, qb * kBlock + wave * 16 + li, t, lo, hi);
   const bool row_live = lo <= hi;
-  const int wlo = uniform(wave_min(row_live ? lo : 0x7fffffff));
-  const int whi = uniform(wave_max(row_live ? hi : -1));
   const int mlo = row_live ? lo : -(1 << 30);
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
   // Delta_t = dO_t . O_t: each of the row's four lanes holds a quarter of the
@@ -572,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   }
   // keys nobody attends (positions outside a summary head's key map) get
   // dk = dv = 0; the row positions of this block cover every such position
-  if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
+  if constexpr (KC == K_SUMMARY || KC == K_SUMMARY_R1) {
     for (int u = tid; u < kBlock * CH; u += kThreads) {
       const int r = u / CH, ch = u % CH;
       const int tp = block_position(g, false, qb, r);
@@ -594,93 +593,100 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
 
-  auto block = [&](auto full_c, const unsigned char* Kt, const unsigned char* Vt, int kb) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const int k0 = kb * kBlock;
-    bool need[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) need[b] = FULL || (k0 + 16 * b <= whi && k0 + 16 * b + 15 >= wlo);
-    f32x4 s[4], dp[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      s[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (!need[b]) continue;
-#pragma unroll
-      for (int k = 0; k < NQ; ++k) {
-        s[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]), qop[k], s[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(Vt + 16 * b * S::RB + a_off[k]), gop[k], dp[b]);
-      }
-    }
-    const int m0 = k0 + 4 * lg - mlo;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = fast_exp2(fmaf(s[b][i], sl2, -lse2));
-        if (!FULL && (uint32_t)(m0 + 16 * b + i) > mspan) p = 0.f;
-        s[b][i] = p * (dp[b][i] - delta);
-      }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-      bf16x8 hi8, lo8;
-      split_b_operand(s[2 * kk], s[2 * kk + 1], hi8, lo8);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const unsigned char* r0 = Kt + 32 * kk * S::RB + t_off[d];
-        const bf16x8 ak = concat(lds_read_tr((const bf16*)r0), lds_read_tr((const bf16*)(r0 + 16 * S::RB)));
-        acc[d] = mfma_bf16(ak, hi8, acc[d]);
-        acc[d] = mfma_bf16(ak, lo8, acc[d]);
-      }
-    }
-  };
-
+  // One code path for every block: PARTIAL blocks only add the mask.
   for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
     const uint32_t entry = entries[e];
-    const int kb = (int)(entry & ~kFullBit);
+    const int k0 = (int)(entry & ~kFullBit) * kBlock;
     const bool full = (entry & kFullBit) != 0;
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
     __syncthreads();
     if (e + NS - 1 < e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
-    if (whi < 0) continue;
-    if (full)
-      block(std::true_type(), ring[stg][0], ring[stg][1], kb);
-    else
-      block(std::false_type(), ring[stg][0], ring[stg][1], kb);
+    const unsigned char* Kt = ring[stg][0];
+    const unsigned char* Vt = ring[stg][1];
+    // S^T = K Q^T and dP^T = V dO^T
+    f32x4 sc[4], dp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        sc[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]), qop[k], sc[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(Vt + 16 * b * S::RB + a_off[k]), gop[k], dp[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[b][i] = fast_exp2(fmaf(sc[b][i], sl2, -lse2));
+    if (!full) {
+      const int m0 = k0 + 4 * lg - mlo;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((uint32_t)(m0 + 16 * b + i) > mspan) sc[b][i] = 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[b][i] *= dp[b][i] - delta;
+    // dQ^T += K^T dS^T, dS as a bf16 hi + lo pair
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 hi8, lo8;
+      split_b_operand(sc[2 * kk], sc[2 * kk + 1], hi8, lo8);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const unsigned char* r = Kt + 32 * kk * S::RB + t_off[d];
+        const bf16x8 ak = concat(lds_read_tr((const bf16*)r), lds_read_tr((const bf16*)(r + 16 * S::RB)));
+        acc[d] = mfma_bf16(ak, hi8, acc[d]);
+        acc[d] = mfma_bf16(ak, lo8, acc[d]);
+      }
+    }
   }
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   if (t < 0) return;
   bf16* dq = (bf16*)a.dq + base + (size_t)t * D;
 #pragma unroll
   for (int d = 0; d < ND; ++d) *(bf16x4*)(dq + 16 * d + 4 * lg) = to_bf16x4(acc[d] * a.scale);
 }
 
+// One kernel per pattern; each workgroup branches once on its head's kind.
+template <int D, int NS, int C0, int C1>
+__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
+  const RowItem item = load_uniform(&a.dq_items[blockIdx.x]);
+  if (item.qb < 0) return;  // schedule padding
+  if (C0 == C1 || item.kind == 0)
+    bwd_dq_bf16_body<D, NS, C0>(a, item.qb, item.bh, 0, ring);
+  else
+    bwd_dq_bf16_body<D, NS, C1>(a, item.qb, item.bh, 1, ring);
+}
+
 // dk/dv: Q and dO blocks with their lse*log2(e) and Delta are staged by
 // direct global->LDS loads into a ring of NS stages (st_stage.hpp), so the
 // loads of NS-1 row blocks are in flight while one is computed; each row's
 // key run (for masks) is computed and stored next to them.
-// At most 168 VGPRs: three waves per SIMD (three workgroups per CU with the
-// two-stage ring) beat two waves with deeper prefetch; four waves would spill.
-template <int D, int NS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_bf16_kernel(
-    BwdArgs a) {
+template <int D>
+struct DkdvStage {
+  unsigned char q[TileShape<D>::BYTES];
+  unsigned char g[TileShape<D>::BYTES];
+  float lse2[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 16)
+  float delta[4 * 64];
+  int lo[kBlock];       // masking base of each row
+  int span[kBlock];     // masking span (unsigned)
+};
+
+template <int D, int NS, int KC>
+__device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvItem& item,
+                                                   DkdvStage<D>* ring) {
   using S = TileShape<D>;
   constexpr int NQ = D / 32, ND = D / 16;
   constexpr int PER_TILE = 2 * S::NI + 2;  // loads per wave per row block: Q, dO, lse2, Delta
-  struct Stage {
-    unsigned char q[S::BYTES];
-    unsigned char g[S::BYTES];
-    float lse2[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 16)
-    float delta[4 * 64];
-    int lo[kBlock];       // masking base of each row
-    int span[kBlock];     // masking span (unsigned)
-  };
-  __shared__ __attribute__((aligned(16))) Stage ring[NS];
-
-  const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
-  if (item.kb < 0) return;  // schedule padding
+  using Stage = DkdvStage<D>;
   const int kb = item.kb, bh = item.bh;
-  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
-  const Geometry& g = kd.geo;
+  const KindDev kd = load_uniform(&a.kinds[item.kind]);
+  const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
   const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
@@ -709,88 +715,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   const StageRows<S::NI, S::RPI> stage(g, false, 16 * wave + lane / S::CH);
   const StageRows<1, kBlock> stage_own(g, false, 16 * wave + li);  // this lane's row, lanes 0..15
   const cptr<uint32_t> entries = as_const(kd.csc_entry);
+  // LDS addresses, in stage 0, of this wave's 16 Q rows (dO follows at
+  // +BYTES) and of its lse2 slot (Delta follows at +DELTA); stage s at
+  // +s*sizeof(Stage)
+  constexpr uint32_t DELTA = offsetof(Stage, delta) - offsetof(Stage, lse2);
+  static_assert(offsetof(Stage, g) - offsetof(Stage, q) == S::BYTES, "stage layout");
+  const uint32_t lds_rows = lds_address(&ring[0].q[16 * wave * S::RB]);
+  const uint32_t lds_vals = lds_address(&ring[0].lse2[64 * wave]);
   auto issue = [&](int e, int stg) {
     const int qb = (int)(entries[e] & ~kFullBit);
+    const uint32_t so = stg * (uint32_t)sizeof(Stage);
     int p[S::NI];
     stage.positions(g, false, qb, p);
-    stage_rows<D>(rq, ring[stg].q, wave, lane, p);
-    stage_rows<D>(rg, ring[stg].g, wave, lane, p);
+    stage_rows<D>(rq, lds_rows + so, lane, p);
+    stage_rows<D>(rg, lds_rows + so + S::BYTES, lane, p);
     int tp[1];
     stage_own.positions(g, false, qb, tp);
     int lo = 1, hi = 0;
     if (tp[0] >= 0) row_interval(g, qb * kBlock + 16 * wave + li, tp[0], lo, hi);
     const bool live = lo <= hi;
-    stage_row_values(rl, ring[stg].lse2, wave, lane, live ? tp[0] : -1);
-    stage_row_values(rd, ring[stg].delta, wave, lane, live ? tp[0] : -1);
+    stage_row_values(rl, lds_vals + so, lane, live ? tp[0] : -1);
+    stage_row_values(rd, lds_vals + so + DELTA, lane, live ? tp[0] : -1);
     if (lane < 16) {
       ring[stg].lo[16 * wave + lane] = live ? lo : -(1 << 30);
       ring[stg].span[16 * wave + lane] = live ? hi - lo : 0;
-    }
-  };
-
-  auto block = [&](auto full_c, const Stage& st) {
-    constexpr bool FULL = decltype(full_c)::value;
-    bool need[4] = {true, true, true, true};
-    if (!FULL) {
-      // which 16-row blocks hold a row whose key run meets this wave's 16 keys
-      const int rlo = st.lo[lane];
-      const uint32_t rspan = (uint32_t)st.span[lane];
-      const bool meets = rlo > -(1 << 30) && rlo <= Kw0 + 15 && (int64_t)rlo + rspan >= Kw0;
-      const uint64_t hit = __ballot(meets);
-      if (hit == 0) return;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) need[b] = ((hit >> (16 * b)) & 0xffffull) != 0;
-    }
-    f32x4 s[4], dp[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      s[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (!need[b]) continue;
-#pragma unroll
-      for (int k = 0; k < NQ; ++k) {
-        s[b] = mfma_bf16(*(const bf16x8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], s[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[b]);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r0 = 16 * b + 4 * lg;  // rows r0 .. r0+3 of this lane's values
-      const float4 l2 = *(const float4*)(&st.lse2[64 * b + 4 * lg]);
-      const float4 de = *(const float4*)(&st.delta[64 * b + 4 * lg]);
-      const float l2a[4] = {l2.x, l2.y, l2.z, l2.w};
-      const float dea[4] = {de.x, de.y, de.z, de.w};
-      int loa[4] = {0, 0, 0, 0}, spa[4] = {0, 0, 0, 0};
-      if (!FULL) {
-        const int4 lo4 = *(const int4*)(&st.lo[r0]);
-        const int4 sp4 = *(const int4*)(&st.span[r0]);
-        loa[0] = lo4.x; loa[1] = lo4.y; loa[2] = lo4.z; loa[3] = lo4.w;
-        spa[0] = sp4.x; spa[1] = sp4.y; spa[2] = sp4.z; spa[3] = sp4.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = fast_exp2(fmaf(s[b][i], sl2, -l2a[i]));
-        if (!FULL && (uint32_t)(Kl - loa[i]) > (uint32_t)spa[i]) p = 0.f;
-        s[b][i] = p;
-        dp[b][i] = p * (dp[b][i] - dea[i]);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-      bf16x8 p_hi, p_lo, d_hi, d_lo;
-      split_b_operand(s[2 * kk], s[2 * kk + 1], p_hi, p_lo);
-      split_b_operand(dp[2 * kk], dp[2 * kk + 1], d_hi, d_lo);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
-        const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
-        const bf16x8 ag = concat(lds_read_tr((const bf16*)rg0), lds_read_tr((const bf16*)(rg0 + 16 * S::RB)));
-        const bf16x8 aq = concat(lds_read_tr((const bf16*)rq0), lds_read_tr((const bf16*)(rq0 + 16 * S::RB)));
-        dv[d] = mfma_bf16(ag, p_hi, dv[d]);
-        dv[d] = mfma_bf16(ag, p_lo, dv[d]);
-        dk[d] = mfma_bf16(aq, d_hi, dk[d]);
-        dk[d] = mfma_bf16(aq, d_lo, dk[d]);
-      }
     }
   };
 
@@ -801,12 +749,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const StageRows<S::NI, S::RPI> kstage(g, true, 16 * wave + lane / S::CH);
     int p[S::NI];
     kstage.positions(g, true, kb, p);
-    stage_rows<D>(rk, ring[NS - 1].q, wave, lane, p);
-    stage_rows<D>(rv, ring[NS - 1].g, wave, lane, p);
+    stage_rows<D>(rk, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage), lane, p);
+    stage_rows<D>(rv, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage) + S::BYTES, lane, p);
   }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (item.e0 + j < item.e1) issue(item.e0 + j, j);
+  // One code path for every block: PARTIAL blocks only add the mask.
   for (int e = item.e0, stg = 0; e < item.e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
     const bool full = (entries[e] & kFullBit) != 0;
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, item.e1 - 1 - e));
@@ -822,11 +771,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
       wait_lgkmcnt0();
     }
     if (e + NS - 1 < item.e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
-    if (full)
-      block(std::true_type(), ring[stg]);
-    else
-      block(std::false_type(), ring[stg]);
+    const Stage& st = ring[stg];
+    f32x4 sc[4], dp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        sc[b] = mfma_bf16(*(const bf16x8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[b]);
+      }
+    }
+    // rows 16b + 4lg + i of this lane's values
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4 l2 = *(const float4*)(&st.lse2[64 * b + 4 * lg]);
+      sc[b][0] = fast_exp2(fmaf(sc[b][0], sl2, -l2.x));
+      sc[b][1] = fast_exp2(fmaf(sc[b][1], sl2, -l2.y));
+      sc[b][2] = fast_exp2(fmaf(sc[b][2], sl2, -l2.z));
+      sc[b][3] = fast_exp2(fmaf(sc[b][3], sl2, -l2.w));
+    }
+    if (!full) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int4 lo4 = *(const int4*)(&st.lo[16 * b + 4 * lg]);
+        const int4 sp4 = *(const int4*)(&st.span[16 * b + 4 * lg]);
+        if ((uint32_t)(Kl - lo4.x) > (uint32_t)sp4.x) sc[b][0] = 0.f;
+        if ((uint32_t)(Kl - lo4.y) > (uint32_t)sp4.y) sc[b][1] = 0.f;
+        if ((uint32_t)(Kl - lo4.z) > (uint32_t)sp4.z) sc[b][2] = 0.f;
+        if ((uint32_t)(Kl - lo4.w) > (uint32_t)sp4.w) sc[b][3] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4 de = *(const float4*)(&st.delta[64 * b + 4 * lg]);
+      dp[b][0] = sc[b][0] * (dp[b][0] - de.x);
+      dp[b][1] = sc[b][1] * (dp[b][1] - de.y);
+      dp[b][2] = sc[b][2] * (dp[b][2] - de.z);
+      dp[b][3] = sc[b][3] * (dp[b][3] - de.w);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 p_hi, p_lo, d_hi, d_lo;
+      split_b_operand(sc[2 * kk], sc[2 * kk + 1], p_hi, p_lo);
+      split_b_operand(dp[2 * kk], dp[2 * kk + 1], d_hi, d_lo);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
+        const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
+        const bf16x8 ag = concat(lds_read_tr((const bf16*)rg0), lds_read_tr((const bf16*)(rg0 + 16 * S::RB)));
+        const bf16x8 aq = concat(lds_read_tr((const bf16*)rq0), lds_read_tr((const bf16*)(rq0 + 16 * S::RB)));
+        dv[d] = mfma_bf16(ag, p_hi, dv[d]);
+        dv[d] = mfma_bf16(ag, p_lo, dv[d]);
+        dk[d] = mfma_bf16(aq, d_hi, dk[d]);
+        dk[d] = mfma_bf16(aq, d_lo, dk[d]);
+      }
+    }
   }
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
 
   if (item.slot < 0) {
     if (kp < 0) return;
@@ -849,6 +851,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   }
 }
 
+// At most 168 VGPRs: three waves per SIMD (three workgroups per CU with the
+// two-stage ring) beat two waves with deeper prefetch; four waves would spill.
+template <int D, int NS, int C0, int C1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_bf16_kernel(
+    BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) DkdvStage<D> ring[NS];
+  const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
+  if (item.kb < 0) return;  // schedule padding
+  if (C0 == C1 || item.kind == 0)
+    bwd_dkdv_bf16_body<D, NS, C0>(a, item, ring);
+  else
+    bwd_dkdv_bf16_body<D, NS, C1>(a, item, ring);
+}
+
 // ---------------------------------------------------------------------------
 // red: sum the fp32 partials of a split key block and store dk / dv.
 // ---------------------------------------------------------------------------
@@ -859,7 +875,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
   constexpr int kParts = 2 * kBlock * CH / kThreads;
   const ReduceItem item = load_uniform(&a.red_items[blockIdx.x / kParts]);
   if (item.kb < 0) return;  // schedule padding
-  const KindDev kd = load_uniform(&a.kinds[(item.bh % a.H) & 1]);
+  const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const size_t base = (size_t)item.bh * a.T * D;
   const int u = (blockIdx.x % kParts) * kThreads + threadIdx.x;
   const int which = u / (kBlock * CH);  // 0 = dk, 1 = dv
@@ -902,21 +918,31 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   }
   if (n_dq > 0) {
     timing_begin(KID_DQ, stream);
-    if constexpr (IsBf16<TE>::value)
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kDqStages>), dim3(n_dq), dim3(kThreads), 0, stream, a);
-    else
+    if constexpr (IsBf16<TE>::value) {
+      err = with_kind_codes(a.pattern, [&](auto c0, auto c1) {
+        hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kDqStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_dq),
+                           dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+      });
+    } else {
       hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
-    err = hipGetLastError();
+      err = hipGetLastError();
+    }
     timing_end(KID_DQ, stream);
     if (err != hipSuccess) return err;
   }
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
-    if constexpr (IsBf16<TE>::value)
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kDkdvStages>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
-    else
+    if constexpr (IsBf16<TE>::value) {
+      err = with_kind_codes(a.pattern, [&](auto c0, auto c1) {
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kDkdvStages, decltype(c0)::value, decltype(c1)::value>),
+                           dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+      });
+    } else {
       hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
-    err = hipGetLastError();
+      err = hipGetLastError();
+    }
     timing_end(KID_DKDV, stream);
     if (err != hipSuccess) return err;
   }

@@ -135,7 +135,8 @@ template <int NLD, int RSTEP>
 struct StageRows {
   int row[NLD], off[NLD];
   bool split;
-  __device__ __forceinline__ StageRows(const Geometry& g, bool keys, int srow) {
+  template <class G>
+  __device__ __forceinline__ StageRows(const G& g, bool keys, int srow) {
     split = split_position_ok(g, keys);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -143,7 +144,8 @@ struct StageRows {
       off[i] = split ? row_part(g, keys, row[i]).off : 0;
     }
   }
-  __device__ __forceinline__ void positions(const Geometry& g, bool keys, int blk, int (&p)[NLD]) const {
+  template <class G>
+  __device__ __forceinline__ void positions(const G& g, bool keys, int blk, int (&p)[NLD]) const {
     if (split) {
       const BlockPart bp = block_part(g, keys, blk);
 #pragma unroll
@@ -188,8 +190,11 @@ __device__ __forceinline__ float buf_load_f32(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
-__device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, 64); }
-__device__ __forceinline__ int xor_shfl(int v, int m) { return __shfl_xor(v, m, 64); }
+// Value of lane (lane ^ m) of the wave (ds_bpermute; m < 64).
+__device__ __forceinline__ int xor_shfl(int v, int m) {
+  return __builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ m) << 2), v);
+}
+__device__ __forceinline__ float xor_shfl(float v, int m) { return __int_as_float(xor_shfl(__float_as_int(v), m)); }
 
 // Reduce over the four lanes that share li (lg = 0..3).
 __device__ __forceinline__ float group4_max(float v) {
@@ -227,6 +232,13 @@ struct KindDev {
   const uint8_t* csc_flags;
   const uint32_t* csr_entry;  // col_idx | flags << 31
   const uint32_t* csc_entry;  // row_idx | csc_flags << 31
+  // Row-block pairs (2p, 2p+1): the union of the two CSR rows, one dword per
+  // key block: block | half-0 bits << 28 | half-1 bits << 30, where the two
+  // bits of a half are kPairVisit (the row block visits the key block) and
+  // kPairFull (it is FULL for that row block).
+  const int32_t* pair_ptr;
+  const uint32_t* pair_entry;
 };
+constexpr uint32_t kPairVisit = 1u, kPairFull = 2u, kPairBlockMask = 0x0fffffffu;
 
 }  // namespace st

@@ -103,9 +103,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) TE Ks[L::K_ELEMS];
   __shared__ __attribute__((aligned(16))) TE Vs[L::V_ELEMS];
 
-  const int2 item = load_uniform(&a.items[blockIdx.x]);
-  if (item.x < 0) return;  // schedule padding
-  const int qb = item.x, bh = item.y;
+  const RowItem item = load_uniform(&a.items[blockIdx.x]);
+  if (item.qb < 0) return;  // schedule padding
+  const int qb = item.qb, bh = item.bh;
   const int h = bh % a.H;
   const KindDev kd = load_uniform(&a.kinds[h & 1]);
   const Geometry& g = kd.geo;
@@ -273,38 +273,41 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 //    when a logit exceeds it by more than 2^8 in exp2 units; blocks where no
 //    lane of the wave needs that skip the cross-lane max and the rescale.
 // ---------------------------------------------------------------------------
-template <int D, int NS>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
+template <int D, int NS, int KC>
+__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, int kind,
+                                              unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
-  constexpr int NQ = D / 32;                 // MFMA k-steps over D
-  constexpr int ND = D / 16;                 // 16-wide output column blocks
-  constexpr int PER_TILE = 2 * S::NI;        // loads per wave per block (K and V)
-  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][S::BYTES];
-
-  const int2 item = load_uniform(&a.items[blockIdx.x]);
-  if (item.x < 0) return;  // schedule padding
-  const int qb = item.x, bh = item.y;
-  const KindDev kd = load_uniform(&a.kinds[(bh % a.H) & 1]);
-  const Geometry& g = kd.geo;
+  constexpr int NQ = D / 32;           // MFMA k-steps over D
+  constexpr int ND = D / 16;           // 16-wide output column blocks
+  constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
+  const KindDev kd = load_uniform(&a.kinds[kind]);
+  const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
   const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
   const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
   const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const int t = block_position(g, false, qb, wave * 16 + li);
-  int lo = 1, hi = 0;
-  if (t >= 0) row_interval(g, qb * kBlock + wave * 16 + li, t, lo, hi);
-  const bool row_live = lo <= hi;
-  const int wlo = uniform(wave_min(row_live ? lo : 0x7fffffff));
-  const int whi = uniform(wave_max(row_live ? hi : -1));
-  // logit of kernel key K is masked when (unsigned)(K - mlo) > mspan
-  const int mlo = row_live ? lo : -(1 << 30);
-  const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
-
-  bf16x8 qop[NQ];  // this wave's 16 query rows as MFMA B operands (from LDS, first block)
+  // Waves 0-1 take row block 2pb, waves 2-3 row block 2pb+1; a wave owns 32
+  // rows, two MFMA groups of 16 (G = 0, 1) that share every K and V operand.
+  const int half = wave >> 1;
+  const int qb = 2 * pb + half;
+  const int r0 = (wave & 1) * 32;
+  int t[2], mlo[2];
+  uint32_t mspan[2];
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    const int r = r0 + 16 * G + li;
+    t[G] = block_position(g, false, qb, r);
+    int lo = 1, hi = 0;
+    if (t[G] >= 0) row_interval(g, qb * kBlock + r, t[G], lo, hi);
+    // logit of kernel key K is masked when (unsigned)(K - mlo) > mspan
+    mlo[G] = lo <= hi ? lo : -(1 << 30);
+    mspan[G] = lo <= hi ? (uint32_t)(hi - lo) : 0u;
+  }
 
   // per-lane byte offsets of the MFMA operand reads inside a staged block
   int a_off[NQ], t_off[ND];
@@ -313,136 +316,188 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
 
-  f32x4 acc[ND];
+  bf16x8 qop[2][NQ];  // the two groups' query rows as MFMA B operands (from LDS, first block)
+  f32x4 acc[2][ND];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int G = 0; G < 2; ++G)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[G][d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
   const float headroom = 8.0f / sl2;  // raw-logit growth allowed before a rescale
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
   const StageRows<S::NI, S::RPI> stage(g, true, 16 * wave + lane / S::CH);
-  const cptr<uint32_t> entries = as_const(kd.csr_entry);
+  const cptr<uint32_t> entries = as_const(kd.pair_entry);
+  // LDS address of this wave's 16 staging rows in stage 0's K tile (V follows
+  // at +BYTES, stage s at +s*STAGE)
+  constexpr uint32_t STAGE = 2 * S::BYTES;
+  const uint32_t lds_rows = lds_address(&ring[0][0][16 * wave * S::RB]);
   auto issue = [&](int e, int stg) {
     int p[S::NI];
-    stage.positions(g, true, (int)(entries[e] & ~kFullBit), p);
-    stage_rows<D>(rk, ring[stg][0], wave, lane, p);
-    stage_rows<D>(rv, ring[stg][1], wave, lane, p);
+    stage.positions(g, true, (int)(entries[e] & kPairBlockMask), p);
+    stage_rows<D>(rk, lds_rows + stg * STAGE, lane, p);
+    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, lane, p);
   };
 
-  auto block = [&](auto full_c, const unsigned char* Kt, const unsigned char* Vt, int kb) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const int k0 = kb * kBlock;
-    bool need[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) need[b] = FULL || (k0 + 16 * b <= whi && k0 + 16 * b + 15 >= wlo);
-    f32x4 s[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      s[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (!need[b]) continue;
-#pragma unroll
-      for (int k = 0; k < NQ; ++k)
-        s[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]), qop[k], s[b]);
-    }
-    if (!FULL) {
-      const int m0 = k0 + 4 * lg - mlo;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((uint32_t)(m0 + 16 * b + i) > mspan) s[b][i] = -INFINITY;
-    }
-    float lm = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) lm = fmaxf(fmaxf(lm, fmaxf(s[b][0], s[b][1])), fmaxf(s[b][2], s[b][3]));
-    if (wave_any(lm > m_run + headroom)) {
-      const float mt = group4_max(lm);
-      const bool raise = mt > m_run + headroom;
-      // raising rows scale by exp2((old - new) max), 0 when the old max is -inf;
-      // the others keep their sums (factor exactly 1, never -inf - -inf)
-      const float alpha = raise ? fast_exp2((m_run - mt) * sl2) : 1.f;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
-      l_run *= alpha;
-      m_run = raise ? mt : m_run;
-    }
-    const float mb = (m_run == -INFINITY) ? 0.f : m_run * sl2;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[b][i] = fast_exp2(fmaf(s[b][i], sl2, -mb));
-        l_run += s[b][i];
-      }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-      const bf16x8 pb = pack_b_operand(s[2 * kk], s[2 * kk + 1]);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const unsigned char* r0 = Vt + 32 * kk * S::RB + t_off[d];
-        const bf16x8 av = concat(lds_read_tr((const bf16*)r0), lds_read_tr((const bf16*)(r0 + 16 * S::RB)));
-        acc[d] = mfma_bf16(av, pb, acc[d]);
-      }
-    }
-  };
-
-  const cptr<int32_t> row_ptr = as_const(kd.row_ptr);
-  const int e0 = row_ptr[qb], e1 = row_ptr[qb + 1];
-  // The row block's Q rows go through the last ring stage (free until the
-  // first iteration refills it), ahead of the first NS-1 key blocks, so every
-  // global load of the loop is a ring DMA.
+  const cptr<int32_t> pair_ptr = as_const(kd.pair_ptr);
+  const int e0 = pair_ptr[pb], e1 = pair_ptr[pb + 1];
+  // The two row blocks' Q rows go through the last ring stage (free until the
+  // first iteration refills it: row block 2pb in the K tile, 2pb+1 in the V
+  // tile), ahead of the first NS-1 key blocks, so every global load of the
+  // loop is a ring DMA.
   if (e0 < e1) {
     const StageRows<S::NI, S::RPI> qstage(g, false, 16 * wave + lane / S::CH);
-    int p[S::NI];
-    qstage.positions(g, false, qb, p);
-    stage_rows<D>(rq, ring[NS - 1][0], wave, lane, p);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      int p[S::NI];
+      qstage.positions(g, false, 2 * pb + hb, p);
+      stage_rows<D>(rq, lds_rows + (NS - 1) * STAGE + hb * S::BYTES, lane, p);
+    }
   }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (e0 + j < e1) issue(e0 + j, j);
   for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
     const uint32_t entry = entries[e];
-    const int kb = (int)(entry & ~kFullBit);
-    const bool full = (entry & kFullBit) != 0;
+    const int k0 = (int)(entry & kPairBlockMask) * kBlock;
+    const uint32_t hbits = (entry >> (28 + 2 * half)) & 3u;  // this row block's visit / FULL bits
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
     __syncthreads();
     if (e == e0) {
-      // this wave's own DMA, complete with the first block
+      // the wave's own rows, staged by all four waves: complete after the barrier
+      const unsigned char* qt = ring[NS - 1][half] + r0 * S::RB;
 #pragma unroll
-      for (int k = 0; k < NQ; ++k) qop[k] = *(const bf16x8*)(ring[NS - 1][0] + 16 * wave * S::RB + a_off[k]);
-      // the reads must land before the DMA below refills that stage
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) qop[G][k] = *(const bf16x8*)(qt + 16 * G * S::RB + a_off[k]);
+      // every wave's reads must land before any wave's DMA below refills
+      // that stage (waves read rows that other waves staged)
       wait_lgkmcnt0();
+      __syncthreads();
     }
     if (e + NS - 1 < e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
-    if (whi < 0) continue;  // no live row in this wave
-    if (full)
-      block(std::true_type(), ring[stg][0], ring[stg][1], kb);
-    else
-      block(std::false_type(), ring[stg][0], ring[stg][1], kb);
-  }
+    if (!(hbits & kPairVisit)) continue;  // the other row block's key block
+    const unsigned char* Kt = ring[stg][0];
+    const unsigned char* Vt = ring[stg][1];
 
-  const float lsum = group4_sum(l_run);
-  if (t < 0) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  bf16* O = (bf16*)a.o + base + (size_t)t * D;
+    // S^T = K Q^T for both groups: each K operand read serves two MFMAs
+    f32x4 sc[2][4];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(acc[d] * inv);
-  if (lg == 0)
-    a.lse[(size_t)bh * a.T + t] = lsum > 0.f ? (m_run * sl2 + fast_log2(lsum)) * kLn2 : -INFINITY;
+    for (int b = 0; b < 4; ++b) {
+      sc[0][b] = sc[1][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        const bf16x8 ka = *(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]);
+        sc[0][b] = mfma_bf16(ka, qop[0][k], sc[0][b]);
+        sc[1][b] = mfma_bf16(ka, qop[1][k], sc[1][b]);
+      }
+    }
+    if (!(hbits & kPairFull)) {
+      // key k0 + 16b + 4lg + i is outside the row's run when
+      // (unsigned)(key - mlo) > mspan
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        const int m0 = k0 + 4 * lg - mlo[G];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((uint32_t)(m0 + 16 * b + i) > mspan[G]) sc[G][b][i] = -INFINITY;
+      }
+    }
+    float lm[2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      lm[G] = fmaxf(fmaxf(sc[G][0][0], sc[G][0][1]), fmaxf(sc[G][0][2], sc[G][0][3]));
+#pragma unroll
+      for (int b = 1; b < 4; ++b)
+        lm[G] = fmaxf(fmaxf(lm[G], fmaxf(sc[G][b][0], sc[G][b][1])), fmaxf(sc[G][b][2], sc[G][b][3]));
+    }
+    if (wave_any(lm[0] > m_run[0] + headroom || lm[1] > m_run[1] + headroom)) {
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        const float mt = group4_max(lm[G]);
+        const bool raise = mt > m_run[G] + headroom;
+        // raising rows scale by exp2((old - new) max), 0 when the old max is
+        // -inf; the others keep their sums (factor exactly 1, never -inf - -inf)
+        const float alpha = raise ? fast_exp2((m_run[G] - mt) * sl2) : 1.f;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) acc[G][d] *= alpha;
+        l_run[G] *= alpha;
+        m_run[G] = raise ? mt : m_run[G];
+      }
+    }
+    bf16x8 pb8[2][2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const float mb = (m_run[G] == -INFINITY) ? 0.f : m_run[G] * sl2;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[G][b][i] = fast_exp2(fmaf(sc[G][b][i], sl2, -mb));
+          l_run[G] += sc[G][b][i];
+        }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) pb8[G][kk] = pack_b_operand(sc[G][2 * kk], sc[G][2 * kk + 1]);
+    }
+    // O^T += V^T P^T for both groups: each V^T operand read serves two MFMAs
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const unsigned char* r = Vt + 32 * kk * S::RB + t_off[d];
+        const bf16x8 av = concat(lds_read_tr((const bf16*)r), lds_read_tr((const bf16*)(r + 16 * S::RB)));
+        acc[0][d] = mfma_bf16(av, pb8[0][kk], acc[0][d]);
+        acc[1][d] = mfma_bf16(av, pb8[1][kk], acc[1][d]);
+      }
+  }
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
+
+#pragma unroll
+  for (int G = 0; G < 2; ++G) {
+    const float lsum = group4_sum(l_run[G]);
+    if (t[G] < 0) continue;
+    // the output is rounded to bf16, so the hardware reciprocal (1 ulp) suffices
+    const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
+    bf16* O = (bf16*)a.o + base + (size_t)t[G] * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(acc[G][d] * inv);
+    if (lg == 0)
+      a.lse[(size_t)bh * a.T + t[G]] = lsum > 0.f ? (m_run[G] * sl2 + fast_log2(lsum)) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace
+
+// One kernel per pattern: the two head kinds' bodies are specialised on their
+// kind codes, and each workgroup branches once, uniformly, on its head's kind.
+template <int D, int NS, int C0, int C1>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
+  const RowItem item = load_uniform(&a.items[blockIdx.x]);
+  if (item.qb < 0) return;  // schedule padding
+  if (C0 == C1 || item.kind == 0)
+    fwd_bf16_body<D, NS, C0>(a, item.qb, item.bh, 0, ring);  // item.qb: pair of row blocks
+  else
+    fwd_bf16_body<D, NS, C1>(a, item.qb, item.bh, 1, ring);
+}
 
 template <typename TE, int D>
 hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   timing_begin(KID_FWD, stream);
-  if constexpr (IsBf16<TE>::value)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdStages>), dim3(n_items), dim3(kThreads), 0, stream, a);
-  else
+  hipError_t err;
+  if constexpr (IsBf16<TE>::value) {
+    err = with_kind_codes(a.pattern, [&](auto c0, auto c1) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_items),
+                         dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    });
+  } else {
     hipLaunchKernelGGL((fwd_kernel<TE, D>), dim3(n_items), dim3(kThreads), 0, stream, a);
-  const hipError_t err = hipGetLastError();
+    err = hipGetLastError();
+  }
   timing_end(KID_FWD, stream);
   return err;
 }

@@ -62,13 +62,24 @@ struct Geometry {
   int n_pad;   // K_STRIDE: class length rounded up to kBlock
   int n_cls;   // K_STRIDE: number of residue classes, min(l, T)
   FastDiv div_l, div_c, div_pad;  // division by l, c (>= 1) and n_pad (>= 1)
+  int blk_c;   // kBlock / c when c divides kBlock (summary blocks per LUT block), else 0
+};
+
+// A Geometry whose kind code is a compile-time constant.  The functions below
+// are templates over the geometry type: called with a GeoC, every branch on the
+// code folds away (the device kernels are instantiated per kind code); called
+// with a plain Geometry, the code is read at run time (host LUT builder).
+template <int KC>
+struct GeoC : Geometry {
+  static constexpr int code = KC;
 };
 
 ST_HD int imin(int a, int b) { return a < b ? a : b; }
 ST_HD int imax(int a, int b) { return a > b ? a : b; }
 
 // Position held by kernel row R, or -1 for padding / out of range.
-ST_HD int row_position(const Geometry& g, int R) {
+template <class G>
+ST_HD int row_position(const G& g, int R) {
   if (R < 0 || R >= g.n_rows) return -1;
   if (g.code == K_STRIDE) {
     const int r = fdiv(R, g.div_pad);
@@ -80,7 +91,8 @@ ST_HD int row_position(const Geometry& g, int R) {
 }
 
 // Position held by kernel key K, or -1 for padding / out of range.
-ST_HD int key_position(const Geometry& g, int K) {
+template <class G>
+ST_HD int key_position(const G& g, int K) {
   if (K < 0 || K >= g.n_keys) return -1;
   if (g.code == K_STRIDE) {
     const int r = fdiv(K, g.div_pad);
@@ -100,11 +112,12 @@ ST_HD int key_position(const Geometry& g, int K) {
 // Position held by row i (0 <= i < kBlock) of 64-block `blk` of the kernel rows
 // (keys == false) or kernel keys (keys == true); -1 for padding.  The branch on
 // the kind is uniform; only the compact summary map divides, by multiply-shift.
-ST_HD int block_position(const Geometry& g, bool keys, int blk, int i) {
+template <class G>
+ST_HD int block_position(const G& g, bool keys, int blk, int i) {
   if (g.code == K_STRIDE) {
-    const int nblk = g.n_pad / kBlock;  // blocks per residue class
-    const int cls = blk / nblk;
-    const int m = (blk - cls * nblk) * kBlock + i;
+    // n_pad is a multiple of kBlock, so a block lies inside one residue class
+    const int cls = fdiv(blk * kBlock, g.div_pad);
+    const int m = blk * kBlock - cls * g.n_pad + i;
     const int p = m * g.l + cls;
     return (cls < g.n_cls && p < g.T) ? p : -1;
   }
@@ -129,29 +142,34 @@ struct RowPart {
 struct BlockPart {
   int base, limit;
 };
-ST_HD bool split_position_ok(const Geometry& g, bool keys) {
+template <class G>
+ST_HD bool split_position_ok(const G& g, bool keys) {
   return !(keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) || (kBlock % g.c) == 0;
 }
-ST_HD RowPart row_part(const Geometry& g, bool keys, int i) {
+template <class G>
+ST_HD RowPart row_part(const G& g, bool keys, int i) {
   if (g.code == K_STRIDE) return {i * g.l};
-  if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1))
-    return {(i / g.c) * g.l + (g.l - g.c) + i % g.c};
+  if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) {
+    const int q = fdiv(i, g.div_c);
+    return {q * g.l + (g.l - g.c) + (i - q * g.c)};
+  }
   return {i};
 }
-ST_HD BlockPart block_part(const Geometry& g, bool keys, int blk) {
+template <class G>
+ST_HD BlockPart block_part(const G& g, bool keys, int blk) {
   if (g.code == K_STRIDE) {
-    const int nblk = g.n_pad / kBlock;
-    const int cls = blk / nblk;
-    const int m0 = (blk - cls * nblk) * kBlock;
+    const int cls = fdiv(blk * kBlock, g.div_pad);
+    const int m0 = blk * kBlock - cls * g.n_pad;
     return {m0 * g.l + cls, cls < g.n_cls ? kBlock : 0};
   }
   if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1))
-    return {blk * (kBlock / g.c) * g.l, g.n_keys - blk * kBlock};
+    return {blk * g.blk_c * g.l, g.n_keys - blk * kBlock};
   return {blk * kBlock, kBlock};
 }
 
 // True when position t of this kind is some kernel key (else nobody attends it).
-ST_HD bool position_is_key(const Geometry& g, int t) {
+template <class G>
+ST_HD bool position_is_key(const G& g, int t) {
   if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
     const int b = fdiv(t, g.div_l);
     const int off = t - b * g.l;
@@ -163,7 +181,8 @@ ST_HD bool position_is_key(const Geometry& g, int t) {
 
 // Run [lo, hi] of kernel keys attended by kernel row R holding position t >= 0.
 // lo > hi means the row attends nothing.
-ST_HD void row_interval(const Geometry& g, int R, int t, int& lo, int& hi) {
+template <class G>
+ST_HD void row_interval(const G& g, int R, int t, int& lo, int& hi) {
   switch (g.code) {
     case K_LOCAL:
       lo = imax(0, t - g.l + 1);

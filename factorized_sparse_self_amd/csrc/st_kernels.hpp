@@ -4,20 +4,43 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "st.h"
 #include "st_device.hpp"
 
 namespace st {
+
+// Calls f(c0, c1) with the kind codes of `pattern`'s two head kinds as
+// std::integral_constant values, so that launchers can pick kernels
+// specialised on them.
+template <class F>
+hipError_t with_kind_codes(int pattern, F&& f) {
+  using std::integral_constant;
+  switch (pattern) {
+    case ST_STRIDED: return f(integral_constant<int, K_LOCAL>(), integral_constant<int, K_STRIDE>());
+    case ST_FIXED: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY>());
+    case ST_FIXED_R1: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY_R1>());
+    default: return f(integral_constant<int, K_CAUSAL>(), integral_constant<int, K_CAUSAL>());
+  }
+}
 
 // Work item of the dK/dV pass: key block kb of head bh, CSC entries [e0, e1).
 // slot >= 0: the key block is split over several items and this one writes
 // fp32 partial sums to workspace slot `slot`; slot < 0: write dk / dv directly.
 struct DkdvItem {
-  int kb, bh, e0, e1, slot, pad0, pad1, pad2;
+  int kb, bh, e0, e1, slot, kind, pad0, pad1;
+};
+
+// Work item of the forward and dq passes: row block qb of head bh, whose
+// head kind (0 or 1) is `kind`.
+struct RowItem {
+  int qb, bh, kind, pad;
 };
 
 // Reduction of a split key block: partial slots [slot0, slot0 + nsplit).
 struct ReduceItem {
-  int kb, bh, slot0, nsplit;
+  int kb, bh, slot0, nsplit, kind, pad0, pad1, pad2;
 };
 
 struct FwdArgs {
@@ -28,8 +51,9 @@ struct FwdArgs {
   float* lse;
   int H, T;
   const KindDev* kinds;  // [2], device memory
-  const int2* items;     // {row block, batch*H + head}
+  const RowItem* items;
   float sl2;             // log2(e) / sqrt(D)
+  int pattern;           // ST_* (host side: selects the kernel)
 };
 
 struct BwdArgs {
@@ -47,11 +71,12 @@ struct BwdArgs {
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
   const KindDev* kinds;
-  const int2* dq_items;
+  const RowItem* dq_items;
   const DkdvItem* dkdv_items;
   const ReduceItem* red_items;
   float sl2;    // log2(e) / sqrt(D)
   float scale;  // 1 / sqrt(D)
+  int pattern;  // ST_* (host side: selects the kernels)
 };
 
 // Kernel ids for the optional launch timing (names in kKernelNames).

@@ -55,6 +55,7 @@ bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g) {
   g->div_l = make_fastdiv((uint32_t)l);
   g->div_c = make_fastdiv(c > 0 ? (uint32_t)c : 1u);
   g->div_pad = make_fastdiv(g->n_pad > 0 ? (uint32_t)g->n_pad : 1u);
+  g->blk_c = (c > 0 && kBlock % c == 0) ? kBlock / c : 0;
   return true;
 }
 

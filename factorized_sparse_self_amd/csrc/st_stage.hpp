@@ -29,10 +29,11 @@ struct TileShape {
   __device__ static __forceinline__ int phys(int r, int c) { return r * RB + ((c ^ (r & (CH - 1))) << 4); }
 };
 
-// LDS byte address of a __shared__ pointer, made wave-uniform.
+// LDS byte address of a __shared__ pointer, made wave-uniform.  A generic
+// pointer into LDS holds the LDS offset in its low 32 bits (the high half is
+// the shared aperture), so no address-space cast (and no null check) is needed.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
-  typedef __attribute__((address_space(3))) const void* lds_ptr;
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr)p);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p);
 }
 
 // One buffer_load ... lds of BYTES (16 or 4) per lane: lane l's bytes land at
@@ -63,28 +64,29 @@ __device__ __forceinline__ void lds_dma(Rsrc r, uint32_t lds_base, uint32_t voff
   }
 }
 
-// Stage this wave's 16 rows (16*wave .. +15) of one 64-row tile of a [T, D]
-// bf16 tensor into `tile` (LDS).  pos[i] is the position held by tile row
-// 16*wave + i*RPI + lane/CH, or -1 for padding.
+// Stage 16 rows of one 64-row tile of a [T, D] bf16 tensor: `rows` is the
+// wave-uniform LDS address of the first of them (a multiple of 16 rows into a
+// tile), pos[i] the position for row i*RPI + lane/CH of the 16, or -1 for
+// padding.  The chunk a lane fetches is the one that its LDS slot holds after
+// the swizzle; the swizzle depends only on the row modulo CH, which the first
+// row's multiple-of-16 offset does not change.
 template <int D>
-__device__ __forceinline__ void stage_rows(Rsrc src, unsigned char* tile, int wave, int lane,
-                                           const int (&pos)[TileShape<D>::NI]) {
+__device__ __forceinline__ void stage_rows(Rsrc src, uint32_t rows, int lane, const int (&pos)[TileShape<D>::NI]) {
   using S = TileShape<D>;
+  const int lc = (lane % S::CH) ^ ((lane / S::CH) & (S::CH - 1));  // logical chunk this lane fetches
 #pragma unroll
   for (int i = 0; i < S::NI; ++i) {
-    const int r = 16 * wave + i * S::RPI + lane / S::CH;
-    const int lc = (lane % S::CH) ^ (r & (S::CH - 1));  // logical chunk this lane fetches
     const uint32_t off = pos[i] >= 0 ? (uint32_t)(pos[i] * S::RB + lc * 16) : kOutOfRange;
-    lds_dma<16>(src, lds_address(tile + (16 * wave + i * S::RPI) * S::RB), off);
+    lds_dma<16>(src, rows + i * S::RPI * S::RB, off);
   }
 }
 
-// Stage one fp32 value per row for this wave's 16 rows into `vals` (LDS):
-// row 16*wave + j lands at vals[64*wave + j]; lanes 16..63 write zeros into
-// the rest of the wave's 256-byte slot.
-__device__ __forceinline__ void stage_row_values(Rsrc src, float* vals, int wave, int lane, int pos) {
+// Stage one fp32 value per row for 16 rows: `vals` is the wave-uniform LDS
+// address of a 64-float slot; lane j < 16 fetches position pos (or zero when
+// pos < 0) into slot word j, lanes 16..63 write zeros into the rest.
+__device__ __forceinline__ void stage_row_values(Rsrc src, uint32_t vals, int lane, int pos) {
   const uint32_t off = (lane < 16 && pos >= 0) ? (uint32_t)pos * 4 : kOutOfRange;
-  lds_dma<4>(src, lds_address(vals + 64 * wave), off);
+  lds_dma<4>(src, vals, off);
 }
 
 // Wait until at most n vector-memory loads of this wave are outstanding
