@@ -7,8 +7,9 @@
 //   dp_tj = dO_t . v_j,        ds_tj = p_tj (dp_tj - Delta_t),
 //   dq_t = sum_j ds_tj k_j / sqrt(D),  dk_j = sum_t ds_tj q_t / sqrt(D),
 //   dv_j = sum_t p_tj dO_t.
-// P and dS enter the dV, dK and dQ products as bf16 hi + lo pairs (about 16
-// significant bits), so those sums are not limited by bf16's 8-bit rounding.
+// In the bf16 kernels P and dS enter the dV, dK and dQ products as bf16 (fp32
+// accumulation); their rounding is well inside the bf16 output tolerance,
+// which the rounding of the stored output O (through Delta) dominates.
 // Kernels (one stream, in order):
 //   pre   Delta for every row; zero dk / dv at positions no query attends
 //         (fp32 only: the bf16 dq kernel does both for its own rows)
@@ -37,43 +38,17 @@ constexpr int kDkdvStages = ST_DKDV_STAGES;
 #endif
 constexpr int kDqStages = ST_DQ_STAGES;
 
-template <typename TE, int D>
-struct BwdLds {
-  static constexpr bool BF = IsBf16<TE>::value;
-  static constexpr int RP = BF ? D + 8 : D + 2;       // row-major pitch
-  static constexpr int TP = kBlock + 8;               // transposed pitch (bf16 only)
-  static constexpr int R_ELEMS = kBlock * RP;
-  static constexpr int T_ELEMS = BF ? D * TP : 1;
-};
-
-// Load rows (2*pr, 2*pr+1), 8-element chunk ch of a bf16 tensor into the
-// row-major copy and (optionally) the transposed copy.
+// fp32 path: tiles staged row-major in LDS (pitch D + 2 floats).
 template <int D>
-__device__ __forceinline__ void stage_pair_bf16(const bf16* __restrict__ src, int p0, int p1, int pr,
-                                                int ch, bf16* rows, bf16* trans) {
-  using L = BwdLds<bf16, D>;
-  uint4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-  if (p0 >= 0) x0 = *(const uint4*)(src + (size_t)p0 * D + ch * 8);
-  if (p1 >= 0) x1 = *(const uint4*)(src + (size_t)p1 * D + ch * 8);
-  *(uint4*)(rows + (2 * pr) * L::RP + ch * 8) = x0;
-  *(uint4*)(rows + (2 * pr + 1) * L::RP + ch * 8) = x1;
-  if (trans) {
-    const uint32_t a[4] = {x0.x, x0.y, x0.z, x0.w};
-    const uint32_t b[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
-      const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
-      *(uint32_t*)(trans + (ch * 8 + 2 * w) * L::TP + 2 * pr) = lo;
-      *(uint32_t*)(trans + (ch * 8 + 2 * w + 1) * L::TP + 2 * pr) = hi;
-    }
-  }
-}
+struct BwdLdsF32 {
+  static constexpr int RP = D + 2;
+  static constexpr int R_ELEMS = kBlock * RP;
+};
 
 template <int D>
 __device__ __forceinline__ void stage_row_f32(const float* __restrict__ src, int p, int r, int ch,
                                               float* rows) {
-  using L = BwdLds<float, D>;
+  using L = BwdLdsF32<D>;
   float4 x = {0.f, 0.f, 0.f, 0.f};
   if (p >= 0) x = *(const float4*)(src + (size_t)p * D + ch * 4);
   float* d = rows + r * L::RP + ch * 4;
@@ -84,9 +59,10 @@ __device__ __forceinline__ void stage_row_f32(const float* __restrict__ src, int
 // ---------------------------------------------------------------------------
 // pre: Delta_t = sum_d dO_t,d O_t,d; zero dk / dv where no query attends.
 // ---------------------------------------------------------------------------
-template <typename TE, int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int VEC = 16 / sizeof(TE);  // elements per 16-byte chunk
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_f32_kernel(BwdArgs a) {
+  using TE = float;
+  constexpr int VEC = 4;                // elements per 16-byte chunk
   constexpr int TPR = D / VEC;          // threads per row (power of two)
   const int64_t row = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / TPR;
   const int ch = threadIdx.x % TPR;
@@ -115,15 +91,14 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dq: per row block; 4 waves x 16 rows; loop over the CSR key blocks.
 // ---------------------------------------------------------------------------
-template <typename TE, int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
-  using L = BwdLds<TE, D>;
-  constexpr bool BF = L::BF;
-  constexpr int NQ = BF ? D / 32 : D / 4;
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a) {
+  using L = BwdLdsF32<D>;
+  using TE = float;
+  constexpr int NQ = D / 4;
   constexpr int ND = D / 16;
-  __shared__ __attribute__((aligned(16))) TE Ks[L::R_ELEMS];
-  __shared__ __attribute__((aligned(16))) TE Vs[L::R_ELEMS];
-  __shared__ __attribute__((aligned(16))) TE Kt[L::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) float Ks[L::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) float Vs[L::R_ELEMS];
 
   const RowItem item = load_uniform(&a.dq_items[blockIdx.x]);
   if (item.qb < 0) return;  // schedule padding
@@ -151,22 +126,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     delta = a.delta[(size_t)bh * a.T + t];
   }
 
-  typedef typename std::conditional<BF, bf16x8, float>::type Op;
-  Op qop[NQ], gop[NQ];
+  float qop[NQ], gop[NQ];
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
-    if constexpr (BF) {
-      uint4 rq = {0, 0, 0, 0}, rg = {0, 0, 0, 0};
-      if (t >= 0) {
-        rq = *(const uint4*)(Qg + (size_t)t * D + 32 * s + 8 * lg);
-        rg = *(const uint4*)(Gg + (size_t)t * D + 32 * s + 8 * lg);
-      }
-      qop[s] = __builtin_bit_cast(bf16x8, rq);
-      gop[s] = __builtin_bit_cast(bf16x8, rg);
-    } else {
-      qop[s] = (t >= 0) ? (float)Qg[(size_t)t * D + 4 * s + lg] : 0.f;
-      gop[s] = (t >= 0) ? (float)Gg[(size_t)t * D + 4 * s + lg] : 0.f;
-    }
+    qop[s] = (t >= 0) ? Qg[(size_t)t * D + 4 * s + lg] : 0.f;
+    gop[s] = (t >= 0) ? Gg[(size_t)t * D + 4 * s + lg] : 0.f;
   }
   f32x4 acc[ND];
 #pragma unroll
@@ -178,23 +142,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     const int kb = kd.col_idx[e];
     const bool full = kd.flags[e] != 0;
     __syncthreads();
-    if constexpr (BF) {
-      constexpr int CH = D / 8;
-      for (int u = tid; u < (kBlock / 2) * CH; u += kThreads) {
-        const int pr = u / CH, ch = u - pr * CH;
-        const int p0 = key_position(g, kb * kBlock + 2 * pr);
-        const int p1 = key_position(g, kb * kBlock + 2 * pr + 1);
-        stage_pair_bf16<D>(Kg, p0, p1, pr, ch, Ks, Kt);
-        stage_pair_bf16<D>(Vg, p0, p1, pr, ch, Vs, nullptr);
-      }
-    } else {
-      constexpr int CH = D / 4;
-      for (int u = tid; u < kBlock * CH; u += kThreads) {
-        const int r = u / CH, ch = u - r * CH;
-        const int p = key_position(g, kb * kBlock + r);
-        stage_row_f32<D>((const float*)Kg, p, r, ch, (float*)Ks);
-        stage_row_f32<D>((const float*)Vg, p, r, ch, (float*)Vs);
-      }
+    constexpr int CH = D / 4;
+    for (int u = tid; u < kBlock * CH; u += kThreads) {
+      const int r = u / CH, ch = u - r * CH;
+      const int p = key_position(g, kb * kBlock + r);
+      stage_row_f32<D>(Kg, p, r, ch, Ks);
+      stage_row_f32<D>(Vg, p, r, ch, Vs);
     }
     __syncthreads();
     if (!wave_active) continue;
@@ -213,17 +166,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
       if (!need[b]) continue;
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        if constexpr (BF) {
-          const bf16x8 ak = *(const bf16x8*)(Ks + (16 * b + li) * L::RP + 32 * k + 8 * lg);
-          const bf16x8 av = *(const bf16x8*)(Vs + (16 * b + li) * L::RP + 32 * k + 8 * lg);
-          s[b] = mfma_bf16(ak, qop[k], s[b]);
-          dp[b] = mfma_bf16(av, gop[k], dp[b]);
-        } else {
-          const float ak = ((const float*)Ks)[(16 * b + li) * L::RP + 4 * k + lg];
-          const float av = ((const float*)Vs)[(16 * b + li) * L::RP + 4 * k + lg];
-          s[b] = mfma_f32(ak, qop[k], s[b]);
-          dp[b] = mfma_f32(av, gop[k], dp[b]);
-        }
+        s[b] = mfma_f32(Ks[(16 * b + li) * L::RP + 4 * k + lg], qop[k], s[b]);
+        dp[b] = mfma_f32(Vs[(16 * b + li) * L::RP + 4 * k + lg], gop[k], dp[b]);
       }
     }
     // ds = p * (dp - Delta), p rebuilt from lse; zero outside the row's run
@@ -237,32 +181,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
         s[b][i] = p * (dp[b][i] - delta);
       }
     // dq^T += K^T ds^T
-    if constexpr (BF) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-        bf16x8 bs_hi, bs_lo;
-        split_b_operand(s[2 * kk], s[2 * kk + 1], bs_hi, bs_lo);
+    for (int b = 0; b < 4; ++b) {
+      if (!need[b]) continue;
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const bf16* row = Kt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
-          const bf16x8 ak = concat(*(const bf16x4*)row, *(const bf16x4*)(row + 16));
-          acc[d] = mfma_bf16(ak, bs_hi, acc[d]);
-          acc[d] = mfma_bf16(ak, bs_lo, acc[d]);
-        }
-      }
-    } else {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (!need[b]) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const float ak = ((const float*)Ks)[(16 * b + 4 * lg + i) * L::RP + 16 * d + li];
-            acc[d] = mfma_f32(ak, s[b][i], acc[d]);
-          }
-      }
+        for (int d = 0; d < ND; ++d)
+          acc[d] = mfma_f32(Ks[(16 * b + 4 * lg + i) * L::RP + 16 * d + li], s[b][i], acc[d]);
     }
   }
   if (t < 0) return;
@@ -270,27 +196,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
     const f32x4 o = acc[d] * a.scale;
-    if constexpr (BF) {
-      *(bf16x4*)(dq + 16 * d + 4 * lg) = to_bf16x4(o);
-    } else {
-      *(float4*)(dq + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-    }
+    *(float4*)(dq + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dkdv: per key block (or a split of its row blocks); 4 waves x 16 keys.
 // ---------------------------------------------------------------------------
-template <typename TE, int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
-  using L = BwdLds<TE, D>;
-  constexpr bool BF = L::BF;
-  constexpr int NQ = BF ? D / 32 : D / 4;
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
+  using L = BwdLdsF32<D>;
+  using TE = float;
+  constexpr int NQ = D / 4;
   constexpr int ND = D / 16;
-  __shared__ __attribute__((aligned(16))) TE Qs[L::R_ELEMS];
-  __shared__ __attribute__((aligned(16))) TE Gs[L::R_ELEMS];
-  __shared__ __attribute__((aligned(16))) TE Qt[L::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) TE Gt[L::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) float Qs[L::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) float Gs[L::R_ELEMS];
   __shared__ __attribute__((aligned(16))) float lse2s[kBlock];
   __shared__ __attribute__((aligned(16))) float dels[kBlock];
   __shared__ __attribute__((aligned(16))) int los[kBlock];
@@ -313,22 +233,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int Kl = Kw0 + li;                  // this lane's key
   const int kp = key_position(g, Kl);
 
-  typedef typename std::conditional<BF, bf16x8, float>::type Op;
-  Op kop[NQ], vop[NQ];
+  float kop[NQ], vop[NQ];
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
-    if constexpr (BF) {
-      uint4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
-      if (kp >= 0) {
-        rk = *(const uint4*)(Kg + (size_t)kp * D + 32 * s + 8 * lg);
-        rv = *(const uint4*)(Vg + (size_t)kp * D + 32 * s + 8 * lg);
-      }
-      kop[s] = __builtin_bit_cast(bf16x8, rk);
-      vop[s] = __builtin_bit_cast(bf16x8, rv);
-    } else {
-      kop[s] = (kp >= 0) ? (float)Kg[(size_t)kp * D + 4 * s + lg] : 0.f;
-      vop[s] = (kp >= 0) ? (float)Vg[(size_t)kp * D + 4 * s + lg] : 0.f;
-    }
+    kop[s] = (kp >= 0) ? Kg[(size_t)kp * D + 4 * s + lg] : 0.f;
+    vop[s] = (kp >= 0) ? Vg[(size_t)kp * D + 4 * s + lg] : 0.f;
   }
   f32x4 dk[ND], dv[ND];
 #pragma unroll
@@ -342,23 +251,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     const int qb = kd.row_idx[e];
     const bool full = kd.csc_flags[e] != 0;
     __syncthreads();
-    if constexpr (BF) {
-      constexpr int CH = D / 8;
-      for (int u = tid; u < (kBlock / 2) * CH; u += kThreads) {
-        const int pr = u / CH, ch = u - pr * CH;
-        const int p0 = row_position(g, qb * kBlock + 2 * pr);
-        const int p1 = row_position(g, qb * kBlock + 2 * pr + 1);
-        stage_pair_bf16<D>(Qg, p0, p1, pr, ch, Qs, Qt);
-        stage_pair_bf16<D>(Gg, p0, p1, pr, ch, Gs, Gt);
-      }
-    } else {
-      constexpr int CH = D / 4;
-      for (int u = tid; u < kBlock * CH; u += kThreads) {
-        const int r = u / CH, ch = u - r * CH;
-        const int p = row_position(g, qb * kBlock + r);
-        stage_row_f32<D>((const float*)Qg, p, r, ch, (float*)Qs);
-        stage_row_f32<D>((const float*)Gg, p, r, ch, (float*)Gs);
-      }
+    constexpr int CH = D / 4;
+    for (int u = tid; u < kBlock * CH; u += kThreads) {
+      const int r = u / CH, ch = u - r * CH;
+      const int p = row_position(g, qb * kBlock + r);
+      stage_row_f32<D>(Qg, p, r, ch, Qs);
+      stage_row_f32<D>(Gg, p, r, ch, Gs);
     }
     if (tid < kBlock) {
       const int R = qb * kBlock + tid;
@@ -396,17 +294,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
       if (!need[b]) continue;
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        if constexpr (BF) {
-          const bf16x8 aq = *(const bf16x8*)(Qs + (16 * b + li) * L::RP + 32 * k + 8 * lg);
-          const bf16x8 ag = *(const bf16x8*)(Gs + (16 * b + li) * L::RP + 32 * k + 8 * lg);
-          s[b] = mfma_bf16(aq, kop[k], s[b]);
-          dp[b] = mfma_bf16(ag, vop[k], dp[b]);
-        } else {
-          const float aq = ((const float*)Qs)[(16 * b + li) * L::RP + 4 * k + lg];
-          const float ag = ((const float*)Gs)[(16 * b + li) * L::RP + 4 * k + lg];
-          s[b] = mfma_f32(aq, kop[k], s[b]);
-          dp[b] = mfma_f32(ag, vop[k], dp[b]);
-        }
+        s[b] = mfma_f32(Qs[(16 * b + li) * L::RP + 4 * k + lg], kop[k], s[b]);
+        dp[b] = mfma_f32(Gs[(16 * b + li) * L::RP + 4 * k + lg], vop[k], dp[b]);
       }
     }
     // p and ds for each (row 16b + 4lg + i, key Kl)
@@ -430,38 +319,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS
-    if constexpr (BF) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (!need[2 * kk] && !need[2 * kk + 1]) continue;
-        bf16x8 bp_hi, bp_lo, bd_hi, bd_lo;
-        split_b_operand(s[2 * kk], s[2 * kk + 1], bp_hi, bp_lo);
-        split_b_operand(dp[2 * kk], dp[2 * kk + 1], bd_hi, bd_lo);
+    for (int b = 0; b < 4; ++b) {
+      if (!need[b]) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const bf16* rg = Gt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
-          const bf16* rq = Qt + (16 * d + li) * L::TP + 32 * kk + 4 * lg;
-          const bf16x8 ag = concat(*(const bf16x4*)rg, *(const bf16x4*)(rg + 16));
-          const bf16x8 aq = concat(*(const bf16x4*)rq, *(const bf16x4*)(rq + 16));
-          dv[d] = mfma_bf16(ag, bp_hi, dv[d]);
-          dv[d] = mfma_bf16(ag, bp_lo, dv[d]);
-          dk[d] = mfma_bf16(aq, bd_hi, dk[d]);
-          dk[d] = mfma_bf16(aq, bd_lo, dk[d]);
+          const int off = (16 * b + 4 * lg + i) * L::RP + 16 * d + li;
+          dv[d] = mfma_f32(Gs[off], s[b][i], dv[d]);
+          dk[d] = mfma_f32(Qs[off], dp[b][i], dk[d]);
         }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (!need[b]) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const int off = (16 * b + 4 * lg + i) * L::RP + 16 * d + li;
-            dv[d] = mfma_f32(((const float*)Gs)[off], s[b][i], dv[d]);
-            dk[d] = mfma_f32(((const float*)Qs)[off], dp[b][i], dk[d]);
-          }
-      }
     }
   }
 
@@ -472,13 +340,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       const f32x4 x = dk[d] * a.scale;
-      if constexpr (BF) {
-        *(bf16x4*)(dkp + 16 * d + 4 * lg) = to_bf16x4(x);
-        *(bf16x4*)(dvp + 16 * d + 4 * lg) = to_bf16x4(dv[d]);
-      } else {
-        *(float4*)(dkp + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
-        *(float4*)(dvp + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
-      }
+      *(float4*)(dkp + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
+      *(float4*)(dvp + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
     }
   } else {
     float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
@@ -630,17 +493,15 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[b][i] *= dp[b][i] - delta;
-    // dQ^T += K^T dS^T, dS as a bf16 hi + lo pair
+    // dQ^T += K^T dS^T
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 hi8, lo8;
-      split_b_operand(sc[2 * kk], sc[2 * kk + 1], hi8, lo8);
+      const bf16x8 ds8 = pack_b_operand(sc[2 * kk], sc[2 * kk + 1]);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const unsigned char* r = Kt + 32 * kk * S::RB + t_off[d];
         const bf16x8 ak = concat(lds_read_tr((const bf16*)r), lds_read_tr((const bf16*)(r + 16 * S::RB)));
-        acc[d] = mfma_bf16(ak, hi8, acc[d]);
-        acc[d] = mfma_bf16(ak, lo8, acc[d]);
+        acc[d] = mfma_bf16(ak, ds8, acc[d]);
       }
     }
   }
@@ -812,19 +673,16 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 p_hi, p_lo, d_hi, d_lo;
-      split_b_operand(sc[2 * kk], sc[2 * kk + 1], p_hi, p_lo);
-      split_b_operand(dp[2 * kk], dp[2 * kk + 1], d_hi, d_lo);
+      const bf16x8 p8 = pack_b_operand(sc[2 * kk], sc[2 * kk + 1]);
+      const bf16x8 ds8 = pack_b_operand(dp[2 * kk], dp[2 * kk + 1]);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
         const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
         const bf16x8 ag = concat(lds_read_tr((const bf16*)rg0), lds_read_tr((const bf16*)(rg0 + 16 * S::RB)));
         const bf16x8 aq = concat(lds_read_tr((const bf16*)rq0), lds_read_tr((const bf16*)(rq0 + 16 * S::RB)));
-        dv[d] = mfma_bf16(ag, p_hi, dv[d]);
-        dv[d] = mfma_bf16(ag, p_lo, dv[d]);
-        dk[d] = mfma_bf16(aq, d_hi, dk[d]);
-        dk[d] = mfma_bf16(aq, d_lo, dk[d]);
+        dv[d] = mfma_bf16(ag, p8, dv[d]);
+        dk[d] = mfma_bf16(aq, ds8, dk[d]);
       }
     }
   }
@@ -911,7 +769,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   // before dk/dv, which reads Delta
   if constexpr (!IsBf16<TE>::value) {
     timing_begin(KID_PRE, stream);
-    hipLaunchKernelGGL((bwd_pre_kernel<TE, D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
     timing_end(KID_PRE, stream);
     if (err != hipSuccess) return err;
@@ -925,7 +783,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
         return hipGetLastError();
       });
     } else {
-      hipLaunchKernelGGL((bwd_dq_kernel<TE, D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), dim3(n_dq), dim3(kThreads), 0, stream, a);
       err = hipGetLastError();
     }
     timing_end(KID_DQ, stream);
@@ -940,7 +798,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
         return hipGetLastError();
       });
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<TE, D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), dim3(n_dkdv), dim3(kThreads), 0, stream, a);
       err = hipGetLastError();
     }
     timing_end(KID_DKDV, stream);

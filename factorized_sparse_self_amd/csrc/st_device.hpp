@@ -65,31 +65,6 @@ __device__ __forceinline__ bf16x8 pack_b_operand(const f32x4& a, const f32x4& b)
   return (bf16x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
-// The same eight values as a bf16 pair x = hi + lo: hi is x truncated to bf16
-// and lo is the rounded remainder, so a product summed over both halves keeps
-// about 16 significant bits of x instead of bf16's 8.
-__device__ __forceinline__ void split_b_operand(const f32x4& a, const f32x4& b, bf16x8& hi,
-                                                bf16x8& lo) {
-  uint32_t hw[4];
-  f32x4 ra, rb;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t a0 = __builtin_bit_cast(uint32_t, a[2 * i]);
-    const uint32_t a1 = __builtin_bit_cast(uint32_t, a[2 * i + 1]);
-    const uint32_t b0 = __builtin_bit_cast(uint32_t, b[2 * i]);
-    const uint32_t b1 = __builtin_bit_cast(uint32_t, b[2 * i + 1]);
-    hw[i] = (a0 >> 16) | (a1 & 0xffff0000u);
-    hw[2 + i] = (b0 >> 16) | (b1 & 0xffff0000u);
-    ra[2 * i] = a[2 * i] - __builtin_bit_cast(float, a0 & 0xffff0000u);
-    ra[2 * i + 1] = a[2 * i + 1] - __builtin_bit_cast(float, a1 & 0xffff0000u);
-    rb[2 * i] = b[2 * i] - __builtin_bit_cast(float, b0 & 0xffff0000u);
-    rb[2 * i + 1] = b[2 * i + 1] - __builtin_bit_cast(float, b1 & 0xffff0000u);
-  }
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  hi = __builtin_bit_cast(bf16x8, (u32x4){hw[0], hw[1], hw[2], hw[3]});
-  lo = pack_b_operand(ra, rb);
-}
-
 __device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
   return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
