@@ -41,28 +41,29 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // wait-count insertion cannot tell the ring stages apart and would make every
 // LDS read wait for all DMA loads in flight, which serialises the ring; the
 // kernels order these loads with their own s_waitcnt vmcnt + barrier instead.
-// M0 carries the LDS base; it is saved and restored, and one wait state
-// separates the M0 write from the load that reads it.
+// M0 carries the LDS base, and one wait state separates the M0 write from the
+// load that reads it.  M0 is clobbered without being restored: nothing else in
+// these kernels uses it (the compiler only would for LDS DMA builtins, GWS or
+// message instructions, which they do not contain; a codegen test checks that
+// M0 appears only inside these asm blocks).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(Rsrc r, uint32_t lds_base, uint32_t voff) {
-  uint32_t saved;
   if constexpr (BYTES == 16) {
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_base), "v"(voff), "s"(r)
-        : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(r)
+                 : "memory", "m0");
   } else {
     static_assert(BYTES == 4, "16- or 4-byte DMA");
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_base), "v"(voff), "s"(r)
-        : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(r)
+                 : "memory", "m0");
   }
 }
+#pragma clang diagnostic pop
 
 // Stage 16 rows of one 64-row tile of a [T, D] bf16 tensor: `rows` is the
 // wave-uniform LDS address of the first of them (a multiple of 16 rows into a
