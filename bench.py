@@ -12,7 +12,8 @@ workload is the fixed pattern at T = 12288 with forward + recompute backward
 Output: one JSON line.  ``value`` is useful TFLOP/s: 14*D*nnz FLOP per step
 (forward 4*D*nnz: QK^T and PV; backward 10*D*nnz: S recomputed, dP, dV, dQ,
 dK) over the step time, nnz = sum over heads of |S(t)|; masked or skipped
-work is never counted.  The step time is taken over ``--steps`` steps
+work is never counted (``executed_tflops`` counts every pair of the visited
+64x64 LUT blocks instead, and is labelled as such).  The step time is taken over ``--steps`` steps
 between two HIP events on the launch stream.  ``roofline`` describes the
 kernel with the largest time per step: its duration comes from HIP events
 that the library records around each kernel launch on the same stream, in a
@@ -101,7 +102,11 @@ def accounting(w):
     fl = {"fwd": 4 * w.D * pairs_total, "bwd_pre": 0, "bwd_dq": 6 * w.D * pairs_total,
           "bwd_dkdv": 8 * w.D * pairs_total, "bwd_reduce": 0}
     useful = (4 if not w.backward else 14) * w.D * pairs_total
-    return {"bytes": by, "flops": fl, "useful_flops": useful, "pairs": pairs_total,
+    # executed: every pair of every visited 64x64 LUT block (masked ones included)
+    blk = lay[0]["block"] ** 2
+    visited = sum(w.B * lay[h % 2]["nnz"] * blk for h in range(w.H))
+    executed = (4 if not w.backward else 14) * w.D * visited
+    return {"bytes": by, "flops": fl, "useful_flops": useful, "executed_flops": executed, "pairs": pairs_total,
             "pairs_per_kind": [lay[0]["pairs"], lay[1]["pairs"]]}
 
 
@@ -109,8 +114,20 @@ def accounting(w):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
+# Slices whose oracle time is estimated above ORACLE_SLICE_S seconds are timed
+# on a subset of their rows instead.
+ORACLE_SLICE_S = 20.0
+
+
+def _one_thread():
+    """Pool initializer: one BLAS / OpenMP thread per oracle process (set before
+    numpy is imported in the worker), so that `cores` is the thread count."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
 def _oracle_unit(args):
-    wname, b, h0 = args
+    wname, b, h0, rows = args
     import torch
     import oracle
     from factorized_sparse_self_amd import inputs
@@ -118,7 +135,12 @@ def _oracle_unit(args):
     tensors = inputs.draw_workload(w)
     arrs = [x[b:b + 1, h0:h0 + 2].to(torch.float64).numpy() for x in tensors]
     t0 = time.perf_counter()
-    if w.backward:
+    if rows is not None:
+        # row sample: the forward and the dq part of the backward at these rows
+        oracle.forward_rows(arrs[0], arrs[1], arrs[2], w.pattern, w.l, w.c, rows)
+        if w.backward:
+            oracle.backward_dq_rows(arrs[0], arrs[1], arrs[2], arrs[3], w.pattern, w.l, w.c, rows)
+    elif w.backward:
         oracle.backward(arrs[0], arrs[1], arrs[2], arrs[3], w.pattern, w.l, w.c)
     else:
         oracle.forward(arrs[0], arrs[1], arrs[2], w.pattern, w.l, w.c)
@@ -126,28 +148,53 @@ def _oracle_unit(args):
 
 
 def cpu_baseline(w, acct, units):
-    """Time the oracle on `units` (batch, head-pair) slices, one worker process each."""
-    from factorized_sparse_self_amd import inputs  # noqa: F401
+    """Time the oracle on `units` (batch, head-pair) slices, one worker process each.
+
+    A slice is the full sequence of two heads (one of each kind), forward and
+    (if the workload has one) backward.  When a slice would take more than
+    about ORACLE_SLICE_S seconds, each worker times the forward and the dq part
+    of the backward on an evenly spaced subset of the rows instead, and only
+    the FLOP of those rows is counted.
+    """
+    import numpy as np
+    import oracle
     pairs = acct["pairs_per_kind"]
-    jobs = []
-    for b in range(w.B):
-        for h0 in range(0, w.H - 1, 2):
-            jobs.append((w.name, b, h0))
-    jobs = jobs[:units]
-    ctx = mp.get_context("spawn")
-    t0 = time.perf_counter()
-    with ctx.Pool(len(jobs)) as pool:
-        per_unit = pool.map(_oracle_unit, jobs)
-    wall = time.perf_counter() - t0
     flop_per_pair = (14 if w.backward else 4) * w.D
-    flops = len(jobs) * (pairs[0] + pairs[1]) * flop_per_pair
+    slice_flops = (pairs[0] + pairs[1]) * flop_per_pair
+    rows = None
+    slices = [(b, h0) for b in range(w.B) for h0 in range(0, w.H - 1, 2)][:units]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(len(slices), initializer=_one_thread) as pool:
+        # pilot: the forward (+ dq part of the backward) on 16 evenly spaced rows of
+        # every slice at once (the processes slow each other down), the slowest
+        # scaled to a whole slice (the full backward adds the dk/dv part: x 1.4)
+        pilot = np.unique(np.linspace(0, w.T - 1, 16).astype(np.int64))
+        per_row = max(pool.map(_oracle_unit, [(w.name, b, h0, pilot) for b, h0 in slices])) / len(pilot)
+        estimate = per_row * w.T * (1.4 if w.backward else 1.0)
+        print(f"cpu baseline: oracle slice estimated at {estimate:.1f} s", file=sys.stderr, flush=True)
+        if estimate > ORACLE_SLICE_S:
+            n = max(16, int(ORACLE_SLICE_S / 2 / per_row))
+            rows = np.unique(np.linspace(0, w.T - 1, n).astype(np.int64))
+            row_pairs = sum(oracle.key_set(w.pattern, kind, int(t), w.T, w.l, w.c).size
+                            for kind in (0, 1) for t in rows)
+            slice_flops = row_pairs * (10 if w.backward else 4) * w.D
+        jobs = [(w.name, b, h0, rows) for b, h0 in slices]
+        print(f"cpu baseline: timing {len(jobs)} slices" + ("" if rows is None else f" on {len(rows)} rows"),
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        per_unit = pool.map(_oracle_unit, jobs)
+        wall = time.perf_counter() - t0
+    flops = len(jobs) * slice_flops
     busy = max(per_unit)
+    what = ("full T={}, {}".format(w.T, "forward + backward" if w.backward else "forward") if rows is None else
+            "{} evenly spaced rows of T={}, forward{} at those rows".format(
+                len(rows), w.T, " + the dq part of the backward" if w.backward else ""))
     return {
         "value": flops / busy / 1e12, "unit": "TFLOP/s", "cores": len(jobs), "kind": "oracle",
         "sample": (f"{len(jobs)} of {w.B * (w.H // 2)} (batch, head-pair) slices of {w.name}: "
-                   f"batch {jobs[0][1]}, heads {jobs[0][2]}-{jobs[-1][2] + 1}, full T={w.T}, "
-                   f"{'forward + backward' if w.backward else 'forward'}, fp64 numpy, one process "
-                   f"per slice; value = sampled useful FLOP / slowest slice time"),
+                   f"batch {jobs[0][1]}, heads {jobs[0][2]}-{jobs[-1][2] + 1}, {what}, fp64 numpy, "
+                   f"one single-threaded process per slice; value = sampled useful FLOP / slowest "
+                   f"slice time"),
         "seconds_per_slice": [round(x, 3) for x in per_unit], "wall_s": round(wall, 3),
         "cpu_model": _cpu_model(),
     }
@@ -283,6 +330,7 @@ def main():
                              "ms_per_step": tot / args.steps}
 
     useful_tflops = acct["useful_flops"] / (ms_per_step * 1e-3) / 1e12
+    executed_tflops = acct["executed_flops"] / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = w.B * w.T / (ms_per_step * 1e-3)
     dom = max(kernels, key=lambda k_: kernels[k_]["ms_per_step"])
     dur_s = kernels[dom]["avg_ms"] * 1e-3
@@ -323,6 +371,8 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_bf16_mfma_peak": round(100 * useful_tflops / MI355X_BF16_TFLOPS, 3),
         "useful_gflop_per_step": round(acct["useful_flops"] / 1e9, 3),
+        "executed_tflops": round(executed_tflops, 3),
+        "executed_gflop_per_step": round(acct["executed_flops"] / 1e9, 3),
         "nnz_pairs": acct["pairs"],
         "kernels": {k_: {kk: round(vv, 5) for kk, vv in v_.items()} for k_, v_ in kernels.items()},
         "layout_build_ms": round(layout_ms, 3),

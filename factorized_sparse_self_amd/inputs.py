@@ -58,7 +58,16 @@ WORKLOADS = [
     Workload("strided_T65536_bf16_fwdbwd", STRIDED, 1, 8, 65536, 64, 256, 0, "bf16", True, 1004,
              note="audio-length sequence, 4 local + 4 strided heads"),
 ]
-WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS}
+# Follow-up workloads at the fixed workload's shape: full causal attention (the
+# comparator of the pages' fixed-vs-full training-step timing) and the summary
+# variant whose summary keys include the query's own block up to t.
+EXTRA_WORKLOADS = [
+    Workload("dense_T12288_bf16_fwdbwd", DENSE, 4, 8, 12288, 64, 128, 0, "bf16", True, 1005,
+             note="full causal attention at the fixed workload's shape"),
+    Workload("fixed_r1_T12288_bf16_fwdbwd", FIXED_R1, 4, 8, 12288, 64, 128, 8, "bf16", True, 1006,
+             note="summary keys of earlier blocks and of the own block up to t"),
+]
+WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def draw(B: int, H: int, T: int, D: int, *, dtype: torch.dtype, seed: int,

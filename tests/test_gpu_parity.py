@@ -186,11 +186,13 @@ def test_autograd_wrapper_matches_entry_points():
 # ---------------------------------------------------------------------------
 
 def sample_rows(T, l, n, seed):
+    """About n query rows: the special rows (block and tile edges, the last rows) and
+    seeded random ones."""
     rng = np.random.default_rng(seed)
-    special = {0, 1, l - 1, l, l + 1, T - 1, T - 2, T - l, 63, 64, 65}
-    rows = set(int(x) for x in rng.choice(T, size=min(n, T), replace=False))
-    rows |= {s for s in special if 0 <= s < T}
-    return np.array(sorted(rows)[:max(n, len(special))], dtype=np.int64)
+    special = {s for s in (0, 1, l - 1, l, l + 1, T - 1, T - 2, T - l, 63, 64, 65) if 0 <= s < T}
+    rest = [int(x) for x in rng.choice(T, size=min(n, T), replace=False) if int(x) not in special]
+    rows = special | set(rest[:max(0, n - len(special))])
+    return np.array(sorted(rows), dtype=np.int64)
 
 
 @pytest.mark.parametrize("w", inputs.WORKLOADS[:2], ids=lambda w: w.name)
@@ -217,15 +219,23 @@ def test_workload_strided_12288_forward_sampled():
 
 def _keys_for_head(w, kind, n, seed):
     rng = np.random.default_rng(seed + kind)
-    if w.pattern == inputs.FIXED and kind == 1:
+    if w.pattern in (inputs.FIXED, inputs.FIXED_R1) and kind == 1:
         nb = -(-w.T // w.l)
         blocks = sorted({0, 1, nb // 2, nb - 2} | set(int(b) for b in rng.integers(0, nb - 1, size=2)))
         return np.array([b * w.l + w.l - w.c + int(rng.integers(0, w.c)) for b in blocks], dtype=np.int64)
+    if w.pattern == inputs.DENSE:
+        # every later query attends key j, and the oracle recomputes each of them in
+        # full, so the dense keys come from the last 512 positions (up to 512
+        # attending queries each)
+        tail = max(0, w.T - 512)
+        keys = set(int(x) for x in rng.choice(np.arange(tail, w.T), size=min(3, w.T - tail),
+                                              replace=False)) | {w.T - 1, w.T - 64, w.T - 65, tail}
+        return np.array(sorted(keys), dtype=np.int64)
     keys = set(int(x) for x in rng.choice(w.T, size=n, replace=False)) | {0, w.T - 1, w.l}
     return np.array(sorted(keys), dtype=np.int64)
 
 
-@pytest.mark.parametrize("w", inputs.WORKLOADS[3:], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", inputs.WORKLOADS[3:] + inputs.EXTRA_WORKLOADS, ids=lambda w: w.name)
 def test_workload_forward_backward_sampled(w):
     log(f"workload {w.name}: forward + backward at full size")
     q, k, v, do = inputs.draw_workload(w, n=4)
@@ -233,7 +243,8 @@ def test_workload_forward_backward_sampled(w):
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, w.pattern, w.l, w.c)
     for x in (out, dq, dk, dv):
         assert torch.isfinite(x).all()
-    rows = sample_rows(w.T, w.l, 512, w.seed)
+    # dense rows are long (up to T keys each), so fewer of them
+    rows = sample_rows(w.T, w.l, 128 if w.pattern == inputs.DENSE else 512, w.seed)
     # batch 0 only for the oracle (batches are independent)
     qn, kn, vn, don = (f64(x[:1]) for x in (q, k, v, do))
     log(f"  oracle rows: {len(rows)} per head")
@@ -242,15 +253,20 @@ def test_workload_forward_backward_sampled(w):
     assert_close(f64(lse[:1])[:, :, rows], L, "f32", "lse")
     rq = oracle.backward_dq_rows(qn, kn, vn, don, w.pattern, w.l, w.c, rows)
     assert_close(f64(dq[:1])[:, :, rows], rq, w.dtype, "dq")
-    for h in range(w.H):
+    # dense: every head has the same key sets and a key's queries are many, so two heads
+    for h in range(2 if w.pattern == inputs.DENSE else w.H):
         kind = h % 2
         keys = _keys_for_head(w, kind, 24, w.seed + h)
         log(f"  oracle keys head {h}: {len(keys)}")
         rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, w.pattern, w.l, w.c, keys, heads=[h])
         assert_close(f64(dk[:1])[:, h, keys], rk[:, h], w.dtype, f"dk head {h}")
         assert_close(f64(dv[:1])[:, h, keys], rv[:, h], w.dtype, f"dv head {h}")
-    if w.pattern == inputs.FIXED:
+    if w.pattern in (inputs.FIXED, inputs.FIXED_R1):
+        # summary heads: non-summary positions are never attended; under FIXED the
+        # last block's summary positions are not either (no later block)
         pos = torch.arange(w.T)
-        never = ((pos % w.l) < w.l - w.c) | (pos >= (w.T // w.l - 1) * w.l)
+        never = (pos % w.l) < w.l - w.c
+        if w.pattern == inputs.FIXED:
+            never |= pos >= (w.T // w.l - 1) * w.l
         dkc, dvc = dk.cpu(), dv.cpu()
         assert (dkc[:, 1::2][:, :, never] == 0).all() and (dvc[:, 1::2][:, :, never] == 0).all()
