@@ -58,14 +58,17 @@ WORKLOADS = [
     Workload("strided_T65536_bf16_fwdbwd", STRIDED, 1, 8, 65536, 64, 256, 0, "bf16", True, 1004,
              note="audio-length sequence, 4 local + 4 strided heads"),
 ]
-# Follow-up workloads at the fixed workload's shape: full causal attention (the
-# comparator of the pages' fixed-vs-full training-step timing) and the summary
-# variant whose summary keys include the query's own block up to t.
+# Follow-up workloads: full causal attention at the fixed workload's shape (the
+# comparator of the pages' fixed-vs-full training-step timing), the summary
+# variant whose summary keys include the query's own block up to t, and a
+# million-length strided sequence.
 EXTRA_WORKLOADS = [
     Workload("dense_T12288_bf16_fwdbwd", DENSE, 4, 8, 12288, 64, 128, 0, "bf16", True, 1005,
              note="full causal attention at the fixed workload's shape"),
     Workload("fixed_r1_T12288_bf16_fwdbwd", FIXED_R1, 4, 8, 12288, 64, 128, 8, "bf16", True, 1006,
              note="summary keys of earlier blocks and of the own block up to t"),
+    Workload("strided_T1048576_bf16_fwdbwd", STRIDED, 1, 2, 1 << 20, 64, 1024, 0, "bf16", True, 1007,
+             note="million-length sequence, one local and one strided head"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

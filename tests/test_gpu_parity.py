@@ -256,7 +256,8 @@ def test_workload_forward_backward_sampled(w):
     # dense: every head has the same key sets and a key's queries are many, so two heads
     for h in range(2 if w.pattern == inputs.DENSE else w.H):
         kind = h % 2
-        keys = _keys_for_head(w, kind, 24, w.seed + h)
+        # long rows (l >= 1024): every attending query is recomputed, so fewer keys
+        keys = _keys_for_head(w, kind, 8 if w.l >= 1024 else 24, w.seed + h)
         log(f"  oracle keys head {h}: {len(keys)}")
         rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, w.pattern, w.l, w.c, keys, heads=[h])
         assert_close(f64(dk[:1])[:, h, keys], rk[:, h], w.dtype, f"dk head {h}")
