@@ -10,7 +10,8 @@ implementation).  The library does this in its own coordinate system, where
 each head kind's rows and keys are re-indexed so that its non-zeros fall into
 dense blocks.  This module restates that coordinate system as plain
 definitions, enumerates every (query, key) pair from
-:func:`oracle.sparse_attention.key_set`, maps both ends into kernel
+:func:`oracle.sparse_attention.part_key_set` (the head kind's set, or one
+pass's part of a merged head's set), maps both ends into kernel
 coordinates and counts the pairs that land in each (row block, key block).
 
 Kernel coordinates for one head kind with block size ``bs``:
@@ -41,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .sparse_attention import DENSE, FIXED, FIXED_R1, STRIDED, key_set
+from .sparse_attention import DENSE, FIXED, FIXED_R1, STRIDED, UNION_BASE, part_key_set
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -49,7 +50,11 @@ def _ceil_div(a: int, b: int) -> int:
 
 
 def kernel_maps(pattern: int, kind: int, T: int, l: int, c: int, bs: int):
-    """(row_pos, key_pos): int64 arrays mapping kernel rows / keys to positions."""
+    """(row_pos, key_pos): int64 arrays mapping kernel rows / keys to positions.
+
+    A merged-head pattern's two passes use the maps of its base pattern's two
+    kinds."""
+    pattern = UNION_BASE.get(pattern, pattern)
     identity = np.arange(T, dtype=np.int64)
     if pattern == STRIDED and kind == 1:
         n = _ceil_div(T, l)
@@ -88,7 +93,7 @@ def block_layout(pattern: int, kind: int, T: int, l: int, c: int, bs: int) -> di
     for R, t in enumerate(row_pos):
         if t < 0:
             continue
-        S = key_set(pattern, kind, int(t), T, l, c)
+        S = part_key_set(pattern, kind, int(t), T, l, c)
         K = key_of_pos[S]
         if (K < 0).any():
             raise AssertionError("a key of the pattern has no kernel coordinate")

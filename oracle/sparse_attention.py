@@ -37,6 +37,11 @@ R-scale   d is the head dimension D; lse is the natural log of the sum of
 R-index   Positions are 0-based; T need not be a multiple of l.
 DENSE     Full causal attention S(t) = {j <= t} (nlp-lineage, "The notation"),
           used as the dense comparator and as a special case.
+UNION     Merged heads (STRIDED_UNION, FIXED_UNION): every head attends the
+          union of the pattern's two sets, as llm-arch-kb §2 states each
+          pattern and as its §3 mask sketch builds one mask from both loops.
+          For the fixed pattern the union is the same under either summary
+          reading (own-block summary keys <= t are already in the own block).
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (mask description, closed-form counts, causality,
@@ -49,7 +54,8 @@ import math
 
 import numpy as np
 
-STRIDED, FIXED, FIXED_R1, DENSE = 0, 1, 2, 3
+STRIDED, FIXED, FIXED_R1, DENSE, STRIDED_UNION, FIXED_UNION = 0, 1, 2, 3, 4, 5
+UNION_BASE = {STRIDED_UNION: STRIDED, FIXED_UNION: FIXED}
 
 
 def head_kind(h: int) -> int:
@@ -71,6 +77,10 @@ def key_set(pattern: int, kind: int, t: int, T: int, l: int, c: int) -> np.ndarr
     """
     if not 0 <= t < T:
         raise ValueError("query position out of range")
+    if pattern in UNION_BASE:
+        # merged heads: the union of both sets, whatever the head (reading UNION)
+        base = UNION_BASE[pattern]
+        return np.union1d(key_set(base, 0, t, T, l, c), key_set(base, 1, t, T, l, c))
     if pattern == STRIDED:
         if kind == 0:
             return np.arange(max(0, t - l + 1), t + 1, dtype=np.int64)
@@ -97,6 +107,9 @@ def in_key_set(pattern: int, kind: int, t, j, l: int, c: int) -> np.ndarray:
     """
     t = np.asarray(t, dtype=np.int64)
     j = np.asarray(j, dtype=np.int64)
+    if pattern in UNION_BASE:
+        base = UNION_BASE[pattern]
+        return in_key_set(base, 0, t, j, l, c) | in_key_set(base, 1, t, j, l, c)
     causal = (j >= 0) & (j <= t)
     if pattern == STRIDED:
         if kind == 0:
@@ -112,6 +125,23 @@ def in_key_set(pattern: int, kind: int, t, j, l: int, c: int) -> np.ndarray:
     if pattern == DENSE:
         return causal
     raise ValueError(f"unknown pattern {pattern}")
+
+
+def part_key_set(pattern: int, part: int, t: int, T: int, l: int, c: int) -> np.ndarray:
+    """The part (0 or 1) of S(t) that one head kind, or one pass over a merged
+    head, covers.
+
+    Factorised patterns: the set of head kind ``part``.  Merged heads: the two
+    sets of the base pattern made disjoint, so that the union splits into two
+    parts whose softmaxes merge exactly by their log-sum-exps.  The strided
+    set loses t itself (already in the local window); the fixed sets are
+    disjoint already (own block vs earlier blocks).
+    """
+    if pattern in UNION_BASE:
+        base = UNION_BASE[pattern]
+        S = key_set(base, part, t, T, l, c)
+        return S[S != t] if (base == STRIDED and part == 1) else S
+    return key_set(pattern, part, t, T, l, c)
 
 
 def queries_of_key(pattern: int, kind: int, j: int, T: int, l: int, c: int) -> np.ndarray:

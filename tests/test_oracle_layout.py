@@ -9,7 +9,17 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import DENSE, FIXED, FIXED_R1, STRIDED
+from oracle import DENSE, FIXED, FIXED_R1, FIXED_UNION, STRIDED, STRIDED_UNION, UNION_BASE
+
+
+def in_part(pattern, kind, t, j, l, c):
+    """Membership in the set one LUT covers: the head kind's set, or for merged heads the
+    base kind's set, without t itself on the strided pass (the window has it)."""
+    if pattern in UNION_BASE:
+        base = UNION_BASE[pattern]
+        m = oracle.in_key_set(base, kind, t, j, l, c)
+        return m & (t != j) if (base == STRIDED and kind == 1) else m
+    return oracle.in_key_set(pattern, kind, t, j, l, c)
 
 
 def brute_force_counts(pattern, kind, T, l, c, bs):
@@ -20,7 +30,7 @@ def brute_force_counts(pattern, kind, T, l, c, bs):
     rp[:len(rows)] = rows
     kp = np.full(n_kb * bs, -1)
     kp[:len(keys)] = keys
-    M = oracle.in_key_set(pattern, kind, rp[:, None], kp[None, :], l, c)
+    M = in_part(pattern, kind, rp[:, None], kp[None, :], l, c)
     M &= (rp[:, None] >= 0) & (kp[None, :] >= 0)
     return M.reshape(n_qb, bs, n_kb, bs).sum(axis=(1, 3))
 
@@ -31,11 +41,17 @@ CASES = [
     (FIXED, 1024, 32, 4, 64), (FIXED, 250, 16, 3, 16), (FIXED, 333, 20, 20, 32),
     (FIXED, 60, 64, 4, 64), (FIXED_R1, 250, 16, 3, 16), (FIXED_R1, 256, 32, 4, 64),
     (DENSE, 200, 16, 0, 64),
+    (STRIDED_UNION, 256, 16, 0, 64), (STRIDED_UNION, 300, 7, 0, 16),
+    (FIXED_UNION, 250, 16, 3, 16), (FIXED_UNION, 1024, 32, 4, 64),
 ]
 
 
 @pytest.mark.parametrize("pattern,T,l,c,bs", CASES)
 def test_lut_matches_dense_block_sums(pattern, T, l, c, bs):
+    if pattern in UNION_BASE:
+        # the two passes of a merged head cover the union exactly once
+        total = sum(oracle.block_layout(pattern, kind, T, l, c, bs)["pair_count"] for kind in (0, 1))
+        assert total == oracle.pair_count(pattern, 0, T, l, c)
     for kind in (0, 1):
         lay = oracle.block_layout(pattern, kind, T, l, c, bs)
         counts = brute_force_counts(pattern, kind, T, l, c, bs)
@@ -51,7 +67,8 @@ def test_lut_matches_dense_block_sums(pattern, T, l, c, bs):
         for k in range(lay["n_kb"]):
             sel = kb == k
             assert lay["row_idx"][cp[k]:cp[k + 1]].tolist() == sorted(qb[sel].tolist())
-        assert lay["pair_count"] == oracle.pair_count(pattern, kind, T, l, c)
+        if pattern not in UNION_BASE:
+            assert lay["pair_count"] == oracle.pair_count(pattern, kind, T, l, c)
 
 
 @pytest.mark.parametrize("pattern,T,l,c,bs", CASES)
@@ -64,13 +81,13 @@ def test_maps_are_bijections(pattern, T, l, c, bs):
         assert len(set(real_keys.tolist())) == real_keys.size
         attended = set()
         for t in range(T):
-            attended |= set(oracle.key_set(pattern, kind, t, T, l, c).tolist())
+            attended |= set(oracle.part_key_set(pattern, kind, t, T, l, c).tolist())
         assert attended <= set(real_keys.tolist())
-        if pattern == FIXED and kind == 1:
+        if UNION_BASE.get(pattern, pattern) == FIXED and kind == 1:
             nb = -(-T // l)
             expect = [b * l + o for b in range(nb - 1) for o in range(l - c, l)]
             assert real_keys.tolist() == expect
-        if pattern == STRIDED and kind == 1:
+        if UNION_BASE.get(pattern, pattern) == STRIDED and kind == 1:
             # within a class the run is in increasing position order, l apart
             n_pad = len(rows) // min(l, T)
             assert n_pad % bs == 0

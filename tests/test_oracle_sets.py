@@ -19,8 +19,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (DENSE, FIXED, FIXED_R1, STRIDED, in_key_set, key_set, pair_count,
-                    queries_of_key)
+from oracle import (DENSE, FIXED, FIXED_R1, FIXED_UNION, STRIDED, STRIDED_UNION, UNION_BASE,
+                    in_key_set, key_set, pair_count, part_key_set, queries_of_key)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -74,7 +74,56 @@ def test_key_sets_match_recursive_construction(pattern, T, l, c):
         assert key_set(pattern, 1, t, T, l, c).tolist() == sorted(k1[t]), (t, 1)
 
 
-@pytest.mark.parametrize("pattern,T,l,c", CASES)
+# merged heads: every head attends the union of the pattern's two sets
+UNION_CASES = [
+    (STRIDED_UNION, 64, 8, 0), (STRIDED_UNION, 50, 7, 0), (STRIDED_UNION, 20, 32, 0), (STRIDED_UNION, 33, 1, 0),
+    (FIXED_UNION, 64, 8, 2), (FIXED_UNION, 50, 7, 3), (FIXED_UNION, 40, 8, 8), (FIXED_UNION, 37, 5, 1),
+]
+
+
+@pytest.mark.parametrize("pattern,T,l,c", UNION_CASES)
+def test_union_sets_match_recursive_construction(pattern, T, l, c):
+    k0, k1 = recursive_sets(UNION_BASE[pattern], T, l, c)
+    for t in range(T):
+        for h in (0, 1):
+            assert key_set(pattern, h, t, T, l, c).tolist() == sorted(k0[t] | k1[t]), (t, h)
+
+
+@pytest.mark.parametrize("pattern,T,l,c", UNION_CASES)
+def test_union_parts_split_the_union_disjointly(pattern, T, l, c):
+    """The two passes of a merged head: part 0 is the local / own-block set, part 1 the
+    strided set without t (already in the window) or the summary set; disjoint, and
+    together the union."""
+    k0, k1 = recursive_sets(UNION_BASE[pattern], T, l, c)
+    for t in range(T):
+        p0 = set(part_key_set(pattern, 0, t, T, l, c).tolist())
+        p1 = set(part_key_set(pattern, 1, t, T, l, c).tolist())
+        assert p0 == k0[t]
+        assert p1 == (k1[t] - {t} if pattern == STRIDED_UNION else k1[t])
+        assert not (p0 & p1)
+        assert p0 | p1 == set(key_set(pattern, 0, t, T, l, c).tolist())
+
+
+@pytest.mark.parametrize("T,l", [(256, 16), (250, 16), (1000, 31), (64, 64), (10, 16)])
+def test_strided_union_counts_closed_form(T, l):
+    """|A1 u A2| = min(l, t+1) + floor(t/l): the page's l + ceil(i/l) - 1, i = t+1, once t >= l-1."""
+    for t in range(T):
+        n = len(key_set(STRIDED_UNION, 0, t, T, l, 0))
+        assert n == min(l, t + 1) + t // l
+        if t >= l - 1:
+            assert n == l + math.ceil((t + 1) / l) - 1
+
+
+@pytest.mark.parametrize("T,l,c", [(256, 16, 4), (250, 16, 3), (1024, 32, 4), (96, 8, 8), (12, 16, 2)])
+def test_fixed_union_counts_closed_form(T, l, c):
+    """|B1 u B2| = (t mod l) + 1 + c*floor(t/l), within the page's bound l + c*ceil(i/l)."""
+    for t in range(T):
+        n = len(key_set(FIXED_UNION, 0, t, T, l, c))
+        assert n == t % l + 1 + c * (t // l)
+        assert n <= l + c * math.ceil((t + 1) / l)
+
+
+@pytest.mark.parametrize("pattern,T,l,c", CASES + UNION_CASES)
 def test_membership_predicate_agrees_with_enumeration(pattern, T, l, c):
     tt, jj = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
     for kind in (0, 1):
@@ -126,7 +175,7 @@ def test_fixed_counts_closed_form(T, l, c):
         assert len(b1 | r1) == len(b1) + len(b2)
 
 
-@pytest.mark.parametrize("pattern,T,l,c", CASES)
+@pytest.mark.parametrize("pattern,T,l,c", CASES + UNION_CASES)
 def test_causality(pattern, T, l, c):
     for kind in (0, 1):
         for t in range(T):

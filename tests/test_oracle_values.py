@@ -20,7 +20,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from oracle import DENSE, FIXED, FIXED_R1, STRIDED
+from oracle import DENSE, FIXED, FIXED_R1, FIXED_UNION, STRIDED, STRIDED_UNION, UNION_BASE
 from tests.test_oracle_sets import recursive_sets
 
 
@@ -29,13 +29,18 @@ def rand(shape, seed):
 
 
 def dense_masks(pattern, T, l, c, H):
-    k0, k1 = recursive_sets(pattern, T, l, c)
+    """One boolean [T, T] mask per head: kind h % 2's set, or the union of both for
+    merged-head patterns."""
+    k0, k1 = recursive_sets(UNION_BASE.get(pattern, pattern), T, l, c)
     masks = []
     for h in range(H):
-        sets = k0 if h % 2 == 0 else k1
         m = np.zeros((T, T), dtype=bool)
         for t in range(T):
-            m[t, sorted(sets[t])] = True
+            if pattern in UNION_BASE:
+                keys = k0[t] | k1[t]
+            else:
+                keys = k0[t] if h % 2 == 0 else k1[t]
+            m[t, sorted(keys)] = True
         masks.append(m)
     return masks
 
@@ -44,6 +49,7 @@ SMALL = [
     (STRIDED, 2, 3, 40, 5, 6, 0), (STRIDED, 1, 2, 33, 8, 4, 0),
     (FIXED, 2, 3, 40, 5, 6, 2), (FIXED, 1, 4, 37, 4, 5, 5),
     (FIXED_R1, 1, 2, 40, 3, 6, 2), (DENSE, 1, 2, 25, 4, 6, 0),
+    (STRIDED_UNION, 1, 2, 40, 5, 6, 0), (FIXED_UNION, 2, 2, 37, 4, 5, 2),
 ]
 
 
@@ -85,7 +91,8 @@ def test_backward_matches_torch_autograd(pattern, B, H, T, D, l, c):
 
 
 @pytest.mark.parametrize("pattern,T,l,c", [(STRIDED, 12, 4, 0), (STRIDED, 11, 3, 0),
-                                           (FIXED, 12, 4, 2), (FIXED, 13, 3, 1), (FIXED_R1, 12, 4, 2)])
+                                           (FIXED, 12, 4, 2), (FIXED, 13, 3, 1), (FIXED_R1, 12, 4, 2),
+                                           (STRIDED_UNION, 11, 3, 0), (FIXED_UNION, 12, 4, 2)])
 def test_backward_finite_differences(pattern, T, l, c):
     B, H, D = 1, 2, 3
     q, k, v, dO = (rand((B, H, T, D), s) for s in (8, 9, 10, 11))
@@ -109,6 +116,33 @@ def test_backward_finite_differences(pattern, T, l, c):
             args_m[pos] = xm
             fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
             assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(g[idx])) + 1e-8, (name, idx, fd, g[idx])
+
+
+@pytest.mark.parametrize("pattern,T,l,c", [(STRIDED_UNION, 40, 5, 0), (FIXED_UNION, 40, 5, 2),
+                                           (STRIDED_UNION, 9, 16, 0)])
+def test_union_is_the_lse_merge_of_its_parts(pattern, T, l, c):
+    """Over a union of two disjoint parts, O = (e^lse0 O0 + e^lse1 O1) / (e^lse0 + e^lse1)
+    and lse = log(e^lse0 + e^lse1), with O_p, lse_p the softmax over part p alone (an empty
+    part has lse = -inf and drops out).  The parts' softmaxes are computed here with torch."""
+    B, H, D = 1, 2, 4
+    q, k, v = (rand((B, H, T, D), s) for s in (20, 21, 22))
+    O, L = oracle.forward(q, k, v, pattern, l, c)
+    for h in range(H):
+        for t in range(T):
+            parts = []
+            for part in (0, 1):
+                S = torch.from_numpy(oracle.part_key_set(pattern, part, t, T, l, c))
+                if len(S) == 0:
+                    parts.append((torch.zeros(D, dtype=torch.float64), -math.inf))
+                    continue
+                s_ = torch.from_numpy(k[0, h])[S] @ torch.from_numpy(q[0, h, t]) / math.sqrt(D)
+                parts.append((torch.softmax(s_, 0) @ torch.from_numpy(v[0, h])[S], float(torch.logsumexp(s_, 0))))
+            (o0, l0), (o1, l1) = parts
+            lse = float(torch.logaddexp(torch.tensor(l0, dtype=torch.float64),
+                                        torch.tensor(l1, dtype=torch.float64)))
+            merged = math.exp(l0 - lse) * o0 + math.exp(l1 - lse) * o1
+            np.testing.assert_allclose(O[0, h, t], merged.numpy(), rtol=0, atol=1e-13)
+            assert L[0, h, t] == pytest.approx(lse, abs=1e-13)
 
 
 def test_single_key_rows_are_exact():
