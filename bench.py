@@ -47,9 +47,9 @@ MI355X_FP32_TFLOPS = 157.3     # dense fp32 MFMA peak, TFLOP/s
 # ---------------------------------------------------------------------------
 
 def active_rows(pattern, kind, T, l, c):
-    """Query rows whose key set is non-empty."""
-    from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1
-    if pattern == ST_FIXED and kind == 1:
+    """Query rows whose key set (of this kind, or of this pass for merged heads) is non-empty."""
+    from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1, ST_FIXED_UNION, ST_STRIDED_UNION
+    if pattern in (ST_FIXED, ST_FIXED_UNION, ST_STRIDED_UNION) and kind == 1:
         return max(0, T - l)
     if pattern == ST_FIXED_R1 and kind == 1:
         return max(0, T - (l - c))
@@ -57,14 +57,33 @@ def active_rows(pattern, kind, T, l, c):
 
 
 def attended_keys(pattern, kind, T, l, c):
-    """Key positions some query attends."""
-    from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1
+    """Key positions some query attends (in this kind, or this pass for merged heads)."""
+    from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1, ST_FIXED_UNION, ST_STRIDED_UNION
     nb = -(-T // l)
-    if pattern == ST_FIXED and kind == 1:
+    if pattern in (ST_FIXED, ST_FIXED_UNION) and kind == 1:
         return (nb - 1) * c
     if pattern == ST_FIXED_R1 and kind == 1:
         return sum(1 for b in range(nb) for o in range(c) if b * l + l - c + o < T)
+    if pattern == ST_STRIDED_UNION and kind == 1:
+        return max(0, T - l)
     return T
+
+
+def second_pass_keys(pattern, T, l, c):
+    """Merged heads: key positions the second pass holds (their first-pass dk / dv are
+    carried in fp32 and merged)."""
+    from factorized_sparse_self_amd import ST_FIXED_UNION
+    nb = -(-T // l)
+    return (nb - 1) * c if pattern == ST_FIXED_UNION else T
+
+
+def head_passes(pattern, h):
+    """(kind, store) of each pass over head h: one pass of the head's own kind, or for
+    merged heads a carrying pass of kind 0 and a merging pass of kind 1."""
+    from factorized_sparse_self_amd import ST_FIXED_UNION, ST_STRIDED_UNION
+    if pattern in (ST_STRIDED_UNION, ST_FIXED_UNION):
+        return [(0, "carry"), (1, "merge")]
+    return [(h % 2, "final")]
 
 
 def accounting(w):
@@ -73,41 +92,57 @@ def accounting(w):
     lay = st_layout_build(w.pattern, w.T, w.l, w.c)
     E = 2 if w.dtype == "bf16" else 4
     row = w.D * E
+    crow = w.D * 4  # fp32 carried row of a merged head
     by = {"fwd": 0, "bwd_pre": 0, "bwd_dq": 0, "bwd_dkdv": 0, "bwd_reduce": 0}
     pairs_total = 0
+    visited = 0
     for h in range(w.H):
-        kind = h % 2
-        pairs = lay[kind]["pairs"]
-        rows = active_rows(w.pattern, kind, w.T, w.l, w.c)
-        keys = attended_keys(w.pattern, kind, w.T, w.l, w.c)
-        pairs_total += w.B * pairs
-        # forward: read q (active rows), k and v (attended keys); write out and lse (every row)
-        by["fwd"] += w.B * (rows * row + 2 * keys * row + w.T * (row + 4))
-        # Delta and the zero fill: read out and dout, write Delta; zero dk and dv where no
-        # query attends (a kernel of its own for fp32)
-        pre = w.T * (2 * row + 4) + 2 * (w.T - keys) * row
-        # dq: read q, dout, lse, Delta (active rows), k and v (keys); write dq (every row)
-        dq = rows * (2 * row + 8) + 2 * keys * row + w.T * row
-        if w.dtype == "bf16":
-            # bf16 dq computes Delta itself: reads q, dout, lse (active rows), out (every
-            # row), k and v (keys); writes dq, Delta and lse*log2(e) (every row) and the
-            # zero fill
-            by["bwd_dq"] += w.B * (rows * (2 * row + 4) + 2 * keys * row + w.T * (2 * row + 8)
-                                   + 2 * (w.T - keys) * row)
-        else:
-            by["bwd_pre"] += w.B * pre
-            by["bwd_dq"] += w.B * dq
-        # dk/dv: read q, dout, lse, Delta (active rows), k and v (keys); write dk and dv (keys)
-        by["bwd_dkdv"] += w.B * (rows * (2 * row + 8) + 4 * keys * row)
+        for kind, store in head_passes(w.pattern, h):
+            pairs = lay[kind]["pairs"]
+            rows = active_rows(w.pattern, kind, w.T, w.l, w.c)
+            keys = attended_keys(w.pattern, kind, w.T, w.l, w.c)
+            pairs_total += w.B * pairs
+            visited += w.B * lay[kind]["nnz"]
+            # forward: read q (active rows), k and v (attended keys); write out and lse
+            # (every row), or the fp32 carried output and lse, or read those and write
+            out_fwd = {"final": w.T * (row + 4), "carry": w.T * (crow + 4),
+                       "merge": w.T * (crow + 4) + w.T * (row + 4)}[store]
+            by["fwd"] += w.B * (rows * row + 2 * keys * row + out_fwd)
+            # Delta and the zero fill: read out and dout, write Delta; zero dk and dv where no
+            # query attends (a kernel of its own for fp32)
+            pre = w.T * (2 * row + 4) + 2 * (w.T - keys) * row
+            # dq: read q, dout, lse, Delta (active rows), k and v (keys); write dq (every row)
+            dq = rows * (2 * row + 8) + 2 * keys * row + w.T * row
+            if w.dtype == "bf16":
+                # bf16 dq computes Delta itself: reads q, dout, lse (active rows), out (every
+                # row), k and v (keys); writes dq (or its carried fp32 row, or reads that and
+                # writes dq), Delta and lse*log2(e) (every row, not in a merging pass) and
+                # the zero fill (plain heads)
+                out_dq = {"final": w.T * row, "carry": w.T * crow, "merge": w.T * (crow + row)}[store]
+                side = 8 * w.T if store != "merge" else 0
+                zero = 2 * (w.T - keys) * row if store == "final" else 0
+                by["bwd_dq"] += w.B * (rows * (2 * row + 4) + 2 * keys * row + w.T * row + out_dq + side + zero)
+            else:
+                by["bwd_pre"] += w.B * pre
+                by["bwd_dq"] += w.B * dq
+            # dk/dv: read q, dout, lse, Delta (active rows), k and v (keys); write dk and dv
+            # (keys); merged heads carry the keys the second pass holds in fp32
+            if store == "final":
+                out_kv = 2 * keys * row
+            elif store == "carry":
+                held = second_pass_keys(w.pattern, w.T, w.l, w.c)
+                out_kv = 2 * (held * crow + (w.T - held) * row)
+            else:
+                out_kv = 2 * second_pass_keys(w.pattern, w.T, w.l, w.c) * (crow + row)
+            by["bwd_dkdv"] += w.B * (rows * (2 * row + 8) + 2 * keys * row + out_kv)
     fl = {"fwd": 4 * w.D * pairs_total, "bwd_pre": 0, "bwd_dq": 6 * w.D * pairs_total,
           "bwd_dkdv": 8 * w.D * pairs_total, "bwd_reduce": 0}
     useful = (4 if not w.backward else 14) * w.D * pairs_total
     # executed: every pair of every visited 64x64 LUT block (masked ones included)
-    blk = lay[0]["block"] ** 2
-    visited = sum(w.B * lay[h % 2]["nnz"] * blk for h in range(w.H))
-    executed = (4 if not w.backward else 14) * w.D * visited
+    executed = (4 if not w.backward else 14) * w.D * visited * lay[0]["block"] ** 2
+    head_pairs = [sum(lay[kind]["pairs"] for kind, _ in head_passes(w.pattern, h)) for h in range(2)]
     return {"bytes": by, "flops": fl, "useful_flops": useful, "executed_flops": executed, "pairs": pairs_total,
-            "pairs_per_kind": [lay[0]["pairs"], lay[1]["pairs"]]}
+            "head_pairs": head_pairs}
 
 
 # ---------------------------------------------------------------------------
@@ -158,9 +193,8 @@ def cpu_baseline(w, acct, units):
     """
     import numpy as np
     import oracle
-    pairs = acct["pairs_per_kind"]
     flop_per_pair = (14 if w.backward else 4) * w.D
-    slice_flops = (pairs[0] + pairs[1]) * flop_per_pair
+    slice_flops = sum(acct["head_pairs"]) * flop_per_pair
     rows = None
     slices = [(b, h0) for b in range(w.B) for h0 in range(0, w.H - 1, 2)][:units]
     ctx = mp.get_context("spawn")
@@ -333,9 +367,11 @@ def main():
     executed_tflops = acct["executed_flops"] / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = w.B * w.T / (ms_per_step * 1e-3)
     dom = max(kernels, key=lambda k_: kernels[k_]["ms_per_step"])
+    # per launch: a step's bytes and FLOP of the kernel over its launches per step
+    # (merged heads launch each kernel once per pass)
     dur_s = kernels[dom]["avg_ms"] * 1e-3
-    dom_bytes = acct["bytes"][dom]
-    dom_flops = acct["flops"][dom]
+    dom_bytes = acct["bytes"][dom] / kernels[dom]["launches_per_step"]
+    dom_flops = acct["flops"][dom] / kernels[dom]["launches_per_step"]
     peak_flops = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
     ridge = peak_flops * 1e12 / (MI355X_HBM_GBS * 1e9)
     ai = dom_flops / dom_bytes if dom_bytes else float("inf")

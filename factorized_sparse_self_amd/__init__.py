@@ -5,13 +5,15 @@ The compute lives in ``libst.so`` (hand-written HIP kernels behind the C ABI of
 package does not load the library; the first call does, and raises if it has
 not been built (``python -m factorized_sparse_self_amd.build``).
 """
-from ._lib import (EXPORTED, KERNEL_NAMES, ST_DENSE, ST_FIXED, ST_FIXED_R1, ST_STRIDED, StError,
+from ._lib import (EXPORTED, KERNEL_NAMES, ST_DENSE, ST_FIXED, ST_FIXED_R1, ST_FIXED_UNION, ST_STRIDED,
+                   ST_STRIDED_UNION, StError,
                    lib, sparse_attention, st_block_size, st_layout_build, st_release,
                    st_sparse_attn_bwd, st_sparse_attn_fwd, st_timing_enable, st_timing_read,
                    st_timing_reset)
 
 __all__ = [
-    "EXPORTED", "ST_STRIDED", "ST_FIXED", "ST_FIXED_R1", "ST_DENSE", "StError", "lib",
+    "EXPORTED", "ST_STRIDED", "ST_FIXED", "ST_FIXED_R1", "ST_DENSE", "ST_STRIDED_UNION",
+    "ST_FIXED_UNION", "StError", "lib",
     "sparse_attention", "st_block_size", "st_layout_build", "st_release",
     "st_sparse_attn_bwd", "st_sparse_attn_fwd", "st_timing_enable", "st_timing_read",
     "st_timing_reset", "KERNEL_NAMES",

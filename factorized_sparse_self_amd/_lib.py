@@ -15,7 +15,7 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libst.so")
 
-ST_STRIDED, ST_FIXED, ST_FIXED_R1, ST_DENSE = 0, 1, 2, 3
+ST_STRIDED, ST_FIXED, ST_FIXED_R1, ST_DENSE, ST_STRIDED_UNION, ST_FIXED_UNION = range(6)
 ST_DIM_BLOCK, ST_DIM_ROWS, ST_DIM_KEYS, ST_DIM_QBLOCKS, ST_DIM_KBLOCKS, ST_DIM_NNZ = range(6)
 
 # name -> (restype, argtypes) of every exported symbol

@@ -35,14 +35,23 @@ struct PlanKey {
   }
 };
 
-struct Plan {
-  void* dmem = nullptr;  // single device allocation holding everything below
-  KindDev* kinds = nullptr;
+// Work items of one pass over the heads.  A plain pattern runs one pass in
+// which each head has its own kind; a merged head runs pass p over every head
+// with kind p.
+struct PassItems {
   RowItem* row_items = nullptr;   // row blocks: fp32 forward, dq
   RowItem* pair_items = nullptr;  // row-block pairs: bf16 forward
   DkdvItem* dkdv_items = nullptr;
   ReduceItem* red_items = nullptr;
-  int n_row_items = 0, n_pair_items = 0, n_dkdv_items = 0, n_red_items = 0, n_slots = 0;
+  int n_row_items = 0, n_pair_items = 0, n_dkdv_items = 0, n_red_items = 0;
+};
+
+struct Plan {
+  void* dmem = nullptr;  // single device allocation holding everything below
+  KindDev* kinds = nullptr;
+  int n_pass = 1;
+  PassItems pass[2];
+  int n_slots = 0;  // partial slots of the dK/dV split (passes reuse them)
   ~Plan() {
     if (dmem) (void)hipFree(dmem);
   }
@@ -126,22 +135,6 @@ int build_plan(const PlanKey& key, Plan* plan) {
   for (int kind = 0; kind < 2; ++kind)
     chunk[kind] = std::max(1, (lay.kind[kind].n_qb + chunks_per_head - 1) / chunks_per_head);
 
-  // Row-block items (forward and dq): every row block of every head; cost =
-  // key blocks visited + 1; grouped by (head, range of row blocks).
-  std::vector<RowItem> rows;
-  std::vector<int64_t> rcost, rgroup;
-  for (int bh = 0; bh < BH; ++bh) {
-    const int kind = (bh % key.H) & 1;
-    const KindLayout& L = lay.kind[kind];
-    for (int qb = 0; qb < L.n_qb; ++qb) {
-      rows.push_back({qb, bh, kind, 0});
-      rcost.push_back(L.row_ptr[qb + 1] - L.row_ptr[qb] + 1);
-      rgroup.push_back((int64_t)bh * 65536 + qb / chunk[kind]);
-    }
-  }
-  std::vector<RowItem> row_items;
-  for (int i : xcd_order(rcost, rgroup)) row_items.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : rows[i]);
-
   // Row-block pairs: the CSR rows of blocks 2p and 2p+1 merged (both ascending)
   // into one list of key blocks with per-half visit / FULL bits.
   std::vector<int32_t> pair_ptr[2];
@@ -164,56 +157,82 @@ int build_plan(const PlanKey& key, Plan* plan) {
       pair_ptr[kind][pb + 1] = (int32_t)pair_entry[kind].size();
     }
   }
-  std::vector<RowItem> pairs;
-  std::vector<int64_t> pcost, pgroup;
-  for (int bh = 0; bh < BH; ++bh) {
-    const int kind = (bh % key.H) & 1;
-    const int n_pairs = (int)pair_ptr[kind].size() - 1;
-    for (int pb = 0; pb < n_pairs; ++pb) {
-      pairs.push_back({pb, bh, kind, 0});
-      pcost.push_back(pair_ptr[kind][pb + 1] - pair_ptr[kind][pb] + 1);
-      pgroup.push_back((int64_t)bh * 65536 + 2 * pb / chunk[kind]);
+  const bool merged = is_union(key.pattern);
+  const int n_pass = merged ? 2 : 1;
+  // kind of head bh in pass p
+  auto kind_of = [&](int p, int bh) { return merged ? p : (bh % key.H) & 1; };
+  struct HostPass {
+    std::vector<RowItem> rows, pairs;
+    std::vector<DkdvItem> dkdv;
+    std::vector<ReduceItem> red;
+  } hp[2];
+  int max_slots = 0;
+  for (int p = 0; p < n_pass; ++p) {
+    // Row-block items (fp32 forward, dq): every row block of every head; cost
+    // = key blocks visited + 1; grouped by (head, range of row blocks).
+    std::vector<RowItem> rows;
+    std::vector<int64_t> rcost, rgroup;
+    for (int bh = 0; bh < BH; ++bh) {
+      const int kind = kind_of(p, bh);
+      const KindLayout& L = lay.kind[kind];
+      for (int qb = 0; qb < L.n_qb; ++qb) {
+        rows.push_back({qb, bh, kind, 0});
+        rcost.push_back(L.row_ptr[qb + 1] - L.row_ptr[qb] + 1);
+        rgroup.push_back((int64_t)bh * 65536 + qb / chunk[kind]);
+      }
     }
-  }
-  std::vector<RowItem> pair_items;
-  for (int i : xcd_order(pcost, pgroup)) pair_items.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : pairs[i]);
+    for (int i : xcd_order(rcost, rgroup)) hp[p].rows.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : rows[i]);
 
-  // dK/dV items: every key block of every head.  A key block whose row-block
-  // list is longer than kDkdvSplit is split at row-block multiples of
-  // kDkdvSplit, so that the splits of different key blocks read the same row
-  // blocks; grouped by (head, first row block read).
-  std::vector<DkdvItem> dkdv;
-  std::vector<int64_t> dcost, dgroup;
-  std::vector<ReduceItem> red;
-  int slots = 0;
-  for (int bh = 0; bh < BH; ++bh) {
-    const int kind = (bh % key.H) & 1;
-    const KindLayout& L = lay.kind[kind];
-    for (int kb = 0; kb < L.n_kb; ++kb) {
-      const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
-      const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
-      if (e1 - e0 <= kDkdvSplit) {
-        dkdv.push_back({kb, bh, e0, e1, -1, kind, 0, 0});
-        dcost.push_back(e1 - e0 + 1);
-        dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
-        continue;
+    // Row-block pair items (bf16 forward).
+    std::vector<RowItem> pairs;
+    std::vector<int64_t> pcost, pgroup;
+    for (int bh = 0; bh < BH; ++bh) {
+      const int kind = kind_of(p, bh);
+      const int n_pairs = (int)pair_ptr[kind].size() - 1;
+      for (int pb = 0; pb < n_pairs; ++pb) {
+        pairs.push_back({pb, bh, kind, 0});
+        pcost.push_back(pair_ptr[kind][pb + 1] - pair_ptr[kind][pb] + 1);
+        pgroup.push_back((int64_t)bh * 65536 + 2 * pb / chunk[kind]);
       }
-      const int slot0 = slots;
-      for (int a = e0; a < e1;) {
-        const int range = L.row_idx[a] / kDkdvSplit;
-        int b = a;
-        while (b < e1 && L.row_idx[b] / kDkdvSplit == range) ++b;
-        dkdv.push_back({kb, bh, a, b, slots++, kind, 0, 0});
-        dcost.push_back(b - a + 1);
-        dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);
-        a = b;
-      }
-      red.push_back({kb, bh, slot0, slots - slot0, kind, 0, 0, 0});
     }
+    for (int i : xcd_order(pcost, pgroup)) hp[p].pairs.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : pairs[i]);
+
+    // dK/dV items: every key block of every head.  A key block whose row-block
+    // list is longer than kDkdvSplit is split at row-block multiples of
+    // kDkdvSplit, so that the splits of different key blocks read the same row
+    // blocks; grouped by (head, first row block read).
+    std::vector<DkdvItem> dkdv;
+    std::vector<int64_t> dcost, dgroup;
+    int slots = 0;
+    for (int bh = 0; bh < BH; ++bh) {
+      const int kind = kind_of(p, bh);
+      const KindLayout& L = lay.kind[kind];
+      for (int kb = 0; kb < L.n_kb; ++kb) {
+        const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
+        const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
+        if (e1 - e0 <= kDkdvSplit) {
+          dkdv.push_back({kb, bh, e0, e1, -1, kind, 0, 0});
+          dcost.push_back(e1 - e0 + 1);
+          dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
+          continue;
+        }
+        const int slot0 = slots;
+        for (int a = e0; a < e1;) {
+          const int range = L.row_idx[a] / kDkdvSplit;
+          int b = a;
+          while (b < e1 && L.row_idx[b] / kDkdvSplit == range) ++b;
+          dkdv.push_back({kb, bh, a, b, slots++, kind, 0, 0});
+          dcost.push_back(b - a + 1);
+          dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);
+          a = b;
+        }
+        hp[p].red.push_back({kb, bh, slot0, slots - slot0, kind, 0, 0, 0});
+      }
+    }
+    for (int i : xcd_order(dcost, dgroup))
+      hp[p].dkdv.push_back(i < 0 ? DkdvItem{-1, -1, 0, 0, -1, 0, 0, 0} : dkdv[i]);
+    max_slots = std::max(max_slots, slots);
   }
-  std::vector<DkdvItem> dkdv_items;
-  for (int i : xcd_order(dcost, dgroup))
-    dkdv_items.push_back(i < 0 ? DkdvItem{-1, -1, 0, 0, -1, 0, 0, 0} : dkdv[i]);
   Blob blob;
   KindDev kinds_host[2];
   size_t off_kinds = blob.add(kinds_host, sizeof(kinds_host));
@@ -234,10 +253,13 @@ int build_plan(const PlanKey& key, Plan* plan) {
     offs[kind][8] = blob.add(pair_ptr[kind].data(), pair_ptr[kind].size() * 4);
     offs[kind][9] = blob.add(pair_entry[kind].data(), pair_entry[kind].size() * 4);
   }
-  const size_t off_rows = blob.add(row_items.data(), row_items.size() * sizeof(RowItem));
-  const size_t off_pairs = blob.add(pair_items.data(), pair_items.size() * sizeof(RowItem));
-  const size_t off_dkdv = blob.add(dkdv_items.data(), dkdv_items.size() * sizeof(DkdvItem));
-  const size_t off_red = blob.add(red.data(), red.size() * sizeof(ReduceItem));
+  size_t off_items[2][4];
+  for (int p = 0; p < n_pass; ++p) {
+    off_items[p][0] = blob.add(hp[p].rows.data(), hp[p].rows.size() * sizeof(RowItem));
+    off_items[p][1] = blob.add(hp[p].pairs.data(), hp[p].pairs.size() * sizeof(RowItem));
+    off_items[p][2] = blob.add(hp[p].dkdv.data(), hp[p].dkdv.size() * sizeof(DkdvItem));
+    off_items[p][3] = blob.add(hp[p].red.data(), hp[p].red.size() * sizeof(ReduceItem));
+  }
 
   hipError_t e = hipMalloc(&plan->dmem, blob.bytes.size());
   if (e != hipSuccess) {
@@ -265,15 +287,19 @@ int build_plan(const PlanKey& key, Plan* plan) {
   e = hipMemcpy(plan->dmem, blob.bytes.data(), blob.bytes.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail("plan upload", e);
   plan->kinds = (KindDev*)(dbase + off_kinds);
-  plan->row_items = (RowItem*)(dbase + off_rows);
-  plan->dkdv_items = (DkdvItem*)(dbase + off_dkdv);
-  plan->red_items = (ReduceItem*)(dbase + off_red);
-  plan->pair_items = (RowItem*)(dbase + off_pairs);
-  plan->n_row_items = (int)row_items.size();
-  plan->n_pair_items = (int)pair_items.size();
-  plan->n_dkdv_items = (int)dkdv_items.size();
-  plan->n_red_items = (int)red.size();
-  plan->n_slots = slots;
+  plan->n_pass = n_pass;
+  for (int p = 0; p < n_pass; ++p) {
+    PassItems& P = plan->pass[p];
+    P.row_items = (RowItem*)(dbase + off_items[p][0]);
+    P.pair_items = (RowItem*)(dbase + off_items[p][1]);
+    P.dkdv_items = (DkdvItem*)(dbase + off_items[p][2]);
+    P.red_items = (ReduceItem*)(dbase + off_items[p][3]);
+    P.n_row_items = (int)hp[p].rows.size();
+    P.n_pair_items = (int)hp[p].pairs.size();
+    P.n_dkdv_items = (int)hp[p].dkdv.size();
+    P.n_red_items = (int)hp[p].red.size();
+  }
+  plan->n_slots = max_slots;
   return ST_OK;
 }
 
@@ -344,13 +370,27 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
   return ST_OK;
 }
 
+bool uses_c(int pattern) { return pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION; }
+
+// Merged heads run bf16 only.
+int check_union_dtype(const char* fn, int pattern, bool bf16_path) {
+  if (is_union(pattern) && !bf16_path) {
+    set_error(std::string(fn) + ": merged-head patterns have no fp32 path");
+    return ST_ERR_UNSUPPORTED;
+  }
+  return ST_OK;
+}
+
 template <typename TE>
 int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
   const void* ptrs[] = {q, k, v, out, lse};
   int rc = check_attn_args(fn, ptrs, 5, B, H, T, D, pattern, l, c);
   if (rc != ST_OK) return rc;
-  if (pattern != ST_FIXED && pattern != ST_FIXED_R1) c = 0;
+  constexpr bool kBf16 = std::is_same<TE, bf16>::value;
+  rc = check_union_dtype(fn, pattern, kBf16);
+  if (rc != ST_OK) return rc;
+  if (!uses_c(pattern)) c = 0;
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return hip_fail(fn, e);
@@ -367,15 +407,31 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   a.H = H;
   a.T = T;
   a.kinds = plan->kinds;
-  // bf16: one workgroup per pair of row blocks; fp32: per row block
-  const bool pairs = std::is_same<TE, bf16>::value;
-  a.items = pairs ? plan->pair_items : plan->row_items;
-  const int n_items = pairs ? plan->n_pair_items : plan->n_row_items;
   a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   a.pattern = pattern;
+  a.out_mode = OUT_FINAL;
+  a.carry_o = nullptr;
+  a.carry_lse = nullptr;
+  if (plan->n_pass == 2) {
+    // first pass: fp32 output and lse of every row, merged by the second
+    const size_t rows = (size_t)B * H * T;
+    const size_t o_bytes = align_up(rows * D * sizeof(float), 256);
+    void* ws = nullptr;
+    rc = get_workspace(device, o_bytes + rows * sizeof(float), &ws);
+    if (rc != ST_OK) return rc;
+    a.carry_o = (float*)ws;
+    a.carry_lse = (float*)((unsigned char*)ws + o_bytes);
+  }
   hipStream_t s = (hipStream_t)stream;
-  e = (D == 32) ? launch_fwd<TE, 32>(a, n_items, s) : launch_fwd<TE, 64>(a, n_items, s);
-  if (e != hipSuccess) return hip_fail(fn, e);
+  for (int p = 0; p < plan->n_pass; ++p) {
+    const PassItems& P = plan->pass[p];
+    // bf16: one workgroup per pair of row blocks; fp32: per row block
+    a.items = kBf16 ? P.pair_items : P.row_items;
+    const int n_items = kBf16 ? P.n_pair_items : P.n_row_items;
+    if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
+    e = (D == 32) ? launch_fwd<TE, 32>(a, n_items, s) : launch_fwd<TE, 64>(a, n_items, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
   return ST_OK;
 }
 
@@ -386,7 +442,9 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
   int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c);
   if (rc != ST_OK) return rc;
-  if (pattern != ST_FIXED && pattern != ST_FIXED_R1) c = 0;
+  rc = check_union_dtype(fn, pattern, std::is_same<TE, bf16>::value);
+  if (rc != ST_OK) return rc;
+  if (!uses_c(pattern)) c = 0;
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return hip_fail(fn, e);
@@ -394,11 +452,16 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   Plan* plan = nullptr;
   rc = get_plan({device, pattern, T, l, c, B, H}, &plan);
   if (rc != ST_OK) return rc;
-  const size_t delta_bytes = align_up((size_t)B * H * T * sizeof(float), 256);
-  const size_t partial_bytes = (size_t)plan->n_slots * 2 * kBlock * D * sizeof(float);
+  // workspace: Delta, lse2, split partials, and for merged heads the first
+  // pass's fp32 dq, dk, dv
+  const size_t rows = (size_t)B * H * T;
+  const size_t delta_bytes = align_up(rows * sizeof(float), 256);
+  const size_t partial_bytes = align_up((size_t)plan->n_slots * 2 * kBlock * D * sizeof(float), 256);
+  const size_t carry_bytes = plan->n_pass == 2 ? align_up(rows * D * sizeof(float), 256) : 0;
   void* ws = nullptr;
-  rc = get_workspace(device, 2 * delta_bytes + partial_bytes, &ws);
+  rc = get_workspace(device, 2 * delta_bytes + partial_bytes + 3 * carry_bytes, &ws);
   if (rc != ST_OK) return rc;
+  unsigned char* wb = (unsigned char*)ws;
   BwdArgs a;
   a.q = q;
   a.k = k;
@@ -409,24 +472,33 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = (float*)ws;
-  a.lse2 = (float*)((unsigned char*)ws + delta_bytes);
-  a.partial = (float*)((unsigned char*)ws + 2 * delta_bytes);
+  a.delta = (float*)wb;
+  a.lse2 = (float*)(wb + delta_bytes);
+  a.partial = (float*)(wb + 2 * delta_bytes);
+  a.carry_dq = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes) : nullptr;
+  a.carry_dk = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes + carry_bytes) : nullptr;
+  a.carry_dv = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes + 2 * carry_bytes) : nullptr;
   a.BH = B * H;
   a.H = H;
   a.T = T;
   a.kinds = plan->kinds;
-  a.dq_items = plan->row_items;
-  const int n_dq = plan->n_row_items;
-  a.dkdv_items = plan->dkdv_items;
-  a.red_items = plan->red_items;
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.sl2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   a.pattern = pattern;
+  a.out_mode = OUT_FINAL;
   hipStream_t s = (hipStream_t)stream;
-  e = (D == 32) ? launch_bwd<TE, 32>(a, n_dq, plan->n_dkdv_items, plan->n_red_items, s)
-                : launch_bwd<TE, 64>(a, n_dq, plan->n_dkdv_items, plan->n_red_items, s);
-  if (e != hipSuccess) return hip_fail(fn, e);
+  // merged heads: every launch of the first pass (carry) precedes the second
+  // (merge) on the stream
+  for (int p = 0; p < plan->n_pass; ++p) {
+    const PassItems& P = plan->pass[p];
+    if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
+    a.dq_items = P.row_items;
+    a.dkdv_items = P.dkdv_items;
+    a.red_items = P.red_items;
+    e = (D == 32) ? launch_bwd<TE, 32>(a, P.n_row_items, P.n_dkdv_items, P.n_red_items, s)
+                  : launch_bwd<TE, 64>(a, P.n_row_items, P.n_dkdv_items, P.n_red_items, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
   return ST_OK;
 }
 

@@ -356,6 +356,42 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Stores of one gradient row (dq of a query, dk or dv of a key): ND runs of 4
+// floats at element offsets 16 d (the lane's quarter of the row; `dst` and
+// `carry` point at its first element), scaled by `scale`, written as the
+// launch's OutMode says.
+// ---------------------------------------------------------------------------
+template <int ND>
+__device__ __forceinline__ void store_grad_row(int mode, float* carry, bf16* dst, const f32x4* x, float scale) {
+  if (mode == OUT_CARRY) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 y = x[d] * scale;
+      *(float4*)(carry + 16 * d) = make_float4(y[0], y[1], y[2], y[3]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    f32x4 y = x[d] * scale;
+    if (mode == OUT_MERGE) {
+      const float4 c = *(const float4*)(carry + 16 * d);
+      y += (f32x4){c.x, c.y, c.z, c.w};
+    }
+    *(bf16x4*)(dst + 16 * d) = to_bf16x4(y);
+  }
+}
+
+// Store mode of the dk / dv row of key position p: in the first pass of a
+// merged head, only keys that the second pass holds are carried; the others
+// are final.
+__device__ __forceinline__ int key_out_mode(const BwdArgs& a, int p) {
+  if (a.out_mode != OUT_CARRY) return a.out_mode;
+  const Geometry g1 = load_uniform(&a.kinds[1].geo);
+  return position_is_key(g1, p) ? OUT_CARRY : OUT_FINAL;
+}
+
+// ---------------------------------------------------------------------------
 // bf16 dq and dk/dv.  As in the forward: the streamed blocks (K and V for dq;
 // Q and dO with their lse, Delta and key runs for dk/dv) go straight from
 // global memory into a ring of swizzled LDS stages (st_stage.hpp) with the
@@ -427,23 +463,27 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
     lse2 = buf_load_f32(make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4), (uint32_t)t * 4) * kLog2e;
     delta = delta_row;
   }
-  // Delta and lse*log2(e) of every row, for the dk/dv pass that follows
-  if (t >= 0 && lg == 0) {
+  // Delta and lse*log2(e) of every row, for the dk/dv pass that follows (the
+  // first pass of a merged head writes them for every row; its second pass
+  // holds rows that attend nothing, whose values it would zero)
+  if (t >= 0 && lg == 0 && a.out_mode != OUT_MERGE) {
     a.delta[(size_t)bh * a.T + t] = delta_row;
     a.lse2[(size_t)bh * a.T + t] = lse2;
   }
   // keys nobody attends (positions outside a summary head's key map) get
   // dk = dv = 0; the row positions of this block cover every such position
+  // (in a merged head the first pass writes them)
   if constexpr (KC == K_SUMMARY || KC == K_SUMMARY_R1) {
-    for (int u = tid; u < kBlock * CH; u += kThreads) {
-      const int r = u / CH, ch = u % CH;
-      const int tp = block_position(g, false, qb, r);
-      if (tp >= 0 && !position_is_key(g, tp)) {
-        const uint4 z = {0, 0, 0, 0};
-        *(uint4*)((bf16*)a.dk + base + (size_t)tp * D + ch * 8) = z;
-        *(uint4*)((bf16*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+    if (a.out_mode == OUT_FINAL)
+      for (int u = tid; u < kBlock * CH; u += kThreads) {
+        const int r = u / CH, ch = u % CH;
+        const int tp = block_position(g, false, qb, r);
+        if (tp >= 0 && !position_is_key(g, tp)) {
+          const uint4 z = {0, 0, 0, 0};
+          *(uint4*)((bf16*)a.dk + base + (size_t)tp * D + ch * 8) = z;
+          *(uint4*)((bf16*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+        }
       }
-    }
   }
   // per-lane byte offsets of the MFMA operand reads inside a staged block
   int a_off[NQ], t_off[ND];
@@ -507,9 +547,8 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
   if (t < 0) return;
-  bf16* dq = (bf16*)a.dq + base + (size_t)t * D;
-#pragma unroll
-  for (int d = 0; d < ND; ++d) *(bf16x4*)(dq + 16 * d + 4 * lg) = to_bf16x4(acc[d] * a.scale);
+  store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
+                     (bf16*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
 }
 
 // One kernel per pattern; each workgroup branches once on its head's kind.
@@ -690,13 +729,10 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
 
   if (item.slot < 0) {
     if (kp < 0) return;
-    bf16* dkp = (bf16*)a.dk + base + (size_t)kp * D;
-    bf16* dvp = (bf16*)a.dv + base + (size_t)kp * D;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      *(bf16x4*)(dkp + 16 * d + 4 * lg) = to_bf16x4(dk[d] * a.scale);
-      *(bf16x4*)(dvp + 16 * d + 4 * lg) = to_bf16x4(dv[d]);
-    }
+    const int mode = key_out_mode(a, kp);
+    const size_t off = ((size_t)bh * a.T + kp) * D + 4 * lg;
+    store_grad_row<ND>(mode, a.carry_dk + off, (bf16*)a.dk + off, dk, a.scale);
+    store_grad_row<ND>(mode, a.carry_dv + off, (bf16*)a.dv + off, dv, 1.f);
   } else {
     float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
     float* pv = pk + kBlock * D;
@@ -751,7 +787,10 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
   }
   TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
   if constexpr (IsBf16<TE>::value) {
-    *(bf16x4*)dst = to_bf16x4((f32x4){s.x, s.y, s.z, s.w});
+    const int mode = key_out_mode(a, kp);
+    f32x4 x[1] = {(f32x4){s.x, s.y, s.z, s.w}};
+    store_grad_row<1>(mode, (which ? a.carry_dv : a.carry_dk) + base + (size_t)kp * D + ch * 4, (bf16*)dst, x,
+                      1.f);
   } else {
     *(float4*)dst = s;
   }
@@ -777,7 +816,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   if (n_dq > 0) {
     timing_begin(KID_DQ, stream);
     if constexpr (IsBf16<TE>::value) {
-      err = with_kind_codes(a.pattern, [&](auto c0, auto c1) {
+      err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
         hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kDqStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_dq),
                            dim3(kThreads), 0, stream, a);
         return hipGetLastError();
@@ -792,7 +831,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
     if constexpr (IsBf16<TE>::value) {
-      err = with_kind_codes(a.pattern, [&](auto c0, auto c1) {
+      err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
         hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kDkdvStages, decltype(c0)::value, decltype(c1)::value>),
                            dim3(n_dkdv), dim3(kThreads), 0, stream, a);
         return hipGetLastError();

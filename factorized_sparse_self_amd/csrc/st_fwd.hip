@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 //    when a logit exceeds it by more than 2^8 in exp2 units; blocks where no
 //    lane of the wave needs that skip the cross-lane max and the rescale.
 // ---------------------------------------------------------------------------
-template <int D, int NS, int KC>
+template <int D, int NS, int KC, bool M>
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, int kind,
                                               unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
@@ -386,11 +386,43 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, 
     if (t[G] < 0) continue;
     // the output is rounded to bf16, so the hardware reciprocal (1 ulp) suffices
     const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
+    const float lse2 = lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
+    const size_t row = (size_t)bh * a.T + t[G];
+    if (M && a.out_mode == OUT_CARRY) {
+      // first pass of a merged head: keep the normalised fp32 output and lse
+      float* C = a.carry_o + row * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const f32x4 o = acc[G][d] * inv;
+        *(float4*)(C + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (lg == 0) a.carry_lse[row] = lse2;
+      continue;
+    }
     bf16* O = (bf16*)a.o + base + (size_t)t[G] * D;
+    if (M && a.out_mode == OUT_MERGE) {
+      // softmax over both key sets: weights exp2(L_p - L) of the two passes'
+      // outputs, L = log2(2^L0 + 2^L1) (a pass with no keys has L_p = -inf)
+      const float lse0 = a.carry_lse[row];
+      const float mx = fmaxf(lse0, lse2);
+      const float w0 = mx == -INFINITY ? 0.f : fast_exp2(lse0 - mx);
+      const float w1 = mx == -INFINITY ? 0.f : fast_exp2(lse2 - mx);
+      const float sw = w0 + w1;
+      const float isw = sw > 0.f ? __builtin_amdgcn_rcpf(sw) : 0.f;
+      const float s0 = w0 * isw, s1 = w1 * inv * isw;
+      const float* C = a.carry_o + row * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const float4 c = *(const float4*)(C + 16 * d + 4 * lg);
+        const f32x4 c4 = {c.x, c.y, c.z, c.w};
+        *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(c4 * s0 + acc[G][d] * s1);
+      }
+      if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
+      continue;
+    }
 #pragma unroll
     for (int d = 0; d < ND; ++d) *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(acc[G][d] * inv);
-    if (lg == 0)
-      a.lse[(size_t)bh * a.T + t[G]] = lsum > 0.f ? (m_run[G] * sl2 + fast_log2(lsum)) * kLn2 : -INFINITY;
+    if (lg == 0) a.lse[row] = lse2 * kLn2;
   }
 }
 
@@ -398,15 +430,17 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, 
 
 // One kernel per pattern: the two head kinds' bodies are specialised on their
 // kind codes, and each workgroup branches once, uniformly, on its head's kind.
-template <int D, int NS, int C0, int C1>
+// M: merged heads (the epilogue carries or merges; plain patterns compile
+// without those stores).
+template <int D, int NS, int C0, int C1, bool M>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
   const RowItem item = load_uniform(&a.items[blockIdx.x]);
   if (item.qb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    fwd_bf16_body<D, NS, C0>(a, item.qb, item.bh, 0, ring);  // item.qb: pair of row blocks
+    fwd_bf16_body<D, NS, C0, M>(a, item.qb, item.bh, 0, ring);  // item.qb: pair of row blocks
   else
-    fwd_bf16_body<D, NS, C1>(a, item.qb, item.bh, 1, ring);
+    fwd_bf16_body<D, NS, C1, M>(a, item.qb, item.bh, 1, ring);
 }
 
 template <typename TE, int D>
@@ -415,9 +449,10 @@ hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   timing_begin(KID_FWD, stream);
   hipError_t err;
   if constexpr (IsBf16<TE>::value) {
-    err = with_kind_codes(a.pattern, [&](auto c0, auto c1) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, kFwdStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_items),
-                         dim3(kThreads), 0, stream, a);
+    err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto m) {
+      hipLaunchKernelGGL(
+          (fwd_bf16_kernel<D, kFwdStages, decltype(c0)::value, decltype(c1)::value, decltype(m)::value>),
+          dim3(n_items), dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     });
   } else {

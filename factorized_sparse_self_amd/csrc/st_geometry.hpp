@@ -15,6 +15,8 @@
 //   K_SUMMARY_R1  compact summary keys of every block (positions >= T are
 //                 padding); earlier blocks plus own-block summary keys <= t
 //   K_CAUSAL      rows = keys = positions; [0, t]
+//   K_STRIDE_X    K_STRIDE without the row's own key: [r*n_pad, R-1] (the
+//                 strided pass of a merged head, whose window holds t)
 #pragma once
 
 #include <stdint.h>
@@ -35,6 +37,7 @@ enum KindCode : int {
   K_SUMMARY = 3,
   K_SUMMARY_R1 = 4,
   K_CAUSAL = 5,
+  K_STRIDE_X = 6,
 };
 
 constexpr int kBlock = 64;  // LUT block size, rows and keys
@@ -77,11 +80,17 @@ struct GeoC : Geometry {
 ST_HD int imin(int a, int b) { return a < b ? a : b; }
 ST_HD int imax(int a, int b) { return a > b ? a : b; }
 
+// Residue-major maps (K_STRIDE and K_STRIDE_X share them).
+template <class G>
+ST_HD bool residue_major(const G& g) {
+  return g.code == K_STRIDE || g.code == K_STRIDE_X;
+}
+
 // Position held by kernel row R, or -1 for padding / out of range.
 template <class G>
 ST_HD int row_position(const G& g, int R) {
   if (R < 0 || R >= g.n_rows) return -1;
-  if (g.code == K_STRIDE) {
+  if (residue_major(g)) {
     const int r = fdiv(R, g.div_pad);
     const int m = R - r * g.n_pad;
     const int64_t p = (int64_t)m * g.l + r;
@@ -94,7 +103,7 @@ ST_HD int row_position(const G& g, int R) {
 template <class G>
 ST_HD int key_position(const G& g, int K) {
   if (K < 0 || K >= g.n_keys) return -1;
-  if (g.code == K_STRIDE) {
+  if (residue_major(g)) {
     const int r = fdiv(K, g.div_pad);
     const int m = K - r * g.n_pad;
     const int64_t p = (int64_t)m * g.l + r;
@@ -114,7 +123,7 @@ ST_HD int key_position(const G& g, int K) {
 // the kind is uniform; only the compact summary map divides, by multiply-shift.
 template <class G>
 ST_HD int block_position(const G& g, bool keys, int blk, int i) {
-  if (g.code == K_STRIDE) {
+  if (residue_major(g)) {
     // n_pad is a multiple of kBlock, so a block lies inside one residue class
     const int cls = fdiv(blk * kBlock, g.div_pad);
     const int m = blk * kBlock - cls * g.n_pad + i;
@@ -148,7 +157,7 @@ ST_HD bool split_position_ok(const G& g, bool keys) {
 }
 template <class G>
 ST_HD RowPart row_part(const G& g, bool keys, int i) {
-  if (g.code == K_STRIDE) return {i * g.l};
+  if (residue_major(g)) return {i * g.l};
   if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) {
     const int q = fdiv(i, g.div_c);
     return {q * g.l + (g.l - g.c) + (i - q * g.c)};
@@ -157,7 +166,7 @@ ST_HD RowPart row_part(const G& g, bool keys, int i) {
 }
 template <class G>
 ST_HD BlockPart block_part(const G& g, bool keys, int blk) {
-  if (g.code == K_STRIDE) {
+  if (residue_major(g)) {
     const int cls = fdiv(blk * kBlock, g.div_pad);
     const int m0 = blk * kBlock - cls * g.n_pad;
     return {m0 * g.l + cls, cls < g.n_cls ? kBlock : 0};
@@ -191,6 +200,10 @@ ST_HD void row_interval(const G& g, int R, int t, int& lo, int& hi) {
     case K_STRIDE:
       lo = fdiv(R, g.div_pad) * g.n_pad;
       hi = R;
+      break;
+    case K_STRIDE_X:
+      lo = fdiv(R, g.div_pad) * g.n_pad;
+      hi = R - 1;
       break;
     case K_BLOCK:
       lo = fdiv(t, g.div_l) * g.l;

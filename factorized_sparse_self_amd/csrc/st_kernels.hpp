@@ -11,19 +11,34 @@
 
 namespace st {
 
-// Calls f(c0, c1) with the kind codes of `pattern`'s two head kinds as
-// std::integral_constant values, so that launchers can pick kernels
-// specialised on them.
+// Calls f(c0, c1, m) with the kind codes of `pattern`'s two head kinds and
+// whether its heads are merged (two passes) as std::integral_constant values,
+// so that launchers can pick kernels specialised on them.
 template <class F>
 hipError_t with_kind_codes(int pattern, F&& f) {
   using std::integral_constant;
+  using plain = integral_constant<bool, false>;
+  using merged = integral_constant<bool, true>;
   switch (pattern) {
-    case ST_STRIDED: return f(integral_constant<int, K_LOCAL>(), integral_constant<int, K_STRIDE>());
-    case ST_FIXED: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY>());
-    case ST_FIXED_R1: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY_R1>());
-    default: return f(integral_constant<int, K_CAUSAL>(), integral_constant<int, K_CAUSAL>());
+    case ST_STRIDED: return f(integral_constant<int, K_LOCAL>(), integral_constant<int, K_STRIDE>(), plain());
+    case ST_FIXED: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY>(), plain());
+    case ST_FIXED_R1: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY_R1>(), plain());
+    case ST_STRIDED_UNION:
+      return f(integral_constant<int, K_LOCAL>(), integral_constant<int, K_STRIDE_X>(), merged());
+    case ST_FIXED_UNION: return f(integral_constant<int, K_BLOCK>(), integral_constant<int, K_SUMMARY>(), merged());
+    default: return f(integral_constant<int, K_CAUSAL>(), integral_constant<int, K_CAUSAL>(), plain());
   }
 }
+
+// True for the merged-head patterns (two passes over every head).
+inline bool is_union(int pattern) { return pattern == ST_STRIDED_UNION || pattern == ST_FIXED_UNION; }
+
+// Where a launch stores its results.  A plain head writes them (OUT_FINAL).
+// A merged head runs two passes over the same rows and keys: the first
+// (OUT_CARRY) keeps its fp32 results in the carry buffers, except for keys the
+// second pass never holds, which it finishes itself; the second (OUT_MERGE)
+// combines its own results with the carried ones and writes the outputs.
+enum OutMode : int { OUT_FINAL = 0, OUT_CARRY = 1, OUT_MERGE = 2 };
 
 // Work item of the dK/dV pass: key block kb of head bh, CSC entries [e0, e1).
 // slot >= 0: the key block is split over several items and this one writes
@@ -54,6 +69,9 @@ struct FwdArgs {
   const RowItem* items;
   float sl2;             // log2(e) / sqrt(D)
   int pattern;           // ST_* (host side: selects the kernel)
+  int out_mode;          // OutMode
+  float* carry_o;        // merged heads: [B*H*T*D] first-pass output (fp32)
+  float* carry_lse;      // merged heads: [B*H*T] first-pass lse, log2 units
 };
 
 struct BwdArgs {
@@ -77,6 +95,10 @@ struct BwdArgs {
   float sl2;    // log2(e) / sqrt(D)
   float scale;  // 1 / sqrt(D)
   int pattern;  // ST_* (host side: selects the kernels)
+  int out_mode;  // OutMode
+  float* carry_dq;  // merged heads: [B*H*T*D] first-pass gradients (fp32)
+  float* carry_dk;
+  float* carry_dv;
 };
 
 // Kernel ids for the optional launch timing (names in kKernelNames).

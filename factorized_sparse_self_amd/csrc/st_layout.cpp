@@ -37,12 +37,14 @@ bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g) {
     case ST_FIXED: g->code = kind ? K_SUMMARY : K_BLOCK; break;
     case ST_FIXED_R1: g->code = kind ? K_SUMMARY_R1 : K_BLOCK; break;
     case ST_DENSE: g->code = K_CAUSAL; break;
+    case ST_STRIDED_UNION: g->code = kind ? K_STRIDE_X : K_LOCAL; break;
+    case ST_FIXED_UNION: g->code = kind ? K_SUMMARY : K_BLOCK; break;
     default: return false;
   }
   g->n_rows = T;
   g->n_keys = T;
   const int nb = (T + l - 1) / l;  // l-blocks, last one possibly short
-  if (g->code == K_STRIDE) {
+  if (g->code == K_STRIDE || g->code == K_STRIDE_X) {
     g->n_pad = (nb + kBlock - 1) / kBlock * kBlock;
     g->n_cls = l < T ? l : T;
     g->n_rows = g->n_cls * g->n_pad;
@@ -60,10 +62,10 @@ bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g) {
 }
 
 std::string check_pattern_args(int pattern, int T, int l, int c) {
-  if (pattern < ST_STRIDED || pattern > ST_DENSE) return "unknown pattern " + std::to_string(pattern);
+  if (pattern < ST_STRIDED || pattern > ST_FIXED_UNION) return "unknown pattern " + std::to_string(pattern);
   if (T < 1 || T > (1 << 24)) return "T must be in [1, 2^24], got " + std::to_string(T);
   if (l < 1 || l > (1 << 24)) return "l must be in [1, 2^24], got " + std::to_string(l);
-  if ((pattern == ST_FIXED || pattern == ST_FIXED_R1) && (c < 1 || c > l))
+  if ((pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION) && (c < 1 || c > l))
     return "c must be in [1, l] for the fixed patterns, got c=" + std::to_string(c) +
            " l=" + std::to_string(l);
   return std::string();
@@ -151,7 +153,7 @@ int st_layout_build(int pattern, int T, int l, int c, st_layout** out) {
   lay->pattern = pattern;
   lay->T = T;
   lay->l = l;
-  lay->c = (pattern == ST_FIXED || pattern == ST_FIXED_R1) ? c : 0;
+  lay->c = (pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION) ? c : 0;
   try {
     for (int kind = 0; kind < 2; ++kind) {
       make_geometry(pattern, kind, T, l, lay->c, &lay->kind[kind].geo);

@@ -18,8 +18,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-STRIDED, FIXED, FIXED_R1, DENSE = 0, 1, 2, 3
-PATTERN_NAMES = {STRIDED: "strided", FIXED: "fixed", FIXED_R1: "fixed_r1", DENSE: "dense"}
+STRIDED, FIXED, FIXED_R1, DENSE, STRIDED_UNION, FIXED_UNION = range(6)
+PATTERN_NAMES = {STRIDED: "strided", FIXED: "fixed", FIXED_R1: "fixed_r1", DENSE: "dense",
+                 STRIDED_UNION: "strided_union", FIXED_UNION: "fixed_union"}
 
 
 @dataclass(frozen=True)
@@ -61,7 +62,8 @@ WORKLOADS = [
 # Follow-up workloads: full causal attention at the fixed workload's shape (the
 # comparator of the pages' fixed-vs-full training-step timing), the summary
 # variant whose summary keys include the query's own block up to t, and a
-# million-length strided sequence.
+# million-length strided sequence, and merged heads (every head attends both
+# sets) at the 12,288-long shapes.
 EXTRA_WORKLOADS = [
     Workload("dense_T12288_bf16_fwdbwd", DENSE, 4, 8, 12288, 64, 128, 0, "bf16", True, 1005,
              note="full causal attention at the fixed workload's shape"),
@@ -69,6 +71,10 @@ EXTRA_WORKLOADS = [
              note="summary keys of earlier blocks and of the own block up to t"),
     Workload("strided_T1048576_bf16_fwdbwd", STRIDED, 1, 2, 1 << 20, 64, 1024, 0, "bf16", True, 1007,
              note="million-length sequence, one local and one strided head"),
+    Workload("fixed_union_T12288_bf16_fwdbwd", FIXED_UNION, 4, 8, 12288, 64, 128, 8, "bf16", True, 1008,
+             note="merged heads: own block plus earlier summary keys in every head"),
+    Workload("strided_union_T12288_bf16_fwdbwd", STRIDED_UNION, 1, 16, 12288, 64, 128, 0, "bf16", True, 1009,
+             note="merged heads: window plus strided keys in every head"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

@@ -22,6 +22,15 @@
  *     positions j <= t (the reading of the llm-arch-kb §3 mask sketch).
  *   ST_DENSE: full causal attention, S(t) = {j <= t}, for both kinds (the
  *     dense comparator of nlp-lineage "The notation").
+ *   ST_STRIDED_UNION, ST_FIXED_UNION: merged heads -- every head attends the
+ *     union of the pattern's two sets (llm-arch-kb §2 states each pattern as
+ *     that union; its §3 mask sketch builds one mask from both loops).  The
+ *     library computes it as two passes over every head, one per kind: the
+ *     first keeps fp32 partial results in the workspace, the second merges
+ *     its own into them (the two softmaxes by their log-sum-exps, gradients
+ *     by addition).  For that split the strided pass leaves out t itself
+ *     (already in the window); the fixed sets are disjoint.  bf16 only: the
+ *     _f32 attention entry points return ST_ERR_UNSUPPORTED for them.
  *
  * Conventions (readings where the pages are silent):
  *   - positions are 0-based; T need not be a multiple of l;
@@ -38,13 +47,15 @@
  * Ownership.  All tensor pointers are device pointers owned by the caller;
  * the library never frees them or keeps them past the call.  The library owns
  * a per-device cache of block LUTs and work schedules and a per-device
- * backward workspace, both grown on demand and freed by st_release().
+ * workspace (backward scratch; for merged heads also the fp32 partial results
+ * the second pass adds to), both grown on demand and freed by st_release().
  *
  * Asynchrony.  The attention entry points enqueue kernels on `stream` (a
  * hipStream_t; NULL means the default stream) and return without waiting.
  * A call that has to build a LUT or grow the workspace performs blocking
- * host-to-device copies or allocations first.  Backward calls that overlap in
- * time on one device share the workspace and race; serialise them.
+ * host-to-device copies or allocations first.  Calls that use the workspace
+ * (every backward call; forward calls with a merged-head pattern) and overlap
+ * in time on one device share it and race; serialise them.
  *
  * Errors.  Every entry point returns ST_OK (0) or a negative st_status; no
  * C++ exception crosses the ABI.  The message of the last failure on the
@@ -72,7 +83,9 @@ typedef enum st_pattern {
   ST_STRIDED = 0,
   ST_FIXED = 1,
   ST_FIXED_R1 = 2,
-  ST_DENSE = 3
+  ST_DENSE = 3,
+  ST_STRIDED_UNION = 4,
+  ST_FIXED_UNION = 5
 } st_pattern;
 
 /* ---------------------------------------------------------------------------
@@ -92,6 +105,8 @@ typedef enum st_pattern {
  *   - ST_FIXED kind 1, compact summary keys: key b*c + o holds position
  *     b*l + (l-c) + o for blocks b < ceil(T/l) - 1 (ST_FIXED_R1: all blocks,
  *     positions >= T are padding); rows are the identity.
+ *   - merged heads: kind p is the p-th pass, with the maps of the base
+ *     pattern's kind p; the LUT of the strided pass omits the row's own key.
  * In these coordinates every row attends one contiguous run of kernel keys.
  * A (row block, key block) pair is listed when it holds at least one
  * attended pair; its flag is 1 (FULL) when all block*block pairs are

@@ -10,7 +10,7 @@
 using namespace st;
 
 int main() {
-  const int patterns[] = {ST_STRIDED, ST_FIXED, ST_FIXED_R1, ST_DENSE};
+  const int patterns[] = {ST_STRIDED, ST_FIXED, ST_FIXED_R1, ST_DENSE, ST_STRIDED_UNION, ST_FIXED_UNION};
   const int Ts[] = {1, 5, 63, 64, 65, 200, 250, 1000, 1024, 4099};
   const int ls[] = {1, 2, 3, 7, 16, 20, 64, 96, 128, 300};
   long checked = 0;
@@ -63,7 +63,7 @@ int main() {
                 ++checked;
               }
           }
-          if (pattern != ST_FIXED && pattern != ST_FIXED_R1) break;
+          if (pattern != ST_FIXED && pattern != ST_FIXED_R1 && pattern != ST_FIXED_UNION) break;
         }
   std::printf("ok %ld\n", checked);
   return 0;

@@ -66,6 +66,17 @@ def test_attention_argument_errors_without_gpu(name):
     assert _call_fwd(name, fake, D=48) == -2
     assert _call_fwd(name, fake, D=128) == -2
     assert b"D must be 32 or 64" in lib().st_last_error()
+    assert _call_fwd(name, fake, pattern=5, c=0) == -1   # merged fixed heads need c too
+
+
+def test_merged_heads_have_no_fp32_path():
+    from factorized_sparse_self_amd import ST_FIXED_UNION, ST_STRIDED_UNION, lib
+    L = lib()
+    fake = 1 << 20
+    for pattern, c in ((ST_STRIDED_UNION, 0), (ST_FIXED_UNION, 2)):
+        assert _call_fwd("st_sparse_attn_fwd_f32", fake, pattern=pattern, c=c) == -2
+        assert b"no fp32 path" in L.st_last_error()
+        assert L.st_sparse_attn_bwd_f32(*([fake] * 9), 1, 2, 64, 64, pattern, 8, c, None) == -2
 
 
 def test_backward_argument_errors_without_gpu():

@@ -119,6 +119,42 @@ def test_small_forward_backward(case, dtype):
     assert_close(f64(dv), rv, dtype, "dv")
 
 
+# Merged heads (every head attends both sets): bf16 only
+SMALL_UNION = [
+    (inputs.STRIDED_UNION, 2, 3, 300, 64, 16, 0),
+    (inputs.STRIDED_UNION, 1, 2, 333, 32, 20, 0),
+    (inputs.STRIDED_UNION, 1, 2, 200, 64, 7, 0),
+    (inputs.STRIDED_UNION, 1, 2, 190, 64, 96, 0),
+    (inputs.STRIDED_UNION, 1, 2, 130, 64, 1, 0),
+    (inputs.STRIDED_UNION, 1, 3, 10, 64, 16, 0),
+    (inputs.STRIDED_UNION, 1, 1, 1, 64, 4, 0),
+    (inputs.FIXED_UNION, 2, 3, 300, 64, 16, 3),
+    (inputs.FIXED_UNION, 1, 2, 333, 32, 20, 20),
+    (inputs.FIXED_UNION, 1, 2, 250, 64, 64, 4),
+    (inputs.FIXED_UNION, 1, 2, 260, 64, 5, 1),
+    (inputs.FIXED_UNION, 1, 3, 10, 64, 16, 3),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_UNION, ids=lambda c: f"p{c[0]}_B{c[1]}H{c[2]}T{c[3]}D{c[4]}l{c[5]}c{c[6]}")
+def test_small_merged_heads(case):
+    pattern, B, H, T, D, l, c = case
+    log(f"small merged heads fwd+bwd {case}")
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=17 + T + l, n=4)
+    out, lse = run_fwd(q, k, v, pattern, l, c)
+    qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
+    O, L = oracle.forward(qn, kn, vn, pattern, l, c)
+    assert_close(f64(out), O, "bf16", "out")
+    assert_close(f64(lse), L, "f32", "lse")
+    # position 0 attends only itself in both sets: out == v exactly
+    assert torch.equal(out[:, :, 0].cpu(), v[:, :, 0])
+    dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+    assert_close(f64(dq), rq, "bf16", "dq")
+    assert_close(f64(dk), rk, "bf16", "dk")
+    assert_close(f64(dv), rv, "bf16", "dv")
+
+
 def test_edge_shapes():
     """T = 1, T < l, l = 1, c = l, a single row block, odd H."""
     cases = [
@@ -223,6 +259,13 @@ def _keys_for_head(w, kind, n, seed):
         nb = -(-w.T // w.l)
         blocks = sorted({0, 1, nb // 2, nb - 2} | set(int(b) for b in rng.integers(0, nb - 1, size=2)))
         return np.array([b * w.l + w.l - w.c + int(rng.integers(0, w.c)) for b in blocks], dtype=np.int64)
+    if w.pattern == inputs.FIXED_UNION:
+        # summary positions (attended by their own block and every later one),
+        # other positions, and the last block's summary positions
+        nb = -(-w.T // w.l)
+        keys = {b * w.l + w.l - w.c + int(rng.integers(0, w.c)) for b in (0, 1, nb // 2, nb - 2, nb - 1)}
+        keys |= set(int(x) for x in rng.choice(w.T, size=n // 2, replace=False)) | {0, w.T - 1}
+        return np.array(sorted(k for k in keys if k < w.T), dtype=np.int64)
     if w.pattern == inputs.DENSE:
         # every later query attends key j, and the oracle recomputes each of them in
         # full, so the dense keys come from the last 512 positions (up to 512

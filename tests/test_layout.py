@@ -21,6 +21,9 @@ CASES = [(w.pattern, w.T, w.l, w.c) for w in inputs.WORKLOADS] + [
     (inputs.STRIDED, 100, 128, 0), (inputs.FIXED, 60, 64, 4), (inputs.FIXED, 1, 1, 1),
     (inputs.STRIDED, 1, 5, 0), (inputs.STRIDED, 129, 1, 0), (inputs.FIXED_R1, 250, 16, 3),
     (inputs.FIXED_R1, 1024, 32, 4), (inputs.DENSE, 300, 16, 0), (inputs.STRIDED, 1000, 96, 0),
+    (inputs.STRIDED_UNION, 250, 16, 0), (inputs.STRIDED_UNION, 12288, 128, 0), (inputs.STRIDED_UNION, 129, 1, 0),
+    (inputs.STRIDED_UNION, 1, 5, 0), (inputs.STRIDED_UNION, 1000, 96, 0), (inputs.FIXED_UNION, 250, 16, 3),
+    (inputs.FIXED_UNION, 12288, 128, 8), (inputs.FIXED_UNION, 333, 20, 20), (inputs.FIXED_UNION, 1, 1, 1),
 ]
 
 
