@@ -39,8 +39,8 @@ struct PlanKey {
 // which each head has its own kind; a merged head runs pass p over every head
 // with kind p.
 struct PassItems {
-  RowItem* row_items = nullptr;   // row blocks: fp32 forward, dq
-  RowItem* pair_items = nullptr;  // row-block pairs: bf16 forward
+  RowItem* row_items = nullptr;    // row blocks: fp32 forward and dq
+  PairItem* pair_items = nullptr;  // row-block pairs: bf16 forward and dq
   DkdvItem* dkdv_items = nullptr;
   ReduceItem* red_items = nullptr;
   int n_row_items = 0, n_pair_items = 0, n_dkdv_items = 0, n_red_items = 0;
@@ -162,7 +162,8 @@ int build_plan(const PlanKey& key, Plan* plan) {
   // kind of head bh in pass p
   auto kind_of = [&](int p, int bh) { return merged ? p : (bh % key.H) & 1; };
   struct HostPass {
-    std::vector<RowItem> rows, pairs;
+    std::vector<RowItem> rows;
+    std::vector<PairItem> pairs;
     std::vector<DkdvItem> dkdv;
     std::vector<ReduceItem> red;
   } hp[2];
@@ -183,19 +184,21 @@ int build_plan(const PlanKey& key, Plan* plan) {
     }
     for (int i : xcd_order(rcost, rgroup)) hp[p].rows.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : rows[i]);
 
-    // Row-block pair items (bf16 forward).
-    std::vector<RowItem> pairs;
+    // Row-block pair items (bf16 forward and dq).
+    std::vector<PairItem> pairs;
     std::vector<int64_t> pcost, pgroup;
     for (int bh = 0; bh < BH; ++bh) {
       const int kind = kind_of(p, bh);
       const int n_pairs = (int)pair_ptr[kind].size() - 1;
       for (int pb = 0; pb < n_pairs; ++pb) {
-        pairs.push_back({pb, bh, kind, 0});
-        pcost.push_back(pair_ptr[kind][pb + 1] - pair_ptr[kind][pb] + 1);
+        const int e0 = pair_ptr[kind][pb], e1 = pair_ptr[kind][pb + 1];
+        pairs.push_back({pb, bh, kind, e0, e1, e1 > e0 ? pair_entry[kind][e0] : 0u, 0, 0});
+        pcost.push_back(e1 - e0 + 1);
         pgroup.push_back((int64_t)bh * 65536 + 2 * pb / chunk[kind]);
       }
     }
-    for (int i : xcd_order(pcost, pgroup)) hp[p].pairs.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : pairs[i]);
+    for (int i : xcd_order(pcost, pgroup))
+      hp[p].pairs.push_back(i < 0 ? PairItem{-1, -1, 0, 0, 0, 0u, 0, 0} : pairs[i]);
 
     // dK/dV items: every key block of every head.  A key block whose row-block
     // list is longer than kDkdvSplit is split at row-block multiples of
@@ -256,7 +259,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   size_t off_items[2][4];
   for (int p = 0; p < n_pass; ++p) {
     off_items[p][0] = blob.add(hp[p].rows.data(), hp[p].rows.size() * sizeof(RowItem));
-    off_items[p][1] = blob.add(hp[p].pairs.data(), hp[p].pairs.size() * sizeof(RowItem));
+    off_items[p][1] = blob.add(hp[p].pairs.data(), hp[p].pairs.size() * sizeof(PairItem));
     off_items[p][2] = blob.add(hp[p].dkdv.data(), hp[p].dkdv.size() * sizeof(DkdvItem));
     off_items[p][3] = blob.add(hp[p].red.data(), hp[p].red.size() * sizeof(ReduceItem));
   }
@@ -291,7 +294,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   for (int p = 0; p < n_pass; ++p) {
     PassItems& P = plan->pass[p];
     P.row_items = (RowItem*)(dbase + off_items[p][0]);
-    P.pair_items = (RowItem*)(dbase + off_items[p][1]);
+    P.pair_items = (PairItem*)(dbase + off_items[p][1]);
     P.dkdv_items = (DkdvItem*)(dbase + off_items[p][2]);
     P.red_items = (ReduceItem*)(dbase + off_items[p][3]);
     P.n_row_items = (int)hp[p].rows.size();
@@ -426,7 +429,8 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   for (int p = 0; p < plan->n_pass; ++p) {
     const PassItems& P = plan->pass[p];
     // bf16: one workgroup per pair of row blocks; fp32: per row block
-    a.items = kBf16 ? P.pair_items : P.row_items;
+    a.items = P.row_items;
+    a.pairs = P.pair_items;
     const int n_items = kBf16 ? P.n_pair_items : P.n_row_items;
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
     e = (D == 32) ? launch_fwd<TE, 32>(a, n_items, s) : launch_fwd<TE, 64>(a, n_items, s);
@@ -492,11 +496,14 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   for (int p = 0; p < plan->n_pass; ++p) {
     const PassItems& P = plan->pass[p];
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
+    // bf16 dq: one workgroup per pair of row blocks; fp32: per row block
     a.dq_items = P.row_items;
+    a.dq_pairs = P.pair_items;
+    const int n_dq = std::is_same<TE, bf16>::value ? P.n_pair_items : P.n_row_items;
     a.dkdv_items = P.dkdv_items;
     a.red_items = P.red_items;
-    e = (D == 32) ? launch_bwd<TE, 32>(a, P.n_row_items, P.n_dkdv_items, P.n_red_items, s)
-                  : launch_bwd<TE, 64>(a, P.n_row_items, P.n_dkdv_items, P.n_red_items, s);
+    e = (D == 32) ? launch_bwd<TE, 32>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
+                  : launch_bwd<TE, 64>(a, n_dq, P.n_dkdv_items, P.n_red_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ST_OK;

@@ -399,13 +399,23 @@ __device__ __forceinline__ int key_out_mode(const BwdArgs& a, int p) {
 // without masks; every transposed MFMA operand (K^T, Q^T, dO^T) comes from
 // LDS transpose reads.
 // ---------------------------------------------------------------------------
+// dq: a work item is a pair of 64-row blocks (LUT blocks 2pb and 2pb+1) and
+// the union of their key-block lists; eight waves, 16 rows each (waves 0-3 the
+// first block, 4-7 the second).  Every K and V block is staged once for both
+// row blocks; a wave skips (uniformly) the blocks its own row block does not
+// visit.
 template <int D, int NS, int KC>
-__device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int bh, int kind,
+__device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairItem& item,
                                                  unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
   constexpr int NQ = D / 32, ND = D / 16, CH = D / 8;
-  constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
-  const KindDev kd = load_uniform(&a.kinds[kind]);
+  constexpr int NW = kDqThreads / 64;  // waves
+  // staging: SW waves each stage SR rows of every tile (SNI instructions)
+  constexpr int SR = S::RPI <= kBlock / NW ? kBlock / NW : S::RPI;
+  constexpr int SW = kBlock / SR, SNI = SR / S::RPI;
+  constexpr int PER_TILE = 2 * SNI;  // loads per staging wave per block (K and V)
+  const int bh = item.bh;
+  const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
@@ -417,29 +427,34 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const StageRows<S::NI, S::RPI> stage(g, true, 16 * wave + lane / S::CH);
-  const cptr<uint32_t> entries = as_const(kd.csr_entry);
-  // LDS address of this wave's 16 rows in stage 0's K tile (V follows at
+  const int half = wave >> 2, sub = wave & 3;  // row block 2pb + half, rows 16 sub + li
+  const int qb = 2 * item.pb + half;
+  const bool stager = wave % (NW / SW) == 0;
+  const int swave = wave / (NW / SW);
+  const StageRows<SNI, S::RPI> stage(g, true, SR * swave + lane / S::CH);
+  const cptr<uint32_t> entries = as_const(kd.pair_entry);
+  // LDS address of this wave's staging rows in stage 0's K tile (V follows at
   // +BYTES, stage s at +s*STAGE)
   constexpr uint32_t STAGE = 2 * S::BYTES;
-  const uint32_t lds_rows = lds_address(&ring[0][0][16 * wave * S::RB]);
-  auto issue = [&](int e, int stg) {
-    int p[S::NI];
-    stage.positions(g, true, (int)(entries[e] & ~kFullBit), p);
+  const uint32_t lds_rows = lds_address(&ring[0][0][SR * swave * S::RB]);
+  auto issue = [&](uint32_t entry, int stg) {
+    if (!stager) return;
+    int p[SNI];
+    stage.positions(g, true, (int)(entry & kPairBlockMask), p);
     stage_rows<D>(rk, lds_rows + stg * STAGE, lane, p);
     stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, lane, p);
   };
-  // The first NS-1 key blocks are in flight while the row's own operands load
+  // The first NS-1 key blocks are in flight while the rows' own operands load
   // (those loads are younger, so the compiler's waits for them cover the ring's
   // first blocks too, and no compiler wait lands inside the loop).
-  const int e0 = as_const(kd.row_ptr)[qb], e1 = as_const(kd.row_ptr)[qb + 1];
+  const int e0 = item.e0, e1 = item.e1;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (e0 + j < e1) issue(e0 + j, j);
+    if (e0 + j < e1) issue(j == 0 ? item.first : entries[e0 + j], j);
 
-  const int t = block_position(g, false, qb, wave * 16 + li);
+  const int t = block_position(g, false, qb, sub * 16 + li);
   int lo = 1, hi = 0;
-  if (t >= 0) row_interval(g, qb * kBlock + wave * 16 + li, t, lo, hi);
+  if (t >= 0) row_interval(g, qb * kBlock + sub * 16 + li, t, lo, hi);
   const bool row_live = lo <= hi;
   const int mlo = row_live ? lo : -(1 << 30);
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
@@ -457,40 +472,17 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
 #pragma unroll
     for (int i = 0; i < 8; ++i) dpart = fmaf((float)gop[s][i], (float)o8[i], dpart);
   }
-  const float delta_row = group4_sum(dpart);
-  float lse2 = 0.f, delta = 0.f;
-  if (row_live) {
-    lse2 = buf_load_f32(make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4), (uint32_t)t * 4) * kLog2e;
-    delta = delta_row;
-  }
-  // Delta and lse*log2(e) of every row, for the dk/dv pass that follows (the
-  // first pass of a merged head writes them for every row; its second pass
-  // holds rows that attend nothing, whose values it would zero)
-  if (t >= 0 && lg == 0 && a.out_mode != OUT_MERGE) {
-    a.delta[(size_t)bh * a.T + t] = delta_row;
-    a.lse2[(size_t)bh * a.T + t] = lse2;
-  }
-  // keys nobody attends (positions outside a summary head's key map) get
-  // dk = dv = 0; the row positions of this block cover every such position
-  // (in a merged head the first pass writes them)
-  if constexpr (KC == K_SUMMARY || KC == K_SUMMARY_R1) {
-    if (a.out_mode == OUT_FINAL)
-      for (int u = tid; u < kBlock * CH; u += kThreads) {
-        const int r = u / CH, ch = u % CH;
-        const int tp = block_position(g, false, qb, r);
-        if (tp >= 0 && !position_is_key(g, tp)) {
-          const uint4 z = {0, 0, 0, 0};
-          *(uint4*)((bf16*)a.dk + base + (size_t)tp * D + ch * 8) = z;
-          *(uint4*)((bf16*)a.dv + base + (size_t)tp * D + ch * 8) = z;
-        }
-      }
-  }
-  // per-lane byte offsets of the MFMA operand reads inside a staged block
-  int a_off[NQ], t_off[ND];
-#pragma unroll
-  for (int k = 0; k < NQ; ++k) a_off[k] = S::phys(li, 4 * k + lg);
-#pragma unroll
-  for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
+  // (rows that attend nothing get 0: no pass reads them)
+  const float delta = row_live ? group4_sum(dpart) : 0.f;
+  const float lse2 =
+      row_live ? buf_load_f32(make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4), (uint32_t)t * 4) * kLog2e
+               : 0.f;
+  // per-lane byte offsets of the MFMA operand reads inside a staged block:
+  // row operand k at a_off ^ (64 k) (chunk 4k + lg), transposed read d at
+  // t_off ^ (32 d) (chunk 2d + ...): the swizzle XORs only the chunk bits
+  static_assert(4 * (NQ - 1) < CH && 2 * (ND - 1) < CH, "operand chunks inside a row");
+  const int a_off = S::phys(li, lg);
+  const int t_off = S::phys(4 * lg + (li >> 2), (li & 3) >> 1) + 8 * (li & 1);
   f32x4 acc[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -498,12 +490,13 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
 
   // One code path for every block: PARTIAL blocks only add the mask.
   for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
-    const uint32_t entry = entries[e];
-    const int k0 = (int)(entry & ~kFullBit) * kBlock;
-    const bool full = (entry & kFullBit) != 0;
+    const uint32_t entry = e == e0 ? item.first : entries[e];
+    const int k0 = (int)(entry & kPairBlockMask) * kBlock;
+    const uint32_t hbits = (entry >> (28 + 2 * half)) & 3u;  // this row block's visit / FULL bits
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
     __syncthreads();
-    if (e + NS - 1 < e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
+    if (e + NS - 1 < e1) issue(entries[e + NS - 1], stg == 0 ? NS - 1 : stg - 1);
+    if (!(hbits & kPairVisit)) continue;  // the other row block's key block
     const unsigned char* Kt = ring[stg][0];
     const unsigned char* Vt = ring[stg][1];
     // S^T = K Q^T and dP^T = V dO^T
@@ -513,15 +506,15 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
       sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        sc[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]), qop[k], sc[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(Vt + 16 * b * S::RB + a_off[k]), gop[k], dp[b]);
+        sc[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + (a_off ^ (64 * k))), qop[k], sc[b]);
+        dp[b] = mfma_bf16(*(const bf16x8*)(Vt + 16 * b * S::RB + (a_off ^ (64 * k))), gop[k], dp[b]);
       }
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[b][i] = fast_exp2(fmaf(sc[b][i], sl2, -lse2));
-    if (!full) {
+    if (!(hbits & kPairFull)) {
       const int m0 = k0 + 4 * lg - mlo;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -539,13 +532,35 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
       const bf16x8 ds8 = pack_b_operand(sc[2 * kk], sc[2 * kk + 1]);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const unsigned char* r = Kt + 32 * kk * S::RB + t_off[d];
+        const unsigned char* r = Kt + 32 * kk * S::RB + (t_off ^ (32 * d));
         const bf16x8 ak = concat(lds_read_tr((const bf16*)r), lds_read_tr((const bf16*)(r + 16 * S::RB)));
         acc[d] = mfma_bf16(ak, ds8, acc[d]);
       }
     }
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
+  // Delta and lse*log2(e) of every row, for the dk/dv pass that follows (the
+  // first pass of a merged head writes them for every row; its second pass
+  // holds rows that attend nothing, whose values it would zero)
+  if (t >= 0 && lg == 0 && a.out_mode != OUT_MERGE) {
+    a.delta[(size_t)bh * a.T + t] = delta;
+    a.lse2[(size_t)bh * a.T + t] = lse2;
+  }
+  // keys nobody attends (positions outside a summary head's key map) get
+  // dk = dv = 0; each row block's positions cover every such position
+  // (in a merged head the first pass writes them)
+  if constexpr (KC == K_SUMMARY || KC == K_SUMMARY_R1) {
+    if (a.out_mode == OUT_FINAL)
+      for (int u = tid & 255; u < kBlock * CH; u += 256) {
+        const int r = u / CH, ch = u % CH;
+        const int tp = block_position(g, false, qb, r);
+        if (tp >= 0 && !position_is_key(g, tp)) {
+          const uint4 z = {0, 0, 0, 0};
+          *(uint4*)((bf16*)a.dk + base + (size_t)tp * D + ch * 8) = z;
+          *(uint4*)((bf16*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+        }
+      }
+  }
   if (t < 0) return;
   store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
                      (bf16*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
@@ -553,14 +568,14 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, int qb, int b
 
 // One kernel per pattern; each workgroup branches once on its head's kind.
 template <int D, int NS, int C0, int C1>
-__global__ __launch_bounds__(kThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
-  const RowItem item = load_uniform(&a.dq_items[blockIdx.x]);
-  if (item.qb < 0) return;  // schedule padding
+  const PairItem item = load_uniform(&a.dq_pairs[blockIdx.x]);
+  if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    bwd_dq_bf16_body<D, NS, C0>(a, item.qb, item.bh, 0, ring);
+    bwd_dq_bf16_body<D, NS, C0>(a, item, ring);
   else
-    bwd_dq_bf16_body<D, NS, C1>(a, item.qb, item.bh, 1, ring);
+    bwd_dq_bf16_body<D, NS, C1>(a, item, ring);
 }
 
 // dk/dv: Q and dO blocks with their lse*log2(e) and Delta are staged by
@@ -818,7 +833,7 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
     if constexpr (IsBf16<TE>::value) {
       err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
         hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kDqStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_dq),
-                           dim3(kThreads), 0, stream, a);
+                           dim3(kDqThreads), 0, stream, a);
         return hipGetLastError();
       });
     } else {

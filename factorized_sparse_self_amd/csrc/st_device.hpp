@@ -28,7 +28,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kThreads = 256;  // 4 waves per workgroup
+constexpr int kThreads = 256;    // 4 waves per workgroup
+constexpr int kDqThreads = 512;  // bf16 dq: 8 waves, 16 rows each of a pair of row blocks
 
 template <typename TE>
 struct IsBf16 {

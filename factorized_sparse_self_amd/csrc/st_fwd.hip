@@ -200,13 +200,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 //    lane of the wave needs that skip the cross-lane max and the rescale.
 // ---------------------------------------------------------------------------
 template <int D, int NS, int KC, bool M>
-__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, int kind,
+__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& item,
                                               unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
   constexpr int NQ = D / 32;           // MFMA k-steps over D
   constexpr int ND = D / 16;           // 16-wide output column blocks
   constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
-  const KindDev kd = load_uniform(&a.kinds[kind]);
+  const int pb = item.pb, bh = item.bh;
+  const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
@@ -258,15 +259,14 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, 
   // at +BYTES, stage s at +s*STAGE)
   constexpr uint32_t STAGE = 2 * S::BYTES;
   const uint32_t lds_rows = lds_address(&ring[0][0][16 * wave * S::RB]);
-  auto issue = [&](int e, int stg) {
+  auto issue = [&](uint32_t entry, int stg) {
     int p[S::NI];
-    stage.positions(g, true, (int)(entries[e] & kPairBlockMask), p);
+    stage.positions(g, true, (int)(entry & kPairBlockMask), p);
     stage_rows<D>(rk, lds_rows + stg * STAGE, lane, p);
     stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, lane, p);
   };
 
-  const cptr<int32_t> pair_ptr = as_const(kd.pair_ptr);
-  const int e0 = pair_ptr[pb], e1 = pair_ptr[pb + 1];
+  const int e0 = item.e0, e1 = item.e1;
   // The two row blocks' Q rows go through the last ring stage (free until the
   // first iteration refills it: row block 2pb in the K tile, 2pb+1 in the V
   // tile), ahead of the first NS-1 key blocks, so every global load of the
@@ -282,9 +282,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, 
   }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (e0 + j < e1) issue(e0 + j, j);
+    if (e0 + j < e1) issue(j == 0 ? item.first : entries[e0 + j], j);
   for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
-    const uint32_t entry = entries[e];
+    const uint32_t entry = e == e0 ? item.first : entries[e];
     const int k0 = (int)(entry & kPairBlockMask) * kBlock;
     const uint32_t hbits = (entry >> (28 + 2 * half)) & 3u;  // this row block's visit / FULL bits
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
@@ -301,7 +301,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, 
       wait_lgkmcnt0();
       __syncthreads();
     }
-    if (e + NS - 1 < e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
+    if (e + NS - 1 < e1) issue(entries[e + NS - 1], stg == 0 ? NS - 1 : stg - 1);
     if (!(hbits & kPairVisit)) continue;  // the other row block's key block
     const unsigned char* Kt = ring[stg][0];
     const unsigned char* Vt = ring[stg][1];
@@ -435,12 +435,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, int pb, int bh, 
 template <int D, int NS, int C0, int C1, bool M>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
-  const RowItem item = load_uniform(&a.items[blockIdx.x]);
-  if (item.qb < 0) return;  // schedule padding
+  const PairItem item = load_uniform(&a.pairs[blockIdx.x]);
+  if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    fwd_bf16_body<D, NS, C0, M>(a, item.qb, item.bh, 0, ring);  // item.qb: pair of row blocks
+    fwd_bf16_body<D, NS, C0, M>(a, item, ring);
   else
-    fwd_bf16_body<D, NS, C1, M>(a, item.qb, item.bh, 1, ring);
+    fwd_bf16_body<D, NS, C1, M>(a, item, ring);
 }
 
 template <typename TE, int D>

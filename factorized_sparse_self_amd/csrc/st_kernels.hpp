@@ -53,6 +53,16 @@ struct RowItem {
   int qb, bh, kind, pad;
 };
 
+// Work item of the bf16 forward and dq passes: the pair of 64-row LUT blocks
+// 2pb and 2pb+1 of head bh (head kind `kind`).  Its key-block list is the
+// kind's pair_entry[e0, e1); `first` repeats pair_entry[e0] (when e0 < e1) so
+// that the first tile load is issued without reading the list.
+struct PairItem {
+  int pb, bh, kind, e0, e1;
+  uint32_t first;
+  int pad0, pad1;
+};
+
 // Reduction of a split key block: partial slots [slot0, slot0 + nsplit).
 struct ReduceItem {
   int kb, bh, slot0, nsplit, kind, pad0, pad1, pad2;
@@ -66,7 +76,8 @@ struct FwdArgs {
   float* lse;
   int H, T;
   const KindDev* kinds;  // [2], device memory
-  const RowItem* items;
+  const RowItem* items;  // fp32 kernel: row blocks
+  const PairItem* pairs;  // bf16 kernel: row-block pairs
   float sl2;             // log2(e) / sqrt(D)
   int pattern;           // ST_* (host side: selects the kernel)
   int out_mode;          // OutMode
@@ -89,7 +100,8 @@ struct BwdArgs {
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
   const KindDev* kinds;
-  const RowItem* dq_items;
+  const RowItem* dq_items;   // fp32 dq: row blocks
+  const PairItem* dq_pairs;  // bf16 dq: row-block pairs
   const DkdvItem* dkdv_items;
   const ReduceItem* red_items;
   float sl2;    // log2(e) / sqrt(D)
