@@ -38,7 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MI355X_HBM_GBS = 8000.0        # HBM3E peak, GB/s
-MI355X_BF16_TFLOPS = 2500.0    # dense bf16 MFMA peak, TFLOP/s
+MI355X_BF16_TFLOPS = 2500.0    # dense bf16 (and fp16) MFMA peak, TFLOP/s
 MI355X_FP32_TFLOPS = 157.3     # dense fp32 MFMA peak, TFLOP/s
 
 
@@ -90,7 +90,7 @@ def accounting(w):
     """Per-kernel algorithmic bytes and useful FLOP for one step of workload w."""
     from factorized_sparse_self_amd import st_layout_build
     lay = st_layout_build(w.pattern, w.T, w.l, w.c)
-    E = 2 if w.dtype == "bf16" else 4
+    E = 4 if w.dtype == "f32" else 2
     row = w.D * E
     crow = w.D * 4  # fp32 carried row of a merged head
     by = {"fwd": 0, "bwd_pre": 0, "bwd_dq": 0, "bwd_dkdv": 0, "bwd_reduce": 0}
@@ -113,8 +113,8 @@ def accounting(w):
             pre = w.T * (2 * row + 4) + 2 * (w.T - keys) * row
             # dq: read q, dout, lse, Delta (active rows), k and v (keys); write dq (every row)
             dq = rows * (2 * row + 8) + 2 * keys * row + w.T * row
-            if w.dtype == "bf16":
-                # bf16 dq computes Delta itself: reads q, dout, lse (active rows), out (every
+            if w.dtype != "f32":
+                # the 16-bit dq computes Delta itself: reads q, dout, lse (active rows), out (every
                 # row), k and v (keys); writes dq (or its carried fp32 row, or reads that and
                 # writes dq), Delta and lse*log2(e) (every row, not in a merging pass) and
                 # the zero fill (plain heads)
@@ -372,7 +372,7 @@ def main():
     dur_s = kernels[dom]["avg_ms"] * 1e-3
     dom_bytes = acct["bytes"][dom] / kernels[dom]["launches_per_step"]
     dom_flops = acct["flops"][dom] / kernels[dom]["launches_per_step"]
-    peak_flops = MI355X_BF16_TFLOPS if w.dtype == "bf16" else MI355X_FP32_TFLOPS
+    peak_flops = MI355X_FP32_TFLOPS if w.dtype == "f32" else MI355X_BF16_TFLOPS
     ridge = peak_flops * 1e12 / (MI355X_HBM_GBS * 1e9)
     ai = dom_flops / dom_bytes if dom_bytes else float("inf")
     if ai < ridge:

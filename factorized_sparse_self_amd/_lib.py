@@ -30,8 +30,10 @@ _SIG = {
     "st_layout_csc": (_I, [_P, _I, _P, _P, _P]),
     "st_layout_free": (None, [_P]),
     "st_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "st_sparse_attn_fwd_f16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "st_sparse_attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "st_sparse_attn_bwd": (_I, [_P] * 9 + [_I] * 7 + [_P]),
+    "st_sparse_attn_bwd_f16": (_I, [_P] * 9 + [_I] * 7 + [_P]),
     "st_sparse_attn_bwd_f32": (_I, [_P] * 9 + [_I] * 7 + [_P]),
     "st_timing_enable": (_I, [_I]),
     "st_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
@@ -165,9 +167,11 @@ def _entry(dtype, base):
     import torch
     if dtype == torch.bfloat16:
         return base
+    if dtype == torch.float16:
+        return base + "_f16"
     if dtype == torch.float32:
         return base + "_f32"
-    raise TypeError("q, k, v must be bfloat16 or float32")
+    raise TypeError("q, k, v must be bfloat16, float16 or float32")
 
 
 def st_sparse_attn_fwd(q, k, v, pattern: int, l: int, c: int = 0, out=None, lse=None):

@@ -40,7 +40,7 @@ struct PlanKey {
 // with kind p.
 struct PassItems {
   RowItem* row_items = nullptr;    // row blocks: fp32 forward and dq
-  PairItem* pair_items = nullptr;  // row-block pairs: bf16 forward and dq
+  PairItem* pair_items = nullptr;  // row-block pairs: 16-bit forward and dq
   DkdvItem* dkdv_items = nullptr;
   ReduceItem* red_items = nullptr;
   int n_row_items = 0, n_pair_items = 0, n_dkdv_items = 0, n_red_items = 0;
@@ -184,7 +184,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
     }
     for (int i : xcd_order(rcost, rgroup)) hp[p].rows.push_back(i < 0 ? RowItem{-1, -1, 0, 0} : rows[i]);
 
-    // Row-block pair items (bf16 forward and dq).
+    // Row-block pair items (16-bit forward and dq).
     std::vector<PairItem> pairs;
     std::vector<int64_t> pcost, pgroup;
     for (int bh = 0; bh < BH; ++bh) {
@@ -375,9 +375,9 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
 
 bool uses_c(int pattern) { return pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION; }
 
-// Merged heads run bf16 only.
-int check_union_dtype(const char* fn, int pattern, bool bf16_path) {
-  if (is_union(pattern) && !bf16_path) {
+// Merged heads run on the 16-bit paths only.
+int check_union_dtype(const char* fn, int pattern, bool path16) {
+  if (is_union(pattern) && !path16) {
     set_error(std::string(fn) + ": merged-head patterns have no fp32 path");
     return ST_ERR_UNSUPPORTED;
   }
@@ -390,8 +390,8 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   const void* ptrs[] = {q, k, v, out, lse};
   int rc = check_attn_args(fn, ptrs, 5, B, H, T, D, pattern, l, c);
   if (rc != ST_OK) return rc;
-  constexpr bool kBf16 = std::is_same<TE, bf16>::value;
-  rc = check_union_dtype(fn, pattern, kBf16);
+  constexpr bool k16 = Is16<TE>::value;
+  rc = check_union_dtype(fn, pattern, k16);
   if (rc != ST_OK) return rc;
   if (!uses_c(pattern)) c = 0;
   int device = 0;
@@ -428,10 +428,10 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   hipStream_t s = (hipStream_t)stream;
   for (int p = 0; p < plan->n_pass; ++p) {
     const PassItems& P = plan->pass[p];
-    // bf16: one workgroup per pair of row blocks; fp32: per row block
+    // 16-bit: one workgroup per pair of row blocks; fp32: per row block
     a.items = P.row_items;
     a.pairs = P.pair_items;
-    const int n_items = kBf16 ? P.n_pair_items : P.n_row_items;
+    const int n_items = k16 ? P.n_pair_items : P.n_row_items;
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
     e = (D == 32) ? launch_fwd<TE, 32>(a, n_items, s) : launch_fwd<TE, 64>(a, n_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
@@ -446,7 +446,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
   int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c);
   if (rc != ST_OK) return rc;
-  rc = check_union_dtype(fn, pattern, std::is_same<TE, bf16>::value);
+  rc = check_union_dtype(fn, pattern, Is16<TE>::value);
   if (rc != ST_OK) return rc;
   if (!uses_c(pattern)) c = 0;
   int device = 0;
@@ -496,10 +496,10 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   for (int p = 0; p < plan->n_pass; ++p) {
     const PassItems& P = plan->pass[p];
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
-    // bf16 dq: one workgroup per pair of row blocks; fp32: per row block
+    // 16-bit dq: one workgroup per pair of row blocks; fp32: per row block
     a.dq_items = P.row_items;
     a.dq_pairs = P.pair_items;
-    const int n_dq = std::is_same<TE, bf16>::value ? P.n_pair_items : P.n_row_items;
+    const int n_dq = Is16<TE>::value ? P.n_pair_items : P.n_row_items;
     a.dkdv_items = P.dkdv_items;
     a.red_items = P.red_items;
     e = (D == 32) ? launch_bwd<TE, 32>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
@@ -588,6 +588,11 @@ int st_sparse_attn_fwd(const void* q, const void* k, const void* v, void* out, f
   return attn_fwd<bf16>("st_sparse_attn_fwd", q, k, v, out, lse, B, H, T, D, pattern, l, c, stream);
 }
 
+int st_sparse_attn_fwd_f16(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                           int H, int T, int D, int pattern, int l, int c, void* stream) {
+  return attn_fwd<f16>("st_sparse_attn_fwd_f16", q, k, v, out, lse, B, H, T, D, pattern, l, c, stream);
+}
+
 int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_fwd<float>("st_sparse_attn_fwd_f32", q, k, v, out, lse, B, H, T, D, pattern, l, c,
@@ -599,6 +604,13 @@ int st_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_bwd<bf16>("st_sparse_attn_bwd", q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D,
                         pattern, l, c, stream);
+}
+
+int st_sparse_attn_bwd_f16(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                           int H, int T, int D, int pattern, int l, int c, void* stream) {
+  return attn_bwd<f16>("st_sparse_attn_bwd_f16", q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D,
+                       pattern, l, c, stream);
 }
 
 int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const void* out,

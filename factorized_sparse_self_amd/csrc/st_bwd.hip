@@ -7,12 +7,13 @@
 //   dp_tj = dO_t . v_j,        ds_tj = p_tj (dp_tj - Delta_t),
 //   dq_t = sum_j ds_tj k_j / sqrt(D),  dk_j = sum_t ds_tj q_t / sqrt(D),
 //   dv_j = sum_t p_tj dO_t.
-// In the bf16 kernels P and dS enter the dV, dK and dQ products as bf16 (fp32
-// accumulation); their rounding is well inside the bf16 output tolerance,
-// which the rounding of the stored output O (through Delta) dominates.
+// In the 16-bit kernels (bf16 or fp16 inputs) P and dS enter the dV, dK and
+// dQ products in the input's type (fp32 accumulation); their rounding is well
+// inside the output tolerance, which the rounding of the stored output O
+// (through Delta) dominates.
 // Kernels (one stream, in order):
 //   pre   Delta for every row; zero dk / dv at positions no query attends
-//         (fp32 only: the bf16 dq kernel does both for its own rows)
+//         (fp32 only: the 16-bit dq kernel does both for its own rows)
 //   dq    per row block over the CSR (no cross-item reduction)
 //   dkdv  per key block over the CSC; key blocks with many row blocks are
 //         split, each split writing fp32 partials
@@ -27,12 +28,12 @@ namespace st {
 
 namespace {
 
-// LDS ring stages of the bf16 dk/dv pass (row blocks in flight = stages - 1)
+// LDS ring stages of the 16-bit dk/dv pass (row blocks in flight = stages - 1)
 #ifndef ST_DKDV_STAGES
 #define ST_DKDV_STAGES 2
 #endif
 constexpr int kDkdvStages = ST_DKDV_STAGES;
-// LDS ring stages of the bf16 dq pass
+// LDS ring stages of the 16-bit dq pass
 #ifndef ST_DQ_STAGES
 #define ST_DQ_STAGES 2
 #endif
@@ -361,8 +362,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
 // `carry` point at its first element), scaled by `scale`, written as the
 // launch's OutMode says.
 // ---------------------------------------------------------------------------
-template <int ND>
-__device__ __forceinline__ void store_grad_row(int mode, float* carry, bf16* dst, const f32x4* x, float scale) {
+template <int ND, typename E>
+__device__ __forceinline__ void store_grad_row(int mode, float* carry, E* dst, const f32x4* x, float scale) {
   if (mode == OUT_CARRY) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
@@ -378,7 +379,7 @@ __device__ __forceinline__ void store_grad_row(int mode, float* carry, bf16* dst
       const float4 c = *(const float4*)(carry + 16 * d);
       y += (f32x4){c.x, c.y, c.z, c.w};
     }
-    *(bf16x4*)(dst + 16 * d) = to_bf16x4(y);
+    *(typename Vec<E>::x4*)(dst + 16 * d) = to_x4<E>(y);
   }
 }
 
@@ -392,7 +393,7 @@ __device__ __forceinline__ int key_out_mode(const BwdArgs& a, int p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 dq and dk/dv.  As in the forward: the streamed blocks (K and V for dq;
+// 16-bit dq and dk/dv.  As in the forward: the streamed blocks (K and V for dq;
 // Q and dO with their lse, Delta and key runs for dk/dv) go straight from
 // global memory into a ring of swizzled LDS stages (st_stage.hpp) with the
 // next blocks' loads in flight (padding rows read as zeros); FULL blocks run
@@ -404,10 +405,11 @@ __device__ __forceinline__ int key_out_mode(const BwdArgs& a, int p) {
 // first block, 4-7 the second).  Every K and V block is staged once for both
 // row blocks; a wave skips (uniformly) the blocks its own row block does not
 // visit.
-template <int D, int NS, int KC>
-__device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairItem& item,
-                                                 unsigned char (*ring)[2][TileShape<D>::BYTES]) {
+template <typename E, int D, int NS, int KC>
+__device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem& item,
+                                                unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
+  typedef typename Vec<E>::x8 V8;
   constexpr int NQ = D / 32, ND = D / 16, CH = D / 8;
   constexpr int NW = kDqThreads / 64;  // waves
   // staging: SW waves each stage SR rows of every tile (SNI instructions)
@@ -419,10 +421,10 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairIte
   const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
-  const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
-  const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
-  const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
-  const Rsrc rg = make_rsrc((const bf16*)a.dout + base, head_bytes);
+  const Rsrc rq = make_rsrc((const E*)a.q + base, head_bytes);
+  const Rsrc rk = make_rsrc((const E*)a.k + base, head_bytes);
+  const Rsrc rv = make_rsrc((const E*)a.v + base, head_bytes);
+  const Rsrc rg = make_rsrc((const E*)a.dout + base, head_bytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -460,15 +462,15 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairIte
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
   // Delta_t = dO_t . O_t: each of the row's four lanes holds a quarter of the
   // row of dO (the MFMA operand) and loads the same quarter of O
-  const Rsrc ro = make_rsrc((const bf16*)a.o + base, head_bytes);
-  bf16x8 qop[NQ], gop[NQ];
+  const Rsrc ro = make_rsrc((const E*)a.o + base, head_bytes);
+  V8 qop[NQ], gop[NQ];
   float dpart = 0.f;
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
     const uint32_t off = t >= 0 ? (uint32_t)(t * D + 32 * s + 8 * lg) * 2 : kOutOfRange;
-    qop[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-    gop[s] = __builtin_bit_cast(bf16x8, buf_load16(rg, off));
-    const bf16x8 o8 = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
+    qop[s] = __builtin_bit_cast(V8, buf_load16(rq, off));
+    gop[s] = __builtin_bit_cast(V8, buf_load16(rg, off));
+    const V8 o8 = __builtin_bit_cast(V8, buf_load16(ro, off));
 #pragma unroll
     for (int i = 0; i < 8; ++i) dpart = fmaf((float)gop[s][i], (float)o8[i], dpart);
   }
@@ -506,8 +508,8 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairIte
       sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        sc[b] = mfma_bf16(*(const bf16x8*)(Kt + 16 * b * S::RB + (a_off ^ (64 * k))), qop[k], sc[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(Vt + 16 * b * S::RB + (a_off ^ (64 * k))), gop[k], dp[b]);
+        sc[b] = mfma16(*(const V8*)(Kt + 16 * b * S::RB + (a_off ^ (64 * k))), qop[k], sc[b]);
+        dp[b] = mfma16(*(const V8*)(Vt + 16 * b * S::RB + (a_off ^ (64 * k))), gop[k], dp[b]);
       }
     }
 #pragma unroll
@@ -529,12 +531,12 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairIte
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 ds8 = pack_b_operand(sc[2 * kk], sc[2 * kk + 1]);
+      const V8 ds8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const unsigned char* r = Kt + 32 * kk * S::RB + (t_off ^ (32 * d));
-        const bf16x8 ak = concat(lds_read_tr((const bf16*)r), lds_read_tr((const bf16*)(r + 16 * S::RB)));
-        acc[d] = mfma_bf16(ak, ds8, acc[d]);
+        const V8 ak = concat(lds_read_tr<E>((const E*)r), lds_read_tr<E>((const E*)(r + 16 * S::RB)));
+        acc[d] = mfma16(ak, ds8, acc[d]);
       }
     }
   }
@@ -556,26 +558,26 @@ __device__ __forceinline__ void bwd_dq_bf16_body(const BwdArgs& a, const PairIte
         const int tp = block_position(g, false, qb, r);
         if (tp >= 0 && !position_is_key(g, tp)) {
           const uint4 z = {0, 0, 0, 0};
-          *(uint4*)((bf16*)a.dk + base + (size_t)tp * D + ch * 8) = z;
-          *(uint4*)((bf16*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+          *(uint4*)((E*)a.dk + base + (size_t)tp * D + ch * 8) = z;
+          *(uint4*)((E*)a.dv + base + (size_t)tp * D + ch * 8) = z;
         }
       }
   }
   if (t < 0) return;
   store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
-                     (bf16*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
+                     (E*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
 }
 
 // One kernel per pattern; each workgroup branches once on its head's kind.
-template <int D, int NS, int C0, int C1>
-__global__ __launch_bounds__(kDqThreads) void bwd_dq_bf16_kernel(BwdArgs a) {
+template <typename E, int D, int NS, int C0, int C1>
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_b16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
   const PairItem item = load_uniform(&a.dq_pairs[blockIdx.x]);
   if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    bwd_dq_bf16_body<D, NS, C0>(a, item, ring);
+    bwd_dq_b16_body<E, D, NS, C0>(a, item, ring);
   else
-    bwd_dq_bf16_body<D, NS, C1>(a, item, ring);
+    bwd_dq_b16_body<E, D, NS, C1>(a, item, ring);
 }
 
 // dk/dv: Q and dO blocks with their lse*log2(e) and Delta are staged by
@@ -592,10 +594,10 @@ struct DkdvStage {
   int span[kBlock];     // masking span (unsigned)
 };
 
-template <int D, int NS, int KC>
-__device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvItem& item,
-                                                   DkdvStage<D>* ring) {
+template <typename E, int D, int NS, int KC>
+__device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvItem& item, DkdvStage<D>* ring) {
   using S = TileShape<D>;
+  typedef typename Vec<E>::x8 V8;
   constexpr int NQ = D / 32, ND = D / 16;
   constexpr int PER_TILE = 2 * S::NI + 2;  // loads per wave per row block: Q, dO, lse2, Delta
   using Stage = DkdvStage<D>;
@@ -604,10 +606,10 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
   const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
-  const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
-  const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
-  const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
-  const Rsrc rg = make_rsrc((const bf16*)a.dout + base, head_bytes);
+  const Rsrc rq = make_rsrc((const E*)a.q + base, head_bytes);
+  const Rsrc rk = make_rsrc((const E*)a.k + base, head_bytes);
+  const Rsrc rv = make_rsrc((const E*)a.v + base, head_bytes);
+  const Rsrc rg = make_rsrc((const E*)a.dout + base, head_bytes);
   const Rsrc rl = make_rsrc(a.lse2 + (size_t)bh * a.T, (uint32_t)a.T * 4);
   const Rsrc rd = make_rsrc(a.delta + (size_t)bh * a.T, (uint32_t)a.T * 4);
 
@@ -616,7 +618,7 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
   const int Kw0 = kb * kBlock + wave * 16;
   const int Kl = Kw0 + li;
   const int kp = block_position(g, true, kb, wave * 16 + li);
-  bf16x8 kop[NQ], vop[NQ];  // this wave's 16 keys as MFMA B operands (from LDS, first block)
+  V8 kop[NQ], vop[NQ];  // this wave's 16 keys as MFMA B operands (from LDS, first block)
   int a_off[NQ], t_off[ND];
 #pragma unroll
   for (int k = 0; k < NQ; ++k) a_off[k] = S::phys(li, 4 * k + lg);
@@ -679,8 +681,8 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
       // this wave's 16 K/V rows (its own DMA, complete with the first block)
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        kop[k] = *(const bf16x8*)(ring[NS - 1].q + 16 * wave * S::RB + a_off[k]);
-        vop[k] = *(const bf16x8*)(ring[NS - 1].g + 16 * wave * S::RB + a_off[k]);
+        kop[k] = *(const V8*)(ring[NS - 1].q + 16 * wave * S::RB + a_off[k]);
+        vop[k] = *(const V8*)(ring[NS - 1].g + 16 * wave * S::RB + a_off[k]);
       }
       // the reads must land before the DMA below refills that stage
       wait_lgkmcnt0();
@@ -693,8 +695,8 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
       sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        sc[b] = mfma_bf16(*(const bf16x8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[b]);
-        dp[b] = mfma_bf16(*(const bf16x8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[b]);
+        sc[b] = mfma16(*(const V8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[b]);
+        dp[b] = mfma16(*(const V8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[b]);
       }
     }
     // rows 16b + 4lg + i of this lane's values
@@ -727,16 +729,16 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 p8 = pack_b_operand(sc[2 * kk], sc[2 * kk + 1]);
-      const bf16x8 ds8 = pack_b_operand(dp[2 * kk], dp[2 * kk + 1]);
+      const V8 p8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
+      const V8 ds8 = pack_b_operand<E>(dp[2 * kk], dp[2 * kk + 1]);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
         const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
-        const bf16x8 ag = concat(lds_read_tr((const bf16*)rg0), lds_read_tr((const bf16*)(rg0 + 16 * S::RB)));
-        const bf16x8 aq = concat(lds_read_tr((const bf16*)rq0), lds_read_tr((const bf16*)(rq0 + 16 * S::RB)));
-        dv[d] = mfma_bf16(ag, p8, dv[d]);
-        dk[d] = mfma_bf16(aq, ds8, dk[d]);
+        const V8 ag = concat(lds_read_tr<E>((const E*)rg0), lds_read_tr<E>((const E*)(rg0 + 16 * S::RB)));
+        const V8 aq = concat(lds_read_tr<E>((const E*)rq0), lds_read_tr<E>((const E*)(rq0 + 16 * S::RB)));
+        dv[d] = mfma16(ag, p8, dv[d]);
+        dk[d] = mfma16(aq, ds8, dk[d]);
       }
     }
   }
@@ -746,8 +748,8 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
     if (kp < 0) return;
     const int mode = key_out_mode(a, kp);
     const size_t off = ((size_t)bh * a.T + kp) * D + 4 * lg;
-    store_grad_row<ND>(mode, a.carry_dk + off, (bf16*)a.dk + off, dk, a.scale);
-    store_grad_row<ND>(mode, a.carry_dv + off, (bf16*)a.dv + off, dv, 1.f);
+    store_grad_row<ND>(mode, a.carry_dk + off, (E*)a.dk + off, dk, a.scale);
+    store_grad_row<ND>(mode, a.carry_dv + off, (E*)a.dv + off, dv, 1.f);
   } else {
     float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
     float* pv = pk + kBlock * D;
@@ -762,16 +764,16 @@ __device__ __forceinline__ void bwd_dkdv_bf16_body(const BwdArgs& a, const DkdvI
 
 // At most 168 VGPRs: three waves per SIMD (three workgroups per CU with the
 // two-stage ring) beat two waves with deeper prefetch; four waves would spill.
-template <int D, int NS, int C0, int C1>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_bf16_kernel(
+template <typename E, int D, int NS, int C0, int C1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_b16_kernel(
     BwdArgs a) {
   __shared__ __attribute__((aligned(16))) DkdvStage<D> ring[NS];
   const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
   if (item.kb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    bwd_dkdv_bf16_body<D, NS, C0>(a, item, ring);
+    bwd_dkdv_b16_body<E, D, NS, C0>(a, item, ring);
   else
-    bwd_dkdv_bf16_body<D, NS, C1>(a, item, ring);
+    bwd_dkdv_b16_body<E, D, NS, C1>(a, item, ring);
 }
 
 // ---------------------------------------------------------------------------
@@ -801,10 +803,10 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
     s.w += x.w;
   }
   TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
-  if constexpr (IsBf16<TE>::value) {
+  if constexpr (Is16<TE>::value) {
     const int mode = key_out_mode(a, kp);
     f32x4 x[1] = {(f32x4){s.x, s.y, s.z, s.w}};
-    store_grad_row<1>(mode, (which ? a.carry_dv : a.carry_dk) + base + (size_t)kp * D + ch * 4, (bf16*)dst, x,
+    store_grad_row<1>(mode, (which ? a.carry_dv : a.carry_dk) + base + (size_t)kp * D + ch * 4, dst, x,
                       1.f);
   } else {
     *(float4*)dst = s;
@@ -819,9 +821,9 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   const int64_t rows = (int64_t)a.BH * a.T;
   const int64_t pre_blocks = (rows * TPR + kThreads - 1) / kThreads;
   hipError_t err = hipSuccess;
-  // bf16: the dq kernel computes Delta and the zero fill itself; it runs
+  // 16-bit: the dq kernel computes Delta and the zero fill itself; it runs
   // before dk/dv, which reads Delta
-  if constexpr (!IsBf16<TE>::value) {
+  if constexpr (!Is16<TE>::value) {
     timing_begin(KID_PRE, stream);
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();
@@ -830,9 +832,9 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   }
   if (n_dq > 0) {
     timing_begin(KID_DQ, stream);
-    if constexpr (IsBf16<TE>::value) {
+    if constexpr (Is16<TE>::value) {
       err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
-        hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, kDqStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_dq),
+        hipLaunchKernelGGL((bwd_dq_b16_kernel<TE, D, kDqStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_dq),
                            dim3(kDqThreads), 0, stream, a);
         return hipGetLastError();
       });
@@ -845,9 +847,9 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   }
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
-    if constexpr (IsBf16<TE>::value) {
+    if constexpr (Is16<TE>::value) {
       err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
-        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, kDkdvStages, decltype(c0)::value, decltype(c1)::value>),
+        hipLaunchKernelGGL((bwd_dkdv_b16_kernel<TE, D, kDkdvStages, decltype(c0)::value, decltype(c1)::value>),
                            dim3(n_dkdv), dim3(kThreads), 0, stream, a);
         return hipGetLastError();
       });
@@ -871,6 +873,8 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
 
 template hipError_t launch_bwd<bf16, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<f16, 32>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<f16, 64>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<float, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<float, 64>(const BwdArgs&, int, int, int, hipStream_t);
 

@@ -2,18 +2,20 @@
 // MFMA wrappers and the lane geometry every kernel shares.
 //
 // Wave layout.  A wave is 64 lanes; lane = 16*lg + li with li in [0,16) and
-// lg in [0,4).  For the 16x16 MFMAs used here (v_mfma_f32_16x16x32_bf16 and
+// lg in [0,4).  For the 16x16 MFMAs used here (v_mfma_f32_16x16x32_{bf16,f16} and
 // v_mfma_f32_16x16x4_f32), with D[M][N] = sum_k A[M][k] B[k][N]:
 //   A operand: lane holds A[M = li][k = kw*lg + (0..kw-1)]
 //   B operand: lane holds B[k = kw*lg + (0..kw-1)][N = li]
 //   C / D    : lane holds D[M = 4*lg + e][N = li], e = 0..3
-// with kw = 8 (bf16, K = 32) or kw = 1 (fp32, K = 4).  So a product whose N
+// with kw = 8 (16-bit, K = 32) or kw = 1 (fp32, K = 4).  So a product whose N
 // index is the lane's own query (or key) leaves that row's values in the
 // lane, which keeps the softmax row reductions mostly inside a lane.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "st_geometry.hpp"
 
@@ -23,25 +25,44 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kThreads = 256;    // 4 waves per workgroup
-constexpr int kDqThreads = 512;  // bf16 dq: 8 waves, 16 rows each of a pair of row blocks
+constexpr int kDqThreads = 512;  // 16-bit dq: 8 waves, 16 rows each of a pair of row blocks
 
-template <typename TE>
-struct IsBf16 {
-  static constexpr bool value = false;
+// 16-bit element types of the MFMA kernels (bf16, fp16) and their vectors.
+template <typename E>
+struct Vec;
+template <>
+struct Vec<bf16> {
+  typedef bf16x8 x8;
+  typedef bf16x4 x4;
+  typedef bf16x2 x2;
 };
 template <>
-struct IsBf16<bf16> {
-  static constexpr bool value = true;
+struct Vec<f16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+  typedef f16x2 x2;
+};
+template <typename TE>
+struct Is16 {
+  static constexpr bool value = std::is_same<TE, bf16>::value || std::is_same<TE, f16>::value;
 };
 
-__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+// v_mfma_f32_16x16x32_{bf16,f16}: fp32 accumulation of 16-bit products.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
@@ -51,23 +72,29 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Four fp32 values rounded to bf16 (round-to-nearest-even), packed.
-__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& x) {
-  const bf16x2 lo = __builtin_convertvector((f32x2){x[0], x[1]}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector((f32x2){x[2], x[3]}, bf16x2);
-  return (bf16x4){lo[0], lo[1], hi[0], hi[1]};
+// Four fp32 values rounded to E (round-to-nearest-even), packed.
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::x4 to_x4(const f32x4& x) {
+  typedef typename Vec<E>::x2 V2;
+  const V2 lo = __builtin_convertvector((f32x2){x[0], x[1]}, V2);
+  const V2 hi = __builtin_convertvector((f32x2){x[2], x[3]}, V2);
+  return (typename Vec<E>::x4){lo[0], lo[1], hi[0], hi[1]};
 }
 
 // Eight values for the B operand of a 32-key (or 32-query) MFMA step:
 // slots 0..3 come from one 16-block's C fragment, slots 4..7 from the next.
-__device__ __forceinline__ bf16x8 pack_b_operand(const f32x4& a, const f32x4& b) {
-  const bf16x4 x = to_bf16x4(a);
-  const bf16x4 y = to_bf16x4(b);
-  return (bf16x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::x8 pack_b_operand(const f32x4& a, const f32x4& b) {
+  const typename Vec<E>::x4 x = to_x4<E>(a);
+  const typename Vec<E>::x4 y = to_x4<E>(b);
+  return (typename Vec<E>::x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
-__device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
-  return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+template <typename V4>
+__device__ __forceinline__ auto concat(const V4& a, const V4& b) {
+  typedef decltype(a[0] + a[0]) El;
+  typedef El V8 __attribute__((ext_vector_type(8)));
+  return (V8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes that
@@ -76,18 +103,11 @@ __device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
 // r0 + j/4, columns c0 + 4*(j mod 4) of a row-major tile, lane i therefore gets
 // column c0 + i of rows r0 .. r0 + 3: the transposed operand an MFMA needs,
 // read from a tile stored untransposed.
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-}
-
-// A operand (rows c0 + li, 32 k-slots) of an MFMA whose k index runs over the
-// rows of a row-major LDS tile X[row][col] with pitch `pitch`: k-slots
-// 8*lg + e map to rows r0 + 4*lg + e (e < 4) and r0 + 16 + 4*lg + e - 4, the
-// same slot order as pack_b_operand() gives a pair of C fragments.
-__device__ __forceinline__ bf16x8 tr_a_operand(const bf16* X, int pitch, int r0, int c0, int li, int lg) {
-  const bf16* p = X + (r0 + 4 * lg + (li >> 2)) * pitch + c0 + 4 * (li & 3);
-  return concat(lds_read_tr(p), lds_read_tr(p + 16 * pitch));
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::x4 lds_read_tr(const E* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_bit_cast(typename Vec<E>::x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
 
 __device__ __forceinline__ bool wave_any(bool v) { return __ballot(v) != 0ull; }

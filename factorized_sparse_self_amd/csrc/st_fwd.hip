@@ -9,8 +9,8 @@
 //
 // S^T = K Q^T runs on MFMA so that each lane holds logits of its own query;
 // the online softmax keeps the running max / sum in registers (cross-lane only
-// over the 4 lanes of a query); O^T += V^T P^T runs on MFMA.  The bf16 kernel
-// is the product path; the fp32 kernel serves fp32 inputs.
+// over the 4 lanes of a query); O^T += V^T P^T runs on MFMA.  The 16-bit kernel
+// (bf16 or fp16 inputs) is the product path; the fp32 kernel serves fp32 inputs.
 #include <type_traits>
 
 #include "st_device.hpp"
@@ -21,7 +21,7 @@ namespace st {
 
 namespace {
 
-// LDS ring stages of the bf16 forward (blocks in flight = stages - 1)
+// LDS ring stages of the 16-bit forward (blocks in flight = stages - 1)
 #ifndef ST_FWD_STAGES
 #define ST_FWD_STAGES 2
 #endif
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 forward.
+// 16-bit (bf16 or fp16) forward.
 //  * Work item = a pair of 64-row LUT blocks (128 kernel rows) of one head; it
 //    walks the union of the two blocks' key-block lists.  Waves 0-1 own the
 //    first block, waves 2-3 the second; a wave owns 32 rows as two MFMA
@@ -199,10 +199,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 //    when a logit exceeds it by more than 2^8 in exp2 units; blocks where no
 //    lane of the wave needs that skip the cross-lane max and the rescale.
 // ---------------------------------------------------------------------------
-template <int D, int NS, int KC, bool M>
-__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& item,
+template <typename E, int D, int NS, int KC, bool M>
+__device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& item,
                                               unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
+  typedef typename Vec<E>::x8 V8;
+  typedef typename Vec<E>::x4 V4;
   constexpr int NQ = D / 32;           // MFMA k-steps over D
   constexpr int ND = D / 16;           // 16-wide output column blocks
   constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
@@ -211,9 +213,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
   const GeoC<KC> g{kd.geo};
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t head_bytes = (uint32_t)a.T * D * 2;
-  const Rsrc rq = make_rsrc((const bf16*)a.q + base, head_bytes);
-  const Rsrc rk = make_rsrc((const bf16*)a.k + base, head_bytes);
-  const Rsrc rv = make_rsrc((const bf16*)a.v + base, head_bytes);
+  const Rsrc rq = make_rsrc((const E*)a.q + base, head_bytes);
+  const Rsrc rk = make_rsrc((const E*)a.k + base, head_bytes);
+  const Rsrc rv = make_rsrc((const E*)a.v + base, head_bytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -243,7 +245,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
 #pragma unroll
   for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
 
-  bf16x8 qop[2][NQ];  // the two groups' query rows as MFMA B operands (from LDS, first block)
+  V8 qop[2][NQ];  // the two groups' query rows as MFMA B operands (from LDS, first block)
   f32x4 acc[2][ND];
 #pragma unroll
   for (int G = 0; G < 2; ++G)
@@ -295,7 +297,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
 #pragma unroll
       for (int G = 0; G < 2; ++G)
 #pragma unroll
-        for (int k = 0; k < NQ; ++k) qop[G][k] = *(const bf16x8*)(qt + 16 * G * S::RB + a_off[k]);
+        for (int k = 0; k < NQ; ++k) qop[G][k] = *(const V8*)(qt + 16 * G * S::RB + a_off[k]);
       // every wave's reads must land before any wave's DMA below refills
       // that stage (waves read rows that other waves staged)
       wait_lgkmcnt0();
@@ -313,9 +315,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
       sc[0][b] = sc[1][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
-        const bf16x8 ka = *(const bf16x8*)(Kt + 16 * b * S::RB + a_off[k]);
-        sc[0][b] = mfma_bf16(ka, qop[0][k], sc[0][b]);
-        sc[1][b] = mfma_bf16(ka, qop[1][k], sc[1][b]);
+        const V8 ka = *(const V8*)(Kt + 16 * b * S::RB + a_off[k]);
+        sc[0][b] = mfma16(ka, qop[0][k], sc[0][b]);
+        sc[1][b] = mfma16(ka, qop[1][k], sc[1][b]);
       }
     }
     if (!(hbits & kPairFull)) {
@@ -353,7 +355,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
         m_run[G] = raise ? mt : m_run[G];
       }
     }
-    bf16x8 pb8[2][2];
+    V8 pb8[2][2];
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       const float mb = (m_run[G] == -INFINITY) ? 0.f : m_run[G] * sl2;
@@ -365,7 +367,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
           l_run[G] += sc[G][b][i];
         }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) pb8[G][kk] = pack_b_operand(sc[G][2 * kk], sc[G][2 * kk + 1]);
+      for (int kk = 0; kk < 2; ++kk) pb8[G][kk] = pack_b_operand<E>(sc[G][2 * kk], sc[G][2 * kk + 1]);
     }
     // O^T += V^T P^T for both groups: each V^T operand read serves two MFMAs
 #pragma unroll
@@ -373,9 +375,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         const unsigned char* r = Vt + 32 * kk * S::RB + t_off[d];
-        const bf16x8 av = concat(lds_read_tr((const bf16*)r), lds_read_tr((const bf16*)(r + 16 * S::RB)));
-        acc[0][d] = mfma_bf16(av, pb8[0][kk], acc[0][d]);
-        acc[1][d] = mfma_bf16(av, pb8[1][kk], acc[1][d]);
+        const V8 av = concat(lds_read_tr<E>((const E*)r), lds_read_tr<E>((const E*)(r + 16 * S::RB)));
+        acc[0][d] = mfma16(av, pb8[0][kk], acc[0][d]);
+        acc[1][d] = mfma16(av, pb8[1][kk], acc[1][d]);
       }
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
@@ -384,7 +386,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
   for (int G = 0; G < 2; ++G) {
     const float lsum = group4_sum(l_run[G]);
     if (t[G] < 0) continue;
-    // the output is rounded to bf16, so the hardware reciprocal (1 ulp) suffices
+    // the output is rounded to 16 bits, so the hardware reciprocal (1 ulp) suffices
     const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
     const float lse2 = lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
     const size_t row = (size_t)bh * a.T + t[G];
@@ -399,7 +401,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
       if (lg == 0) a.carry_lse[row] = lse2;
       continue;
     }
-    bf16* O = (bf16*)a.o + base + (size_t)t[G] * D;
+    E* O = (E*)a.o + base + (size_t)t[G] * D;
     if (M && a.out_mode == OUT_MERGE) {
       // softmax over both key sets: weights exp2(L_p - L) of the two passes'
       // outputs, L = log2(2^L0 + 2^L1) (a pass with no keys has L_p = -inf)
@@ -415,13 +417,13 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
       for (int d = 0; d < ND; ++d) {
         const float4 c = *(const float4*)(C + 16 * d + 4 * lg);
         const f32x4 c4 = {c.x, c.y, c.z, c.w};
-        *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(c4 * s0 + acc[G][d] * s1);
+        *(V4*)(O + 16 * d + 4 * lg) = to_x4<E>(c4 * s0 + acc[G][d] * s1);
       }
       if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
       continue;
     }
 #pragma unroll
-    for (int d = 0; d < ND; ++d) *(bf16x4*)(O + 16 * d + 4 * lg) = to_bf16x4(acc[G][d] * inv);
+    for (int d = 0; d < ND; ++d) *(V4*)(O + 16 * d + 4 * lg) = to_x4<E>(acc[G][d] * inv);
     if (lg == 0) a.lse[row] = lse2 * kLn2;
   }
 }
@@ -432,15 +434,15 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a, const PairItem& 
 // kind codes, and each workgroup branches once, uniformly, on its head's kind.
 // M: merged heads (the epilogue carries or merges; plain patterns compile
 // without those stores).
-template <int D, int NS, int C0, int C1, bool M>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
+template <typename E, int D, int NS, int C0, int C1, bool M>
+__global__ __launch_bounds__(kThreads) void fwd_b16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
   const PairItem item = load_uniform(&a.pairs[blockIdx.x]);
   if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    fwd_bf16_body<D, NS, C0, M>(a, item, ring);
+    fwd_b16_body<E, D, NS, C0, M>(a, item, ring);
   else
-    fwd_bf16_body<D, NS, C1, M>(a, item, ring);
+    fwd_b16_body<E, D, NS, C1, M>(a, item, ring);
 }
 
 template <typename TE, int D>
@@ -448,10 +450,10 @@ hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   timing_begin(KID_FWD, stream);
   hipError_t err;
-  if constexpr (IsBf16<TE>::value) {
+  if constexpr (Is16<TE>::value) {
     err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto m) {
       hipLaunchKernelGGL(
-          (fwd_bf16_kernel<D, kFwdStages, decltype(c0)::value, decltype(c1)::value, decltype(m)::value>),
+          (fwd_b16_kernel<TE, D, kFwdStages, decltype(c0)::value, decltype(c1)::value, decltype(m)::value>),
           dim3(n_items), dim3(kThreads), 0, stream, a);
       return hipGetLastError();
     });
@@ -465,6 +467,8 @@ hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
 
 template hipError_t launch_fwd<bf16, 32>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<bf16, 64>(const FwdArgs&, int, hipStream_t);
+template hipError_t launch_fwd<f16, 32>(const FwdArgs&, int, hipStream_t);
+template hipError_t launch_fwd<f16, 64>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<float, 32>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<float, 64>(const FwdArgs&, int, hipStream_t);
 

@@ -53,7 +53,7 @@ struct RowItem {
   int qb, bh, kind, pad;
 };
 
-// Work item of the bf16 forward and dq passes: the pair of 64-row LUT blocks
+// Work item of the 16-bit forward and dq passes: the pair of 64-row LUT blocks
 // 2pb and 2pb+1 of head bh (head kind `kind`).  Its key-block list is the
 // kind's pair_entry[e0, e1); `first` repeats pair_entry[e0] (when e0 < e1) so
 // that the first tile load is issued without reading the list.
@@ -77,7 +77,7 @@ struct FwdArgs {
   int H, T;
   const KindDev* kinds;  // [2], device memory
   const RowItem* items;  // fp32 kernel: row blocks
-  const PairItem* pairs;  // bf16 kernel: row-block pairs
+  const PairItem* pairs;  // 16-bit kernel: row-block pairs
   float sl2;             // log2(e) / sqrt(D)
   int pattern;           // ST_* (host side: selects the kernel)
   int out_mode;          // OutMode
@@ -96,12 +96,12 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;    // [B*H*T] workspace: rowsum(dout * out)
-  float* lse2;     // [B*H*T] workspace: lse * log2(e) (bf16 path; written by dq)
+  float* lse2;     // [B*H*T] workspace: lse * log2(e) (16-bit path; written by dq)
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
   const KindDev* kinds;
   const RowItem* dq_items;   // fp32 dq: row blocks
-  const PairItem* dq_pairs;  // bf16 dq: row-block pairs
+  const PairItem* dq_pairs;  // 16-bit dq: row-block pairs
   const DkdvItem* dkdv_items;
   const ReduceItem* red_items;
   float sl2;    // log2(e) / sqrt(D)

@@ -1,6 +1,7 @@
-// Direct global -> LDS staging of 64-row bf16 tiles for the gfx950 kernels.
+// Direct global -> LDS staging of 64-row 16-bit tiles (bf16 or fp16) for the
+// gfx950 kernels.
 //
-// A tile holds 64 rows of D bf16 (row bytes RB = 2*D, no padding).  The 16-byte
+// A tile holds 64 rows of D 16-bit values (row bytes RB = 2*D, no padding).  The 16-byte
 // chunk c of row r is stored at chunk c ^ (r mod CH), CH = D/8 chunks per row:
 // rows that an MFMA operand read touches at the same time land on different
 // banks, for both the row-operand reads and the LDS transpose reads.
@@ -65,7 +66,7 @@ __device__ __forceinline__ void lds_dma(Rsrc r, uint32_t lds_base, uint32_t voff
 }
 #pragma clang diagnostic pop
 
-// Stage N*RPI rows of one 64-row tile of a [T, D] bf16 tensor (N = NI: the
+// Stage N*RPI rows of one 64-row tile of a [T, D] 16-bit tensor (N = NI: the
 // wave's 16 rows): `rows` is the wave-uniform LDS address of the first of them
 // (a multiple of CH rows into a tile), pos[i] the position for row
 // i*RPI + lane/CH of them, or -1 for padding.  The chunk a lane fetches is the

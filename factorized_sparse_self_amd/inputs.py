@@ -10,7 +10,7 @@ projected activations; the datasets themselves are not used.
 Recipe (identical on every machine): ``torch.Generator().manual_seed(seed)``,
 draws in the order q, k, v, dO, each ``randn(B, H, T, D)`` in fp32, multiplied
 by ``scale`` and then rounded to the compute dtype (round-to-nearest-even for
-bf16).  The oracle receives these stored values widened exactly to fp64.
+bf16 and fp16).  The oracle receives these stored values widened exactly to fp64.
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ class Workload:
     D: int
     l: int
     c: int
-    dtype: str  # "bf16" or "f32"
+    dtype: str  # "bf16", "f16" or "f32"
     backward: bool
     seed: int
     scale: float = 1.0
@@ -43,7 +43,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[self.dtype]
 
 
 # The five workloads of the hot path.  Seeds are 1000 + position.
@@ -75,6 +75,8 @@ EXTRA_WORKLOADS = [
              note="merged heads: own block plus earlier summary keys in every head"),
     Workload("strided_union_T12288_bf16_fwdbwd", STRIDED_UNION, 1, 16, 12288, 64, 128, 0, "bf16", True, 1009,
              note="merged heads: window plus strided keys in every head"),
+    Workload("fixed_T12288_f16_fwdbwd", FIXED, 4, 8, 12288, 64, 128, 8, "f16", True, 1010,
+             note="the fixed workload with fp16 (IEEE binary16) inputs"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

@@ -29,8 +29,9 @@
  *     first keeps fp32 partial results in the workspace, the second merges
  *     its own into them (the two softmaxes by their log-sum-exps, gradients
  *     by addition).  For that split the strided pass leaves out t itself
- *     (already in the window); the fixed sets are disjoint.  bf16 only: the
- *     _f32 attention entry points return ST_ERR_UNSUPPORTED for them.
+ *     (already in the window); the fixed sets are disjoint.  16-bit inputs
+ *     only: the _f32 attention entry points return ST_ERR_UNSUPPORTED for
+ *     them.
  *
  * Conventions (readings where the pages are silent):
  *   - positions are 0-based; T need not be a multiple of l;
@@ -42,7 +43,8 @@
  * Layout.  q, k, v, out, dout, dq, dk, dv are dense row-major [B, H, T, D]
  * (D fastest); lse is [B, H, T] fp32.  The unsuffixed entry points take and
  * return bf16 (bfloat16, round-to-nearest-even on output) with fp32
- * arithmetic inside; the _f32 entry points take and return fp32.
+ * arithmetic inside; the _f16 entry points do the same with fp16 (IEEE
+ * binary16); the _f32 entry points take and return fp32.
  *
  * Ownership.  All tensor pointers are device pointers owned by the caller;
  * the library never frees them or keeps them past the call.  The library owns
@@ -171,6 +173,15 @@ int st_sparse_attn_fwd(const void* q, const void* k, const void* v, void* out, f
 int st_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
                        int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+
+/* fp16 twins: same arguments, fp16 (IEEE binary16) tensors, fp32 arithmetic
+ * (the pages fix only "16-bit" precision; this is the other 16-bit format).
+ * Outputs are rounded to nearest even. */
+int st_sparse_attn_fwd_f16(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+int st_sparse_attn_bwd_f16(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int T, int D, int pattern, int l, int c, void* stream);
 
 /* fp32 twins: same arguments, fp32 tensors. */
 int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,

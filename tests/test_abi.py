@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("st_layout_build", "st_sparse_attn_fwd", "st_sparse_attn_bwd", "st_sparse_attn_fwd_f32",
+    for n in ("st_layout_build", "st_sparse_attn_fwd", "st_sparse_attn_bwd", "st_sparse_attn_fwd_f16",
+              "st_sparse_attn_bwd_f16", "st_sparse_attn_fwd_f32",
               "st_sparse_attn_bwd_f32", "st_layout_csr", "st_layout_csc", "st_layout_maps"):
         assert n in names
 
@@ -52,7 +53,7 @@ def _call_fwd(name, ptr, B=1, H=2, T=64, D=64, pattern=0, l=8, c=0):
     return getattr(lib(), name)(ptr, ptr, ptr, ptr, ptr, B, H, T, D, pattern, l, c, None)
 
 
-@pytest.mark.parametrize("name", ["st_sparse_attn_fwd", "st_sparse_attn_fwd_f32"])
+@pytest.mark.parametrize("name", ["st_sparse_attn_fwd", "st_sparse_attn_fwd_f16", "st_sparse_attn_fwd_f32"])
 def test_attention_argument_errors_without_gpu(name):
     from factorized_sparse_self_amd import lib
     fake = 1 << 20  # aligned, never dereferenced: every case fails the checks first

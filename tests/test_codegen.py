@@ -3,7 +3,7 @@
 - The LDS DMA helper sets M0 inside its inline asm and does not restore it; that is only
   sound while the compiler itself never uses M0 in these kernels.  The test fails if M0
   appears anywhere outside the inline asm blocks.
-- The bf16 kernels must not spill registers to scratch memory.
+- The 16-bit (bf16 / fp16) kernels must not spill registers to scratch memory.
 """
 import os
 import re
@@ -54,10 +54,12 @@ def test_m0_only_inside_inline_asm(device_asm, src):
 
 
 @pytest.mark.parametrize("src", SOURCES)
-def test_bf16_kernels_do_not_spill(device_asm, src):
+def test_16bit_kernels_do_not_spill(device_asm, src):
     text = device_asm(src)
-    kernels = re.findall(r"\.name:\s+(\S*bf16_kernel\S*)\n(.*?)\.wavefront_size", text, flags=re.S)
-    assert kernels, "no bf16 kernel metadata found"
+    kernels = re.findall(r"\.name:\s+(\S*b16_kernel\S*)\n(.*?)\.wavefront_size", text, flags=re.S)
+    assert kernels, "no 16-bit kernel metadata found"
+    # both element types are instantiated
+    assert any("DF16b" in n for n, _ in kernels) and any("DF16_" in n for n, _ in kernels)
     for name, meta in kernels:
         spill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", meta).group(1))
         scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", meta).group(1))

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Tolerances are the ones the hot path is held to: max |error| <= 2e-2 for bf16
+Tolerances are the ones the hot path is held to: max |error| <= 2e-2 for bf16 and fp16
 inputs and <= 1e-4 for fp32 inputs, on out, lse, dq, dk and dv (fp64 oracle).
 Rows with an empty key set must give out == 0 and lse == -inf exactly, single-
 key rows out == v exactly, and keys nobody attends dk == dv == 0 exactly.
@@ -22,8 +22,9 @@ from factorized_sparse_self_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "f32": 1e-4}
-SIGNIFICAND_BITS = {"bf16": 8, "f32": 24}
+TOL = {"bf16": 2e-2, "f16": 2e-2, "f32": 1e-4}
+SIGNIFICAND_BITS = {"bf16": 8, "f16": 11, "f32": 24}
+TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def allowed_error(ref, dtype):
@@ -100,12 +101,12 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"p{c[0]}_B{c[1]}H{c[2]}T{c[3]}D{c[4]}l{c[5]}c{c[6]}")
 def test_small_forward_backward(case, dtype):
     pattern, B, H, T, D, l, c = case
     log(f"small fwd+bwd {case} {dtype}")
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = TORCH_DTYPE[dtype]
     q, k, v, do = inputs.draw(B, H, T, D, dtype=tdt, seed=7 + T + l, n=4)
     out, lse = run_fwd(q, k, v, pattern, l, c)
     qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
@@ -119,7 +120,7 @@ def test_small_forward_backward(case, dtype):
     assert_close(f64(dv), rv, dtype, "dv")
 
 
-# Merged heads (every head attends both sets): bf16 only
+# Merged heads (every head attends both sets): 16-bit inputs only
 SMALL_UNION = [
     (inputs.STRIDED_UNION, 2, 3, 300, 64, 16, 0),
     (inputs.STRIDED_UNION, 1, 2, 333, 32, 20, 0),
@@ -136,23 +137,24 @@ SMALL_UNION = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("case", SMALL_UNION, ids=lambda c: f"p{c[0]}_B{c[1]}H{c[2]}T{c[3]}D{c[4]}l{c[5]}c{c[6]}")
-def test_small_merged_heads(case):
+def test_small_merged_heads(case, dtype):
     pattern, B, H, T, D, l, c = case
-    log(f"small merged heads fwd+bwd {case}")
-    q, k, v, do = inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=17 + T + l, n=4)
+    log(f"small merged heads fwd+bwd {case} {dtype}")
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=17 + T + l, n=4)
     out, lse = run_fwd(q, k, v, pattern, l, c)
     qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
     O, L = oracle.forward(qn, kn, vn, pattern, l, c)
-    assert_close(f64(out), O, "bf16", "out")
+    assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     # position 0 attends only itself in both sets: out == v exactly
     assert torch.equal(out[:, :, 0].cpu(), v[:, :, 0])
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
     rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
-    assert_close(f64(dq), rq, "bf16", "dq")
-    assert_close(f64(dk), rk, "bf16", "dk")
-    assert_close(f64(dv), rv, "bf16", "dv")
+    assert_close(f64(dq), rq, dtype, "dq")
+    assert_close(f64(dk), rk, dtype, "dk")
+    assert_close(f64(dv), rv, dtype, "dv")
 
 
 def test_edge_shapes():
@@ -163,8 +165,8 @@ def test_edge_shapes():
         (inputs.STRIDED, 2, 2, 70, 32, 1, 0), (inputs.FIXED, 1, 2, 70, 64, 1, 1),
         (inputs.FIXED, 1, 5, 130, 64, 8, 8), (inputs.DENSE, 1, 1, 65, 64, 1, 0),
     ]
-    for dtype in ("bf16", "f32"):
-        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for dtype in ("bf16", "f16", "f32"):
+        tdt = TORCH_DTYPE[dtype]
         for pattern, B, H, T, D, l, c in cases:
             log(f"edge {pattern} B{B} H{H} T{T} D{D} l{l} c{c} {dtype}")
             q, k, v, do = inputs.draw(B, H, T, D, dtype=tdt, seed=99 + T, n=4)
