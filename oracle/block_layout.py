@@ -28,7 +28,8 @@ The maps:
   classes); rows and keys share the map.  The strided set of t is then the
   class-r prefix m' <= m.
 * fixed kind 1, compacted summary keys: K = b*c + o holds position
-  b*l + (l - c) + o.  Under the strictly-earlier-block reading (FIXED) only
+  b*l + S[o], S the sorted summary offsets (c = |S|; for the default set the
+  last c offsets, b*l + (l - c) + o).  Under the strictly-earlier-block reading (FIXED) only
   blocks 0 .. nb-2 (nb = ceil(T/l)) appear, since the last block's summary
   keys have no later query; under FIXED_R1 all nb blocks appear and
   positions >= T are padding.  Rows are the identity.
@@ -42,7 +43,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .sparse_attention import DENSE, FIXED, FIXED_R1, STRIDED, UNION_BASE, part_key_set
+from .sparse_attention import DENSE, FIXED, FIXED_R1, STRIDED, UNION_BASE, part_key_set, summary_offsets
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -70,10 +71,11 @@ def kernel_maps(pattern: int, kind: int, T: int, l: int, c: int, bs: int):
     if pattern in (FIXED, FIXED_R1) and kind == 1:
         nb = _ceil_div(T, l)
         n_blocks = nb - 1 if pattern == FIXED else nb
+        S = summary_offsets(l, c)
         keys = []
         for b in range(n_blocks):
-            for o in range(c):
-                j = b * l + (l - c) + o
+            for o in range(len(S)):
+                j = b * l + int(S[o])
                 keys.append(j if j < T else -1)
         return identity, np.asarray(keys, dtype=np.int64)
     if pattern in (STRIDED, FIXED, FIXED_R1, DENSE):

@@ -26,10 +26,14 @@ R-heads   Factorised heads: head h uses sub-pattern ``h % 2``; kind 0 is the
           local / own-block set, kind 1 the strided / summary set.
 R-self    The local window and the strided set both contain t itself
           (window [t-l+1, t]; strided t, t-l, t-2l, ...).
-R-summary The summary set is the last c offsets of each l-block.  Fixed kind 1
-          (pattern FIXED) uses summary keys of strictly earlier blocks only.
-          FIXED_R1 also admits own-block summary keys j <= t, which is what the
-          mask sketch's loop over ``block + 1`` blocks does.
+R-summary The summary set is a fixed set S of offsets within each l-block
+          (llm-arch-kb §2, Pattern B; the §3 sketch takes it as an argument).
+          Everywhere a pattern takes ``c``, ``c`` is either the count |S| with
+          S the last c offsets (nlp-lineage, "The idea": summary positions at
+          the end of each block) or the offsets of S themselves (a sequence).
+          Fixed kind 1 (pattern FIXED) uses summary keys of strictly earlier
+          blocks only.  FIXED_R1 also admits own-block summary keys j <= t,
+          which is what the mask sketch's loop over ``block + 1`` blocks does.
 R-empty   A row with an empty key set (fixed kind 1, first block) has O = 0 and
           lse = -inf, and contributes nothing to any gradient.
 R-scale   d is the head dimension D; lse is the natural log of the sum of
@@ -63,6 +67,17 @@ def head_kind(h: int) -> int:
     return h % 2
 
 
+def summary_offsets(l: int, c) -> np.ndarray:
+    """The summary set S as sorted offsets in [0, l) (reading R-summary): the
+    last ``c`` offsets for an integer ``c``, else the given offsets."""
+    if isinstance(c, (int, np.integer)):
+        return np.arange(l - int(c), l, dtype=np.int64)
+    S = np.asarray(sorted(int(o) for o in c), dtype=np.int64)
+    if S.size == 0 or S[0] < 0 or S[-1] >= l or np.unique(S).size != S.size:
+        raise ValueError("summary offsets must be distinct and in [0, l)")
+    return S
+
+
 # --------------------------------------------------------------------------
 # Key sets
 # --------------------------------------------------------------------------
@@ -90,9 +105,9 @@ def key_set(pattern: int, kind: int, t: int, T: int, l: int, c: int) -> np.ndarr
         if kind == 0:
             return np.arange(blk * l, t + 1, dtype=np.int64)
         last_block = blk - 1 if pattern == FIXED else blk
-        # summary offsets l-c .. l-1 of blocks 0 .. last_block, block by block
+        # the summary offsets of blocks 0 .. last_block, block by block
         starts = np.arange(last_block + 1, dtype=np.int64)[:, None] * l
-        keys = (starts + np.arange(l - c, l, dtype=np.int64)[None, :]).ravel()
+        keys = (starts + summary_offsets(l, c)[None, :]).ravel()
         return keys[keys <= t]
     if pattern == DENSE:
         return np.arange(0, t + 1, dtype=np.int64)
@@ -118,7 +133,7 @@ def in_key_set(pattern: int, kind: int, t, j, l: int, c: int) -> np.ndarray:
     if pattern in (FIXED, FIXED_R1):
         if kind == 0:
             return causal & (j // l == t // l)
-        summary = (j % l) >= (l - c)
+        summary = np.isin(j % l, summary_offsets(l, c))
         if pattern == FIXED:
             return (j >= 0) & summary & (j // l < t // l)
         return causal & summary

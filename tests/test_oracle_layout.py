@@ -43,6 +43,8 @@ CASES = [
     (DENSE, 200, 16, 0, 64),
     (STRIDED_UNION, 256, 16, 0, 64), (STRIDED_UNION, 300, 7, 0, 16),
     (FIXED_UNION, 250, 16, 3, 16), (FIXED_UNION, 1024, 32, 4, 64),
+    (FIXED, 250, 16, (0, 5, 9), 16), (FIXED_R1, 250, 16, (2, 15), 64), (FIXED_UNION, 256, 32, (0, 31), 64),
+    (FIXED, 300, 20, (1, 2, 3, 17), 32),
 ]
 
 
@@ -85,7 +87,8 @@ def test_maps_are_bijections(pattern, T, l, c, bs):
         assert attended <= set(real_keys.tolist())
         if UNION_BASE.get(pattern, pattern) == FIXED and kind == 1:
             nb = -(-T // l)
-            expect = [b * l + o for b in range(nb - 1) for o in range(l - c, l)]
+            offsets = range(l - c, l) if isinstance(c, int) else sorted(c)
+            expect = [b * l + o for b in range(nb - 1) for o in offsets]
             assert real_keys.tolist() == expect
         if UNION_BASE.get(pattern, pattern) == STRIDED and kind == 1:
             # within a class the run is in increasing position order, l apart

@@ -26,8 +26,9 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def recursive_sets(pattern, T, l, c):
-    """Per-query key sets (kind 0, kind 1) built position by position from the prose."""
-    summary = set(range(l - c, l))
+    """Per-query key sets (kind 0, kind 1) built position by position from the prose.
+    ``c``: the summary set's size (its last c offsets) or its offsets."""
+    summary = set(range(l - c, l)) if isinstance(c, int) else set(c)
     k0, k1 = [], []
     for t in range(T):
         blk_start = (t // l) * l
@@ -64,9 +65,15 @@ CASES = [
     (FIXED_R1, 64, 8, 2), (FIXED_R1, 50, 7, 3), (FIXED_R1, 41, 8, 8),
     (DENSE, 30, 4, 0),
 ]
+# general summary sets S (llm-arch-kb §2 Pattern B): given as offsets
+SIGMA_CASES = [
+    (FIXED, 64, 8, (0, 5)), (FIXED, 50, 7, (2,)), (FIXED, 40, 8, (0, 1, 2, 3, 4, 5, 6, 7)),
+    (FIXED, 37, 5, (0, 4)), (FIXED_R1, 64, 8, (1, 3, 6)), (FIXED_R1, 41, 8, (0, 7)),
+    (FIXED_R1, 50, 7, (3,)),
+]
 
 
-@pytest.mark.parametrize("pattern,T,l,c", CASES)
+@pytest.mark.parametrize("pattern,T,l,c", CASES + SIGMA_CASES)
 def test_key_sets_match_recursive_construction(pattern, T, l, c):
     k0, k1 = recursive_sets(pattern, T, l, c)
     for t in range(T):
@@ -78,6 +85,7 @@ def test_key_sets_match_recursive_construction(pattern, T, l, c):
 UNION_CASES = [
     (STRIDED_UNION, 64, 8, 0), (STRIDED_UNION, 50, 7, 0), (STRIDED_UNION, 20, 32, 0), (STRIDED_UNION, 33, 1, 0),
     (FIXED_UNION, 64, 8, 2), (FIXED_UNION, 50, 7, 3), (FIXED_UNION, 40, 8, 8), (FIXED_UNION, 37, 5, 1),
+    (FIXED_UNION, 64, 8, (0, 5)), (FIXED_UNION, 37, 5, (2,)),
 ]
 
 
@@ -123,7 +131,7 @@ def test_fixed_union_counts_closed_form(T, l, c):
         assert n <= l + c * math.ceil((t + 1) / l)
 
 
-@pytest.mark.parametrize("pattern,T,l,c", CASES + UNION_CASES)
+@pytest.mark.parametrize("pattern,T,l,c", CASES + SIGMA_CASES + UNION_CASES)
 def test_membership_predicate_agrees_with_enumeration(pattern, T, l, c):
     tt, jj = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
     for kind in (0, 1):
@@ -242,3 +250,27 @@ def test_page_cost_figures():
         union = pair_count(FIXED, 0, T, l, c) + pair_count(FIXED, 1, T, l, c)
         bound = sum(l + c * math.ceil(i / l) for i in range(1, T + 1))
         assert case["min_fraction_of_bound"] * bound <= union <= bound
+
+
+def test_summary_offsets_default_and_explicit_agree():
+    """An integer c is the last c offsets; the same offsets given explicitly (in any
+    order) give the same sets, and invalid offsets are refused."""
+    from oracle import summary_offsets
+    assert summary_offsets(8, 3).tolist() == [5, 6, 7]
+    for pattern in (FIXED, FIXED_R1, FIXED_UNION):
+        for t in range(50):
+            for kind in (0, 1):
+                assert (key_set(pattern, kind, t, 50, 8, 3).tolist()
+                        == key_set(pattern, kind, t, 50, 8, (7, 5, 6)).tolist())
+    for bad in ((8,), (-1,), (2, 2), ()):
+        with pytest.raises(ValueError):
+            summary_offsets(8, bad)
+
+
+@pytest.mark.parametrize("T,l,S", [(64, 8, (0, 5)), (50, 7, (2,)), (41, 8, (0, 7)), (100, 16, (1, 4, 9))])
+def test_general_summary_counts(T, l, S):
+    """|B2(t)| = |S| * floor(t/l) under FIXED, plus #{s in S : s <= t mod l} under FIXED_R1."""
+    for t in range(T):
+        assert len(key_set(FIXED, 1, t, T, l, S)) == len(S) * (t // l)
+        own = sum(1 for s in S if s <= t % l)
+        assert len(key_set(FIXED_R1, 1, t, T, l, S)) == len(S) * (t // l) + own

@@ -50,6 +50,8 @@ SMALL = [
     (FIXED, 2, 3, 40, 5, 6, 2), (FIXED, 1, 4, 37, 4, 5, 5),
     (FIXED_R1, 1, 2, 40, 3, 6, 2), (DENSE, 1, 2, 25, 4, 6, 0),
     (STRIDED_UNION, 1, 2, 40, 5, 6, 0), (FIXED_UNION, 2, 2, 37, 4, 5, 2),
+    # general summary sets (offsets)
+    (FIXED, 2, 3, 40, 5, 6, (0, 3)), (FIXED_R1, 1, 2, 40, 3, 6, (1, 4)), (FIXED_UNION, 1, 2, 37, 4, 5, (0, 2)),
 ]
 
 
