@@ -49,21 +49,23 @@ MI355X_FP32_TFLOPS = 157.3     # dense fp32 MFMA peak, TFLOP/s
 def active_rows(pattern, kind, T, l, c):
     """Query rows whose key set (of this kind, or of this pass for merged heads) is non-empty."""
     from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1, ST_FIXED_UNION, ST_STRIDED_UNION
+    from factorized_sparse_self_amd.inputs import summary_offsets
     if pattern in (ST_FIXED, ST_FIXED_UNION, ST_STRIDED_UNION) and kind == 1:
         return max(0, T - l)
     if pattern == ST_FIXED_R1 and kind == 1:
-        return max(0, T - (l - c))
+        return max(0, T - summary_offsets(l, c)[0])
     return T
 
 
 def attended_keys(pattern, kind, T, l, c):
     """Key positions some query attends (in this kind, or this pass for merged heads)."""
     from factorized_sparse_self_amd import ST_FIXED, ST_FIXED_R1, ST_FIXED_UNION, ST_STRIDED_UNION
+    from factorized_sparse_self_amd.inputs import summary_offsets
     nb = -(-T // l)
     if pattern in (ST_FIXED, ST_FIXED_UNION) and kind == 1:
-        return (nb - 1) * c
+        return (nb - 1) * len(summary_offsets(l, c))
     if pattern == ST_FIXED_R1 and kind == 1:
-        return sum(1 for b in range(nb) for o in range(c) if b * l + l - c + o < T)
+        return sum(1 for b in range(nb) for s in summary_offsets(l, c) if b * l + s < T)
     if pattern == ST_STRIDED_UNION and kind == 1:
         return max(0, T - l)
     return T
@@ -73,8 +75,9 @@ def second_pass_keys(pattern, T, l, c):
     """Merged heads: key positions the second pass holds (their first-pass dk / dv are
     carried in fp32 and merged)."""
     from factorized_sparse_self_amd import ST_FIXED_UNION
+    from factorized_sparse_self_amd.inputs import summary_offsets
     nb = -(-T // l)
-    return (nb - 1) * c if pattern == ST_FIXED_UNION else T
+    return (nb - 1) * len(summary_offsets(l, c)) if pattern == ST_FIXED_UNION else T
 
 
 def head_passes(pattern, h):

@@ -17,12 +17,23 @@ LIB_PATH = os.path.join(PKG, "libst.so")
 
 ST_STRIDED, ST_FIXED, ST_FIXED_R1, ST_DENSE, ST_STRIDED_UNION, ST_FIXED_UNION = range(6)
 ST_DIM_BLOCK, ST_DIM_ROWS, ST_DIM_KEYS, ST_DIM_QBLOCKS, ST_DIM_KBLOCKS, ST_DIM_NNZ = range(6)
+ST_BF16, ST_F16, ST_F32 = range(3)
+
+
+def _summary(c):
+    """(count, int32 array or None) for a summary argument: an integer c (the last c
+    offsets of each block) or the summary offsets themselves (a sequence)."""
+    if isinstance(c, (int, np.integer)):
+        return int(c), None
+    offs = np.ascontiguousarray(np.asarray(list(c), dtype=np.int32))
+    return int(offs.size), offs
 
 # name -> (restype, argtypes) of every exported symbol
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SIG = {
     "st_layout_build": (_I, [_I, _I, _I, _I, ctypes.POINTER(_P)]),
+    "st_layout_build_ex": (_I, [_I, _I, _I, _I, _P, ctypes.POINTER(_P)]),
     "st_layout_dims": (_I, [_P, _I, ctypes.POINTER(ctypes.c_int32)]),
     "st_layout_pairs": (_I, [_P, _I, ctypes.POINTER(ctypes.c_int64)]),
     "st_layout_maps": (_I, [_P, _I, _P, _P]),
@@ -35,6 +46,8 @@ _SIG = {
     "st_sparse_attn_bwd": (_I, [_P] * 9 + [_I] * 7 + [_P]),
     "st_sparse_attn_bwd_f16": (_I, [_P] * 9 + [_I] * 7 + [_P]),
     "st_sparse_attn_bwd_f32": (_I, [_P] * 9 + [_I] * 7 + [_P]),
+    "st_sparse_attn_fwd_ex": (_I, [_I] + [_P] * 5 + [_I] * 7 + [_P, _P]),
+    "st_sparse_attn_bwd_ex": (_I, [_I] + [_P] * 9 + [_I] * 7 + [_P, _P]),
     "st_timing_enable": (_I, [_I]),
     "st_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
     "st_timing_reset": (None, []),
@@ -82,11 +95,17 @@ def _check(fn: str, status: int) -> None:
 # Layout (host only)
 # ---------------------------------------------------------------------------
 
-def st_layout_build(pattern: int, T: int, l: int, c: int) -> list[dict]:
-    """Block LUTs of both head kinds as numpy arrays: [kind0, kind1]."""
+def st_layout_build(pattern: int, T: int, l: int, c=0) -> list[dict]:
+    """Block LUTs of both head kinds as numpy arrays: [kind0, kind1].  ``c``: the
+    summary count (last c offsets) or the summary offsets (a sequence)."""
     L = lib()
     handle = _P()
-    _check("st_layout_build", L.st_layout_build(pattern, T, l, c, ctypes.byref(handle)))
+    n, offs = _summary(c)
+    if offs is None:
+        _check("st_layout_build", L.st_layout_build(pattern, T, l, n, ctypes.byref(handle)))
+    else:
+        _check("st_layout_build_ex", L.st_layout_build_ex(pattern, T, l, n, offs.ctypes.data_as(_P),
+                                                          ctypes.byref(handle)))
     try:
         out = []
         for kind in (0, 1):
@@ -163,19 +182,21 @@ def _shape_check(name, x, like):
         raise ValueError(f"{name} must be on q's device")
 
 
-def _entry(dtype, base):
+def _dtype_code(dtype):
     import torch
-    if dtype == torch.bfloat16:
-        return base
-    if dtype == torch.float16:
-        return base + "_f16"
-    if dtype == torch.float32:
-        return base + "_f32"
-    raise TypeError("q, k, v must be bfloat16, float16 or float32")
+    codes = {torch.bfloat16: ST_BF16, torch.float16: ST_F16, torch.float32: ST_F32}
+    if dtype not in codes:
+        raise TypeError("q, k, v must be bfloat16, float16 or float32")
+    return codes[dtype]
 
 
-def st_sparse_attn_fwd(q, k, v, pattern: int, l: int, c: int = 0, out=None, lse=None):
-    """out [B,H,T,D] and lse [B,H,T] fp32 of sparse causal attention."""
+def _entry(dtype, base):
+    return base + ("", "_f16", "_f32")[_dtype_code(dtype)]
+
+
+def st_sparse_attn_fwd(q, k, v, pattern: int, l: int, c=0, out=None, lse=None):
+    """out [B,H,T,D] and lse [B,H,T] fp32 of sparse causal attention.  ``c``: the
+    summary count (last c offsets of each block) or the summary offsets."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, D]")
@@ -190,15 +211,20 @@ def st_sparse_attn_fwd(q, k, v, pattern: int, l: int, c: int = 0, out=None, lse=
     _shape_check("out", out, q)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
-    name = _entry(q.dtype, "st_sparse_attn_fwd")
+    n, offs = _summary(c)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        _check(name, getattr(lib(), name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                          lse.data_ptr(), B, H, T, D, pattern, l, c, stream))
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+        if offs is None:
+            name = _entry(q.dtype, "st_sparse_attn_fwd")
+            _check(name, getattr(lib(), name)(*ptrs, B, H, T, D, pattern, l, n, stream))
+        else:
+            _check("st_sparse_attn_fwd_ex", lib().st_sparse_attn_fwd_ex(
+                _dtype_code(q.dtype), *ptrs, B, H, T, D, pattern, l, n, offs.ctypes.data_as(_P), stream))
     return out, lse
 
 
-def st_sparse_attn_bwd(q, k, v, out, lse, dout, pattern: int, l: int, c: int = 0,
+def st_sparse_attn_bwd(q, k, v, out, lse, dout, pattern: int, l: int, c=0,
                        dq=None, dk=None, dv=None):
     """dq, dk, dv of L = <dout, out>, recomputing the attention weights from lse."""
     import torch
@@ -212,13 +238,17 @@ def st_sparse_attn_bwd(q, k, v, out, lse, dout, pattern: int, l: int, c: int = 0
     dv = torch.empty_like(q) if dv is None else dv
     for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
         _shape_check(name, x, q)
-    name = _entry(q.dtype, "st_sparse_attn_bwd")
+    n, offs = _summary(c)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        _check(name, getattr(lib(), name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                                          dk.data_ptr(), dv.data_ptr(), B, H, T, D, pattern, l, c,
-                                          stream))
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+        if offs is None:
+            name = _entry(q.dtype, "st_sparse_attn_bwd")
+            _check(name, getattr(lib(), name)(*ptrs, B, H, T, D, pattern, l, n, stream))
+        else:
+            _check("st_sparse_attn_bwd_ex", lib().st_sparse_attn_bwd_ex(
+                _dtype_code(q.dtype), *ptrs, B, H, T, D, pattern, l, n, offs.ctypes.data_as(_P), stream))
     return dq, dk, dv
 
 
@@ -248,7 +278,7 @@ def _autograd_function():
 _SparseAttention = None
 
 
-def sparse_attention(q, k, v, pattern: int, l: int, c: int = 0):
+def sparse_attention(q, k, v, pattern: int, l: int, c=0):
     """Differentiable sparse attention (torch.autograd) over st_sparse_attn_fwd / _bwd."""
     global _SparseAttention
     if _SparseAttention is None:

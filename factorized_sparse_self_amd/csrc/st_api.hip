@@ -29,9 +29,10 @@ constexpr int kDkdvSplit = 32;
 
 struct PlanKey {
   int device, pattern, T, l, c, B, H;
+  std::vector<int32_t> summary;  // canonical summary set (empty: the last c offsets)
   bool operator<(const PlanKey& o) const {
-    return std::tie(device, pattern, T, l, c, B, H) <
-           std::tie(o.device, o.pattern, o.T, o.l, o.c, o.B, o.H);
+    return std::tie(device, pattern, T, l, c, B, H, summary) <
+           std::tie(o.device, o.pattern, o.T, o.l, o.c, o.B, o.H, o.summary);
   }
 };
 
@@ -125,8 +126,10 @@ int build_plan(const PlanKey& key, Plan* plan) {
   lay.T = key.T;
   lay.l = key.l;
   lay.c = key.c;
+  lay.summary = key.summary;
+  const int32_t* sigma_host = lay.summary.empty() ? nullptr : lay.summary.data();
   for (int kind = 0; kind < 2; ++kind) {
-    make_geometry(key.pattern, kind, key.T, key.l, key.c, &lay.kind[kind].geo);
+    make_geometry(key.pattern, kind, key.T, key.l, key.c, sigma_host, &lay.kind[kind].geo);
     build_kind(lay.kind[kind]);
   }
   const int BH = key.B * key.H;
@@ -239,6 +242,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   Blob blob;
   KindDev kinds_host[2];
   size_t off_kinds = blob.add(kinds_host, sizeof(kinds_host));
+  const size_t off_sigma = blob.add(lay.summary.data(), lay.summary.size() * sizeof(int32_t));
   size_t offs[2][10];
   for (int kind = 0; kind < 2; ++kind) {
     const KindLayout& L = lay.kind[kind];
@@ -275,6 +279,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
     const KindLayout& L = lay.kind[kind];
     KindDev& k = kinds_host[kind];
     k.geo = L.geo;
+    k.geo.sigma = lay.summary.empty() ? nullptr : (const int32_t*)(dbase + off_sigma);
     k.row_ptr = (const int32_t*)(dbase + offs[kind][0]);
     k.col_idx = (const int32_t*)(dbase + offs[kind][1]);
     k.flags = (const uint8_t*)(dbase + offs[kind][2]);
@@ -343,7 +348,7 @@ int get_workspace(int device, size_t bytes, void** out) {
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, int H, int T, int D,
-                    int pattern, int l, int c) {
+                    int pattern, int l, int c, const int32_t* summary) {
   for (int i = 0; i < n_ptrs; ++i)
     if (!aligned16(ptrs[i])) {
       set_error(std::string(fn) + ": tensor pointer " + std::to_string(i) +
@@ -354,7 +359,7 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
     set_error(std::string(fn) + ": need B >= 1, H >= 1, B*H <= 2^20");
     return ST_ERR_INVALID;
   }
-  const std::string why = check_pattern_args(pattern, T, l, c);
+  const std::string why = check_pattern_args(pattern, T, l, c, summary);
   if (!why.empty()) {
     set_error(std::string(fn) + ": " + why);
     return ST_ERR_INVALID;
@@ -364,7 +369,7 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
     return ST_ERR_UNSUPPORTED;
   }
   Geometry g;
-  make_geometry(pattern, 1, T, l, c, &g);
+  make_geometry(pattern, 1, T, l, c, nullptr, &g);
   const int64_t blocks = ((int64_t)std::max(g.n_rows, T) + kBlock - 1) / kBlock;
   if (blocks * B * H >= (int64_t)1 << 31) {
     set_error(std::string(fn) + ": too many work items for one launch");
@@ -372,8 +377,6 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
   }
   return ST_OK;
 }
-
-bool uses_c(int pattern) { return pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION; }
 
 // Merged heads run on the 16-bit paths only.
 int check_union_dtype(const char* fn, int pattern, bool path16) {
@@ -386,20 +389,20 @@ int check_union_dtype(const char* fn, int pattern, bool path16) {
 
 template <typename TE>
 int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* out, float* lse,
-             int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
+             int B, int H, int T, int D, int pattern, int l, int c, const int32_t* summary, void* stream) {
   const void* ptrs[] = {q, k, v, out, lse};
-  int rc = check_attn_args(fn, ptrs, 5, B, H, T, D, pattern, l, c);
+  int rc = check_attn_args(fn, ptrs, 5, B, H, T, D, pattern, l, c, summary);
   if (rc != ST_OK) return rc;
   constexpr bool k16 = Is16<TE>::value;
   rc = check_union_dtype(fn, pattern, k16);
   if (rc != ST_OK) return rc;
-  if (!uses_c(pattern)) c = 0;
+  if (!uses_summary(pattern)) c = 0;
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return hip_fail(fn, e);
   std::lock_guard<std::mutex> lock(g_mutex);
   Plan* plan = nullptr;
-  rc = get_plan({device, pattern, T, l, c, B, H}, &plan);
+  rc = get_plan({device, pattern, T, l, c, B, H, canonical_summary(pattern, l, c, summary)}, &plan);
   if (rc != ST_OK) return rc;
   FwdArgs a;
   a.q = q;
@@ -442,19 +445,19 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
 template <typename TE>
 int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const void* out,
              const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H, int T,
-             int D, int pattern, int l, int c, void* stream) {
+             int D, int pattern, int l, int c, const int32_t* summary, void* stream) {
   const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
-  int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c);
+  int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c, summary);
   if (rc != ST_OK) return rc;
   rc = check_union_dtype(fn, pattern, Is16<TE>::value);
   if (rc != ST_OK) return rc;
-  if (!uses_c(pattern)) c = 0;
+  if (!uses_summary(pattern)) c = 0;
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return hip_fail(fn, e);
   std::lock_guard<std::mutex> lock(g_mutex);
   Plan* plan = nullptr;
-  rc = get_plan({device, pattern, T, l, c, B, H}, &plan);
+  rc = get_plan({device, pattern, T, l, c, B, H, canonical_summary(pattern, l, c, summary)}, &plan);
   if (rc != ST_OK) return rc;
   // workspace: Delta, lse2, split partials, and for merged heads the first
   // pass's fp32 dq, dk, dv
@@ -585,39 +588,67 @@ extern "C" {
 
 int st_sparse_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                        int H, int T, int D, int pattern, int l, int c, void* stream) {
-  return attn_fwd<bf16>("st_sparse_attn_fwd", q, k, v, out, lse, B, H, T, D, pattern, l, c, stream);
+  return attn_fwd<bf16>("st_sparse_attn_fwd", q, k, v, out, lse, B, H, T, D, pattern, l, c, nullptr, stream);
 }
 
 int st_sparse_attn_fwd_f16(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                            int H, int T, int D, int pattern, int l, int c, void* stream) {
-  return attn_fwd<f16>("st_sparse_attn_fwd_f16", q, k, v, out, lse, B, H, T, D, pattern, l, c, stream);
+  return attn_fwd<f16>("st_sparse_attn_fwd_f16", q, k, v, out, lse, B, H, T, D, pattern, l, c, nullptr, stream);
 }
 
 int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_fwd<float>("st_sparse_attn_fwd_f32", q, k, v, out, lse, B, H, T, D, pattern, l, c,
-                         stream);
+                         nullptr, stream);
 }
 
 int st_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
                        int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_bwd<bf16>("st_sparse_attn_bwd", q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D,
-                        pattern, l, c, stream);
+                        pattern, l, c, nullptr, stream);
 }
 
 int st_sparse_attn_bwd_f16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
                            int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_bwd<f16>("st_sparse_attn_bwd_f16", q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D,
-                       pattern, l, c, stream);
+                       pattern, l, c, nullptr, stream);
 }
 
 int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream) {
   return attn_bwd<float>("st_sparse_attn_bwd_f32", q, k, v, out, lse, dout, dq, dk, dv, B, H, T,
-                         D, pattern, l, c, stream);
+                         D, pattern, l, c, nullptr, stream);
+}
+
+int st_sparse_attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                          int H, int T, int D, int pattern, int l, int c, const int32_t* summary,
+                          void* stream) {
+  const char* fn = "st_sparse_attn_fwd_ex";
+  switch (dtype) {
+    case ST_BF16: return attn_fwd<bf16>(fn, q, k, v, out, lse, B, H, T, D, pattern, l, c, summary, stream);
+    case ST_F16: return attn_fwd<f16>(fn, q, k, v, out, lse, B, H, T, D, pattern, l, c, summary, stream);
+    case ST_F32: return attn_fwd<float>(fn, q, k, v, out, lse, B, H, T, D, pattern, l, c, summary, stream);
+    default: set_error(std::string(fn) + ": unknown dtype " + std::to_string(dtype)); return ST_ERR_INVALID;
+  }
+}
+
+int st_sparse_attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
+                          int T, int D, int pattern, int l, int c, const int32_t* summary, void* stream) {
+  const char* fn = "st_sparse_attn_bwd_ex";
+  switch (dtype) {
+    case ST_BF16:
+      return attn_bwd<bf16>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary, stream);
+    case ST_F16:
+      return attn_bwd<f16>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary, stream);
+    case ST_F32:
+      return attn_bwd<float>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary,
+                             stream);
+    default: set_error(std::string(fn) + ": unknown dtype " + std::to_string(dtype)); return ST_ERR_INVALID;
+  }
 }
 
 int st_timing_enable(int on) {

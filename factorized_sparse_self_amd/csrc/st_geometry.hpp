@@ -10,8 +10,9 @@
 //   K_STRIDE      residue-major: position m*l + r <-> r*n_pad + m; the strided
 //                 set of t is the class prefix [r*n_pad, R]
 //   K_BLOCK       rows = keys = positions; [l*floor(t/l), t]
-//   K_SUMMARY     compact summary keys b*c + o <-> b*l + (l-c) + o for blocks
-//                 b < ceil(T/l) - 1; strictly earlier blocks: [0, c*floor(t/l) - 1]
+//   K_SUMMARY     compact summary keys b*c + o <-> b*l + S[o] for blocks
+//                 b < ceil(T/l) - 1, S the summary offsets (by default the last
+//                 c: S[o] = l - c + o); strictly earlier blocks: [0, c*floor(t/l) - 1]
 //   K_SUMMARY_R1  compact summary keys of every block (positions >= T are
 //                 padding); earlier blocks plus own-block summary keys <= t
 //   K_CAUSAL      rows = keys = positions; [0, t]
@@ -66,6 +67,8 @@ struct Geometry {
   int n_cls;   // K_STRIDE: number of residue classes, min(l, T)
   FastDiv div_l, div_c, div_pad;  // division by l, c (>= 1) and n_pad (>= 1)
   int blk_c;   // kBlock / c when c divides kBlock (summary blocks per LUT block), else 0
+  const int32_t* sigma;  // summary kinds: the c offsets of S, ascending (host or device
+                         // memory, as the geometry's user); null: the last c offsets
 };
 
 // A Geometry whose kind code is a compile-time constant.  The functions below
@@ -84,6 +87,32 @@ ST_HD int imax(int a, int b) { return a > b ? a : b; }
 template <class G>
 ST_HD bool residue_major(const G& g) {
   return g.code == K_STRIDE || g.code == K_STRIDE_X;
+}
+
+// Summary set S of a summary kind: offset of its o-th element, the number of
+// elements <= off, and membership (off in [0, l)).
+template <class G>
+ST_HD int summary_offset(const G& g, int o) {
+  return g.sigma ? g.sigma[o] : g.l - g.c + o;
+}
+template <class G>
+ST_HD int summary_count(const G& g, int off) {
+  if (!g.sigma) return imax(0, off - (g.l - g.c) + 1);
+  int lo = 0, hi = g.c;  // first element > off
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (g.sigma[mid] <= off)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+template <class G>
+ST_HD bool summary_member(const G& g, int off) {
+  if (!g.sigma) return off >= g.l - g.c;
+  const int n = summary_count(g, off);
+  return n > 0 && g.sigma[n - 1] == off;
 }
 
 // Position held by kernel row R, or -1 for padding / out of range.
@@ -112,7 +141,7 @@ ST_HD int key_position(const G& g, int K) {
   if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
     const int b = fdiv(K, g.div_c);
     const int o = K - b * g.c;
-    const int64_t p = (int64_t)b * g.l + (g.l - g.c) + o;
+    const int64_t p = (int64_t)b * g.l + summary_offset(g, o);
     return p < g.T ? (int)p : -1;
   }
   return K;
@@ -134,7 +163,7 @@ ST_HD int block_position(const G& g, bool keys, int blk, int i) {
   if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) {
     if (R >= g.n_keys) return -1;
     const int q = fdiv(R, g.div_c);
-    const int p = q * g.l + (g.l - g.c) + (R - q * g.c);
+    const int p = q * g.l + summary_offset(g, R - q * g.c);
     return p < g.T ? p : -1;
   }
   return R < g.T ? R : -1;
@@ -160,7 +189,7 @@ ST_HD RowPart row_part(const G& g, bool keys, int i) {
   if (residue_major(g)) return {i * g.l};
   if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) {
     const int q = fdiv(i, g.div_c);
-    return {q * g.l + (g.l - g.c) + (i - q * g.c)};
+    return {q * g.l + summary_offset(g, i - q * g.c)};
   }
   return {i};
 }
@@ -182,7 +211,7 @@ ST_HD bool position_is_key(const G& g, int t) {
   if (g.code == K_SUMMARY || g.code == K_SUMMARY_R1) {
     const int b = fdiv(t, g.div_l);
     const int off = t - b * g.l;
-    if (off < g.l - g.c) return false;
+    if (!summary_member(g, off)) return false;
     return g.code == K_SUMMARY_R1 || (int64_t)(b + 1) * g.c <= g.n_keys;
   }
   return true;
@@ -217,7 +246,7 @@ ST_HD void row_interval(const G& g, int R, int t, int& lo, int& hi) {
       const int b = fdiv(t, g.div_l);
       const int off = t - b * g.l;
       lo = 0;
-      hi = g.c * b + imax(0, off - (g.l - g.c) + 1) - 1;
+      hi = g.c * b + summary_count(g, off) - 1;
       break;
     }
     default:  // K_CAUSAL

@@ -21,12 +21,22 @@ struct KindLayout {
   std::vector<uint8_t> csc_flags;
 };
 
-// Fill the geometry of (pattern, kind); returns false on an unknown pattern.
-bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g);
+// True for the patterns with a summary kind (they take c and a summary set).
+bool uses_summary(int pattern);
 
-// Argument check shared by st_layout_build and the attention calls.
+// Fill the geometry of (pattern, kind); returns false on an unknown pattern.
+// sigma: the summary offsets (null for the last c); the geometry keeps the
+// pointer, which must outlive it.
+bool make_geometry(int pattern, int kind, int T, int l, int c, const int32_t* sigma, Geometry* g);
+
+// Argument check shared by st_layout_build and the attention calls (summary:
+// null, or c strictly ascending offsets in [0, l) for a summary pattern).
 // Returns an empty string when valid, else the reason.
-std::string check_pattern_args(int pattern, int T, int l, int c);
+std::string check_pattern_args(int pattern, int T, int l, int c, const int32_t* summary);
+
+// The summary set as stored: empty for the default set (the last c offsets,
+// whether given or not), else the c offsets.
+std::vector<int32_t> canonical_summary(int pattern, int l, int c, const int32_t* summary);
 
 // Build the CSR / CSC of one kind (the geometry must already be set).
 void build_kind(KindLayout& L);
@@ -38,5 +48,6 @@ void set_error(const std::string& msg);
 
 struct st_layout {
   int pattern, T, l, c;
+  std::vector<int32_t> summary;  // non-default summary offsets (the geometries point here)
   st::KindLayout kind[2];
 };

@@ -26,7 +26,12 @@ void set_error(const std::string& msg) { g_last_error = msg; }
 
 static const char* last_error_cstr() { return g_last_error.c_str(); }
 
-bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g) {
+bool uses_summary(int pattern) {
+  return pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION;
+}
+
+bool make_geometry(int pattern, int kind, int T, int l, int c, const int32_t* sigma, Geometry* g) {
+  g->sigma = sigma;
   g->T = T;
   g->l = l;
   g->c = c;
@@ -61,14 +66,30 @@ bool make_geometry(int pattern, int kind, int T, int l, int c, Geometry* g) {
   return true;
 }
 
-std::string check_pattern_args(int pattern, int T, int l, int c) {
+std::string check_pattern_args(int pattern, int T, int l, int c, const int32_t* summary) {
   if (pattern < ST_STRIDED || pattern > ST_FIXED_UNION) return "unknown pattern " + std::to_string(pattern);
   if (T < 1 || T > (1 << 24)) return "T must be in [1, 2^24], got " + std::to_string(T);
   if (l < 1 || l > (1 << 24)) return "l must be in [1, 2^24], got " + std::to_string(l);
-  if ((pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION) && (c < 1 || c > l))
+  if (uses_summary(pattern) && (c < 1 || c > l))
     return "c must be in [1, l] for the fixed patterns, got c=" + std::to_string(c) +
            " l=" + std::to_string(l);
+  if (summary) {
+    if (!uses_summary(pattern)) return "a summary set is only taken by the fixed patterns";
+    for (int o = 0; o < c; ++o) {
+      if (summary[o] < 0 || summary[o] >= l)
+        return "summary offset " + std::to_string(summary[o]) + " is not in [0, l)";
+      if (o > 0 && summary[o] <= summary[o - 1]) return "summary offsets must be strictly ascending";
+    }
+  }
   return std::string();
+}
+
+std::vector<int32_t> canonical_summary(int pattern, int l, int c, const int32_t* summary) {
+  if (!summary || !uses_summary(pattern)) return {};
+  bool tail = true;
+  for (int o = 0; o < c; ++o) tail = tail && summary[o] == l - c + o;
+  if (tail) return {};
+  return std::vector<int32_t>(summary, summary + c);
 }
 
 void build_kind(KindLayout& L) {
@@ -134,15 +155,16 @@ using namespace st;
 
 extern "C" {
 
-int st_layout_build(int pattern, int T, int l, int c, st_layout** out) {
+static int layout_build(const char* fn, int pattern, int T, int l, int c, const int32_t* summary,
+                        st_layout** out) {
   if (!out) {
-    set_error("st_layout_build: out is null");
+    set_error(std::string(fn) + ": out is null");
     return ST_ERR_INVALID;
   }
   *out = nullptr;
-  const std::string why = check_pattern_args(pattern, T, l, c);
+  const std::string why = check_pattern_args(pattern, T, l, c, summary);
   if (!why.empty()) {
-    set_error("st_layout_build: " + why);
+    set_error(std::string(fn) + ": " + why);
     return ST_ERR_INVALID;
   }
   st_layout* lay = new (std::nothrow) st_layout;
@@ -153,19 +175,29 @@ int st_layout_build(int pattern, int T, int l, int c, st_layout** out) {
   lay->pattern = pattern;
   lay->T = T;
   lay->l = l;
-  lay->c = (pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION) ? c : 0;
+  lay->c = uses_summary(pattern) ? c : 0;
   try {
+    lay->summary = canonical_summary(pattern, l, c, summary);
+    const int32_t* sigma = lay->summary.empty() ? nullptr : lay->summary.data();
     for (int kind = 0; kind < 2; ++kind) {
-      make_geometry(pattern, kind, T, l, lay->c, &lay->kind[kind].geo);
+      make_geometry(pattern, kind, T, l, lay->c, sigma, &lay->kind[kind].geo);
       build_kind(lay->kind[kind]);
     }
   } catch (const std::bad_alloc&) {
     delete lay;
-    set_error("st_layout_build: out of host memory");
+    set_error(std::string(fn) + ": out of host memory");
     return ST_ERR_NOMEM;
   }
   *out = lay;
   return ST_OK;
+}
+
+int st_layout_build(int pattern, int T, int l, int c, st_layout** out) {
+  return layout_build("st_layout_build", pattern, T, l, c, nullptr, out);
+}
+
+int st_layout_build_ex(int pattern, int T, int l, int c, const int32_t* summary, st_layout** out) {
+  return layout_build("st_layout_build_ex", pattern, T, l, c, summary, out);
 }
 
 static const KindLayout* kind_of(const st_layout* lay, int kind, const char* fn) {

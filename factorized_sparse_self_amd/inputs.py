@@ -23,6 +23,11 @@ PATTERN_NAMES = {STRIDED: "strided", FIXED: "fixed", FIXED_R1: "fixed_r1", DENSE
                  STRIDED_UNION: "strided_union", FIXED_UNION: "fixed_union"}
 
 
+def summary_offsets(l: int, c) -> tuple:
+    """A workload's summary offsets: the last c of each block, or the given ones."""
+    return tuple(range(l - c, l)) if isinstance(c, int) else tuple(sorted(c))
+
+
 @dataclass(frozen=True)
 class Workload:
     """One attention problem: pattern, shapes, dtype and the passes it runs."""
@@ -34,7 +39,7 @@ class Workload:
     T: int
     D: int
     l: int
-    c: int
+    c: object  # summary count (its last c offsets), or the summary offsets (a tuple)
     dtype: str  # "bf16", "f16" or "f32"
     backward: bool
     seed: int
@@ -77,6 +82,8 @@ EXTRA_WORKLOADS = [
              note="merged heads: window plus strided keys in every head"),
     Workload("fixed_T12288_f16_fwdbwd", FIXED, 4, 8, 12288, 64, 128, 8, "f16", True, 1010,
              note="the fixed workload with fp16 (IEEE binary16) inputs"),
+    Workload("fixed_spread_T12288_bf16_fwdbwd", FIXED, 4, 8, 12288, 64, 128, tuple(range(0, 128, 16)), "bf16",
+             True, 1011, note="the fixed workload with 8 summary offsets spread over each block"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

@@ -81,6 +81,13 @@ typedef enum st_status {
   ST_ERR_NOMEM = -4        /* host or device allocation failed */
 } st_status;
 
+/* Element type of the tensors, for the _ex attention entry points. */
+typedef enum {
+  ST_BF16 = 0, /* bfloat16 (the unsuffixed entry points) */
+  ST_F16 = 1,  /* IEEE binary16 (the _f16 entry points)   */
+  ST_F32 = 2   /* fp32 (the _f32 entry points)            */
+} st_dtype;
+
 typedef enum st_pattern {
   ST_STRIDED = 0,
   ST_FIXED = 1,
@@ -134,6 +141,17 @@ enum {
  * arguments, ST_ERR_NOMEM on allocation failure. */
 int st_layout_build(int pattern, int T, int l, int c, st_layout** out);
 
+/* Summary sets.  The fixed patterns' summary kind attends, in every l-block,
+ * the keys at the offsets of a summary set S (llm-arch-kb §2, Pattern B: a
+ * fixed set of offsets within each block; its §3 mask sketch takes it as an
+ * argument).  The entry points without `summary` use the last c offsets
+ * (nlp-lineage, "The idea": summary positions at the end of each block).
+ * `summary`: NULL (the last c offsets), or c offsets in [0, l), strictly
+ * ascending, in host memory, read during the call only.  Only the fixed
+ * patterns take one (ST_ERR_INVALID otherwise, or for a malformed set).
+ * Compact summary key b*c + o then holds position b*l + summary[o]. */
+int st_layout_build_ex(int pattern, int T, int l, int c, const int32_t* summary, st_layout** out);
+
 /* dims[ST_DIM_COUNT] of head kind 0 or 1. */
 int st_layout_dims(const st_layout* lay, int kind, int32_t* dims);
 
@@ -182,6 +200,17 @@ int st_sparse_attn_fwd_f16(const void* q, const void* k, const void* v, void* ou
 int st_sparse_attn_bwd_f16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream);
+
+/* Forward and backward with an element type code and a summary set (see
+ * st_layout_build_ex); otherwise as the entry points above.  An unknown dtype
+ * gives ST_ERR_INVALID. */
+int st_sparse_attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int H, int T, int D, int pattern, int l, int c,
+                          const int32_t* summary, void* stream);
+int st_sparse_attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                          int H, int T, int D, int pattern, int l, int c, const int32_t* summary,
+                          void* stream);
 
 /* fp32 twins: same arguments, fp32 tensors. */
 int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -3,6 +3,7 @@
 // key_position() for every kernel row and key of many geometries.
 #include <cstdio>
 #include <cstdlib>
+#include <vector>
 
 #include "../../factorized_sparse_self_amd/csrc/st_internal.hpp"
 #include "../../include/st.h"
@@ -18,9 +19,28 @@ int main() {
     for (int T : Ts)
       for (int l : ls)
         for (int c = 1; c <= l && c <= 9; c += (c < 4 ? 1 : 4)) {
+          // the default summary set (last c offsets) and a spread one, o*l/c
+          std::vector<int32_t> spread(c);
+          for (int o = 0; o < c; ++o) spread[o] = (int32_t)((long)o * l / c);
+          const bool fixed = pattern == ST_FIXED || pattern == ST_FIXED_R1 || pattern == ST_FIXED_UNION;
+          for (int variant = 0; variant < (fixed ? 2 : 1); ++variant)
           for (int kind = 0; kind < 2; ++kind) {
             Geometry g;
-            make_geometry(pattern, kind, T, l, c, &g);
+            make_geometry(pattern, kind, T, l, c, variant ? spread.data() : nullptr, &g);
+            // a position is a kernel key exactly when position_is_key says so
+            {
+              std::vector<char> is_key(T, 0);
+              for (int K = 0; K < g.n_keys; ++K) {
+                const int p = key_position(g, K);
+                if (p >= 0) is_key[p] = 1;
+              }
+              for (int t = 0; t < T; ++t)
+                if ((bool)is_key[t] != position_is_key(g, t)) {
+                  std::printf("key set mismatch p%d T%d l%d c%d kind%d var%d t%d\n", pattern, T, l, c, kind,
+                              variant, t);
+                  return 1;
+                }
+            }
             const int nrb = (g.n_rows + kBlock - 1) / kBlock, nkb = (g.n_keys + kBlock - 1) / kBlock;
             for (int b = 0; b < nrb; ++b)
               for (int i = 0; i < kBlock; ++i) {

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("st_layout_build", "st_sparse_attn_fwd", "st_sparse_attn_bwd", "st_sparse_attn_fwd_f16",
               "st_sparse_attn_bwd_f16", "st_sparse_attn_fwd_f32",
-              "st_sparse_attn_bwd_f32", "st_layout_csr", "st_layout_csc", "st_layout_maps"):
+              "st_sparse_attn_bwd_f32", "st_layout_csr", "st_layout_csc", "st_layout_maps",
+              "st_layout_build_ex", "st_sparse_attn_fwd_ex", "st_sparse_attn_bwd_ex"):
         assert n in names
 
 
@@ -89,3 +90,17 @@ def test_backward_argument_errors_without_gpu():
     args[5] = None
     assert L.st_sparse_attn_bwd(*args, 1, 2, 64, 64, 0, 8, 0, None) == -1
     assert b"pointer 5" in L.st_last_error()
+
+
+def test_extended_entry_points_check_dtype_and_summary_without_gpu():
+    from factorized_sparse_self_amd import lib
+    L = lib()
+    fake = 1 << 20
+    good = (ctypes.c_int32 * 2)(1, 5)
+    bad = (ctypes.c_int32 * 2)(5, 1)
+    assert L.st_sparse_attn_fwd_ex(7, fake, fake, fake, fake, fake, 1, 2, 64, 64, 1, 8, 2, good, None) == -1
+    assert b"unknown dtype" in L.st_last_error()
+    assert L.st_sparse_attn_fwd_ex(0, fake, fake, fake, fake, fake, 1, 2, 64, 64, 1, 8, 2, bad, None) == -1
+    assert b"ascending" in L.st_last_error()
+    assert L.st_sparse_attn_bwd_ex(1, *([fake] * 9), 1, 2, 64, 64, 0, 8, 0, good, None) == -1
+    assert b"only taken by the fixed patterns" in L.st_last_error()

@@ -157,6 +157,55 @@ def test_small_merged_heads(case, dtype):
     assert_close(f64(dv), rv, dtype, "dv")
 
 
+# General summary sets (offsets within each l-block) for the fixed patterns
+SMALL_SIGMA = [
+    (inputs.FIXED, 2, 3, 300, 64, 16, (0, 5, 9)),
+    (inputs.FIXED, 1, 2, 333, 32, 20, (0, 7, 19)),
+    (inputs.FIXED_R1, 1, 2, 300, 64, 16, (2, 15)),
+    (inputs.FIXED_R1, 1, 2, 260, 64, 5, (0,)),
+    (inputs.FIXED_UNION, 1, 2, 250, 64, 32, (0, 31)),
+    (inputs.FIXED_UNION, 1, 3, 200, 64, 16, (3, 4, 8, 12)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("case", SMALL_SIGMA, ids=lambda c: f"p{c[0]}_H{c[2]}T{c[3]}D{c[4]}l{c[5]}S{'-'.join(map(str, c[6]))}")
+def test_small_summary_sets(case, dtype):
+    pattern, B, H, T, D, l, S = case
+    if dtype == "f32" and pattern == inputs.FIXED_UNION:
+        pytest.skip("merged heads run on 16-bit inputs only")
+    log(f"small summary set fwd+bwd {case} {dtype}")
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=23 + T + l, n=4)
+    out, lse = run_fwd(q, k, v, pattern, l, S)
+    qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
+    O, L = oracle.forward(qn, kn, vn, pattern, l, S)
+    assert_close(f64(out), O, dtype, "out")
+    assert_close(f64(lse), L, "f32", "lse")
+    dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, S)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, S)
+    assert_close(f64(dq), rq, dtype, "dq")
+    assert_close(f64(dk), rk, dtype, "dk")
+    assert_close(f64(dv), rv, dtype, "dv")
+    if pattern == inputs.FIXED:
+        # summary heads: positions outside S, and the last block, are never attended
+        pos = torch.arange(T)
+        never = ~torch.isin(pos % l, torch.tensor(S)) | (pos >= (-(-T // l) - 1) * l)
+        dkc, dvc = dk.cpu(), dv.cpu()
+        assert (dkc[:, 1::2][:, :, never] == 0).all() and (dvc[:, 1::2][:, :, never] == 0).all()
+
+
+def test_explicit_default_summary_set_matches_count():
+    """The last c offsets given explicitly run the same plan: identical bits."""
+    B, H, T, D, l, c = 1, 2, 300, 64, 16, 3
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=31, n=4)
+    o1, l1 = run_fwd(q, k, v, inputs.FIXED_R1, l, c)
+    o2, l2 = run_fwd(q, k, v, inputs.FIXED_R1, l, (13, 14, 15))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = run_bwd(q, k, v, o1, l1, do, inputs.FIXED_R1, l, c)
+    g2 = run_bwd(q, k, v, o1, l1, do, inputs.FIXED_R1, l, (13, 14, 15))
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
 def test_edge_shapes():
     """T = 1, T < l, l = 1, c = l, a single row block, odd H."""
     cases = [
@@ -259,13 +308,15 @@ def _keys_for_head(w, kind, n, seed):
     rng = np.random.default_rng(seed + kind)
     if w.pattern in (inputs.FIXED, inputs.FIXED_R1) and kind == 1:
         nb = -(-w.T // w.l)
+        S = inputs.summary_offsets(w.l, w.c)
         blocks = sorted({0, 1, nb // 2, nb - 2} | set(int(b) for b in rng.integers(0, nb - 1, size=2)))
-        return np.array([b * w.l + w.l - w.c + int(rng.integers(0, w.c)) for b in blocks], dtype=np.int64)
+        return np.array([b * w.l + S[int(rng.integers(0, len(S)))] for b in blocks], dtype=np.int64)
     if w.pattern == inputs.FIXED_UNION:
         # summary positions (attended by their own block and every later one),
         # other positions, and the last block's summary positions
         nb = -(-w.T // w.l)
-        keys = {b * w.l + w.l - w.c + int(rng.integers(0, w.c)) for b in (0, 1, nb // 2, nb - 2, nb - 1)}
+        S = inputs.summary_offsets(w.l, w.c)
+        keys = {b * w.l + S[int(rng.integers(0, len(S)))] for b in (0, 1, nb // 2, nb - 2, nb - 1)}
         keys |= set(int(x) for x in rng.choice(w.T, size=n // 2, replace=False)) | {0, w.T - 1}
         return np.array(sorted(k for k in keys if k < w.T), dtype=np.int64)
     if w.pattern == inputs.DENSE:
@@ -311,7 +362,7 @@ def test_workload_forward_backward_sampled(w):
         # summary heads: non-summary positions are never attended; under FIXED the
         # last block's summary positions are not either (no later block)
         pos = torch.arange(w.T)
-        never = (pos % w.l) < w.l - w.c
+        never = ~torch.isin(pos % w.l, torch.tensor(inputs.summary_offsets(w.l, w.c)))
         if w.pattern == inputs.FIXED:
             never |= pos >= (w.T // w.l - 1) * w.l
         dkc, dvc = dk.cpu(), dv.cpu()

@@ -24,6 +24,10 @@ CASES = [(w.pattern, w.T, w.l, w.c) for w in inputs.WORKLOADS] + [
     (inputs.STRIDED_UNION, 250, 16, 0), (inputs.STRIDED_UNION, 12288, 128, 0), (inputs.STRIDED_UNION, 129, 1, 0),
     (inputs.STRIDED_UNION, 1, 5, 0), (inputs.STRIDED_UNION, 1000, 96, 0), (inputs.FIXED_UNION, 250, 16, 3),
     (inputs.FIXED_UNION, 12288, 128, 8), (inputs.FIXED_UNION, 333, 20, 20), (inputs.FIXED_UNION, 1, 1, 1),
+    # general summary sets (offsets within each l-block)
+    (inputs.FIXED, 250, 16, (0, 5, 9)), (inputs.FIXED, 12288, 128, tuple(range(0, 128, 16))),
+    (inputs.FIXED, 300, 20, (0, 7, 19)), (inputs.FIXED_R1, 250, 16, (2, 15)), (inputs.FIXED_R1, 300, 20, (0,)),
+    (inputs.FIXED_R1, 1000, 96, (1, 2, 50, 95)), (inputs.FIXED_UNION, 256, 32, (0, 31)),
 ]
 
 
@@ -55,9 +59,21 @@ def test_layout_block_counts_of_the_workloads():
     assert fixed[1]["nnz"] == 1224 and int(fixed[1]["flags"].sum()) == 1056
 
 
+def test_explicit_tail_summary_is_the_default_layout():
+    from factorized_sparse_self_amd import st_layout_build
+    a = st_layout_build(inputs.FIXED_R1, 250, 16, 3)
+    b = st_layout_build(inputs.FIXED_R1, 250, 16, (13, 14, 15))
+    for kind in (0, 1):
+        for key in a[kind]:
+            np.testing.assert_array_equal(a[kind][key], b[kind][key])
+
+
 @pytest.mark.parametrize("args", [(9, 100, 8, 2), (inputs.FIXED, 100, 8, 0), (inputs.FIXED, 100, 8, 9),
                                   (inputs.STRIDED, 0, 8, 0), (inputs.STRIDED, 100, 0, 0),
-                                  (inputs.STRIDED, (1 << 24) + 1, 8, 0)])
+                                  (inputs.STRIDED, (1 << 24) + 1, 8, 0),
+                                  (inputs.FIXED, 100, 8, (3, 2)), (inputs.FIXED, 100, 8, (1, 1)),
+                                  (inputs.FIXED, 100, 8, (0, 8)), (inputs.FIXED_R1, 100, 8, (-1,)),
+                                  (inputs.STRIDED, 100, 8, (1,)), (inputs.DENSE, 100, 8, (0,))])
 def test_layout_rejects_bad_arguments(args):
     from factorized_sparse_self_amd import StError, st_layout_build
     with pytest.raises(StError) as e:
