@@ -364,8 +364,8 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
     set_error(std::string(fn) + ": " + why);
     return ST_ERR_INVALID;
   }
-  if (D != 32 && D != 64) {
-    set_error(std::string(fn) + ": head dimension D must be 32 or 64, got " + std::to_string(D));
+  if (D != 32 && D != 64 && D != 128) {
+    set_error(std::string(fn) + ": head dimension D must be 32, 64 or 128, got " + std::to_string(D));
     return ST_ERR_UNSUPPORTED;
   }
   Geometry g;
@@ -436,7 +436,9 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
     a.pairs = P.pair_items;
     const int n_items = k16 ? P.n_pair_items : P.n_row_items;
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
-    e = (D == 32) ? launch_fwd<TE, 32>(a, n_items, s) : launch_fwd<TE, 64>(a, n_items, s);
+    e = D == 32 ? launch_fwd<TE, 32>(a, n_items, s)
+        : D == 64 ? launch_fwd<TE, 64>(a, n_items, s)
+                  : launch_fwd<TE, 128>(a, n_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ST_OK;
@@ -505,8 +507,9 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
     const int n_dq = Is16<TE>::value ? P.n_pair_items : P.n_row_items;
     a.dkdv_items = P.dkdv_items;
     a.red_items = P.red_items;
-    e = (D == 32) ? launch_bwd<TE, 32>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
-                  : launch_bwd<TE, 64>(a, n_dq, P.n_dkdv_items, P.n_red_items, s);
+    e = D == 32 ? launch_bwd<TE, 32>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
+        : D == 64 ? launch_bwd<TE, 64>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
+                  : launch_bwd<TE, 128>(a, n_dq, P.n_dkdv_items, P.n_red_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ST_OK;

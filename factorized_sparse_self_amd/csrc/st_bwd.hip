@@ -443,8 +443,8 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
     if (!stager) return;
     int p[SNI];
     stage.positions(g, true, (int)(entry & kPairBlockMask), p);
-    stage_rows<D>(rk, lds_rows + stg * STAGE, lane, p);
-    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, lane, p);
+    stage_rows<D>(rk, lds_rows + stg * STAGE, SR * swave, lane, p);
+    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, SR * swave, lane, p);
   };
   // The first NS-1 key blocks are in flight while the rows' own operands load
   // (those loads are younger, so the compiler's waits for them cover the ring's
@@ -644,8 +644,8 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     const uint32_t so = stg * (uint32_t)sizeof(Stage);
     int p[S::NI];
     stage.positions(g, false, qb, p);
-    stage_rows<D>(rq, lds_rows + so, lane, p);
-    stage_rows<D>(rg, lds_rows + so + S::BYTES, lane, p);
+    stage_rows<D>(rq, lds_rows + so, 16 * wave, lane, p);
+    stage_rows<D>(rg, lds_rows + so + S::BYTES, 16 * wave, lane, p);
     int tp[1];
     stage_own.positions(g, false, qb, tp);
     int lo = 1, hi = 0;
@@ -666,8 +666,8 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     const StageRows<S::NI, S::RPI> kstage(g, true, 16 * wave + lane / S::CH);
     int p[S::NI];
     kstage.positions(g, true, kb, p);
-    stage_rows<D>(rk, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage), lane, p);
-    stage_rows<D>(rv, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage) + S::BYTES, lane, p);
+    stage_rows<D>(rk, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage), 16 * wave, lane, p);
+    stage_rows<D>(rv, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage) + S::BYTES, 16 * wave, lane, p);
   }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
@@ -873,9 +873,12 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
 
 template hipError_t launch_bwd<bf16, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<f16, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<f16, 64>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<f16, 128>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<float, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd<float, 64>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd<float, 128>(const BwdArgs&, int, int, int, hipStream_t);
 
 }  // namespace st

@@ -264,8 +264,8 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
   auto issue = [&](uint32_t entry, int stg) {
     int p[S::NI];
     stage.positions(g, true, (int)(entry & kPairBlockMask), p);
-    stage_rows<D>(rk, lds_rows + stg * STAGE, lane, p);
-    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, lane, p);
+    stage_rows<D>(rk, lds_rows + stg * STAGE, 16 * wave, lane, p);
+    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, 16 * wave, lane, p);
   };
 
   const int e0 = item.e0, e1 = item.e1;
@@ -279,7 +279,7 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
     for (int hb = 0; hb < 2; ++hb) {
       int p[S::NI];
       qstage.positions(g, false, 2 * pb + hb, p);
-      stage_rows<D>(rq, lds_rows + (NS - 1) * STAGE + hb * S::BYTES, lane, p);
+      stage_rows<D>(rq, lds_rows + (NS - 1) * STAGE + hb * S::BYTES, 16 * wave, lane, p);
     }
   }
 #pragma unroll
@@ -467,9 +467,12 @@ hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
 
 template hipError_t launch_fwd<bf16, 32>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<bf16, 64>(const FwdArgs&, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 128>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<f16, 32>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<f16, 64>(const FwdArgs&, int, hipStream_t);
+template hipError_t launch_fwd<f16, 128>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<float, 32>(const FwdArgs&, int, hipStream_t);
 template hipError_t launch_fwd<float, 64>(const FwdArgs&, int, hipStream_t);
+template hipError_t launch_fwd<float, 128>(const FwdArgs&, int, hipStream_t);
 
 }  // namespace st

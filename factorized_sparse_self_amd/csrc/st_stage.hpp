@@ -67,17 +67,17 @@ __device__ __forceinline__ void lds_dma(Rsrc r, uint32_t lds_base, uint32_t voff
 #pragma clang diagnostic pop
 
 // Stage N*RPI rows of one 64-row tile of a [T, D] 16-bit tensor (N = NI: the
-// wave's 16 rows): `rows` is the wave-uniform LDS address of the first of them
-// (a multiple of CH rows into a tile), pos[i] the position for row
-// i*RPI + lane/CH of them, or -1 for padding.  The chunk a lane fetches is the
-// one that its LDS slot holds after the swizzle; the swizzle depends only on
-// the row modulo CH, which the first row's offset does not change.
+// wave's 16 rows): `rows` is the wave-uniform LDS address of the first of them,
+// tile row `row0`; pos[i] is the position for tile row row0 + i*RPI + lane/CH,
+// or -1 for padding.  The chunk a lane fetches is the one that its LDS slot
+// holds after the swizzle of its row (row mod CH).
 template <int D, int N>
-__device__ __forceinline__ void stage_rows(Rsrc src, uint32_t rows, int lane, const int (&pos)[N]) {
+__device__ __forceinline__ void stage_rows(Rsrc src, uint32_t rows, int row0, int lane, const int (&pos)[N]) {
   using S = TileShape<D>;
-  const int lc = (lane % S::CH) ^ ((lane / S::CH) & (S::CH - 1));  // logical chunk this lane fetches
 #pragma unroll
   for (int i = 0; i < N; ++i) {
+    const int r = row0 + i * S::RPI + lane / S::CH;              // tile row this lane fills
+    const int lc = (lane % S::CH) ^ (r & (S::CH - 1));           // logical chunk this lane fetches
     const uint32_t off = pos[i] >= 0 ? (uint32_t)(pos[i] * S::RB + lc * 16) : kOutOfRange;
     lds_dma<16>(src, rows + i * S::RPI * S::RB, off);
   }

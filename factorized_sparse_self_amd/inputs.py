@@ -84,6 +84,8 @@ EXTRA_WORKLOADS = [
              note="the fixed workload with fp16 (IEEE binary16) inputs"),
     Workload("fixed_spread_T12288_bf16_fwdbwd", FIXED, 4, 8, 12288, 64, 128, tuple(range(0, 128, 16)), "bf16",
              True, 1011, note="the fixed workload with 8 summary offsets spread over each block"),
+    Workload("fixed_D128_T12288_bf16_fwdbwd", FIXED, 4, 8, 12288, 128, 128, 8, "bf16", True, 1012,
+             note="the fixed workload with head dimension 128"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 

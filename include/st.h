@@ -76,7 +76,7 @@ extern "C" {
 typedef enum st_status {
   ST_OK = 0,
   ST_ERR_INVALID = -1,     /* bad argument: null/misaligned pointer, size out of range */
-  ST_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (e.g. D not 32 or 64) */
+  ST_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (e.g. D not 32, 64 or 128) */
   ST_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
   ST_ERR_NOMEM = -4        /* host or device allocation failed */
 } st_status;
@@ -173,7 +173,7 @@ void st_layout_free(st_layout* lay);
 
 /* ---------------------------------------------------------------------------
  * Attention.  Shapes: 1 <= B, 1 <= H, B*H <= 2^20, 1 <= T <= 2^24,
- * D in {32, 64}; pattern, l and c as for st_layout_build.  Every pointer must
+ * D in {32, 64, 128}; pattern, l and c as for st_layout_build.  Every pointer must
  * be non-null and 16-byte aligned, and the tensors must not overlap (except
  * that inputs may alias one another).
  * ------------------------------------------------------------------------- */

@@ -66,8 +66,8 @@ def test_attention_argument_errors_without_gpu(name):
     assert _call_fwd(name, fake, pattern=1, c=0) == -1
     assert _call_fwd(name, fake, pattern=1, l=4, c=5) == -1
     assert _call_fwd(name, fake, D=48) == -2
-    assert _call_fwd(name, fake, D=128) == -2
-    assert b"D must be 32 or 64" in lib().st_last_error()
+    assert _call_fwd(name, fake, D=256) == -2
+    assert b"D must be 32, 64 or 128" in lib().st_last_error()
     assert _call_fwd(name, fake, pattern=5, c=0) == -1   # merged fixed heads need c too
 
 

@@ -206,6 +206,37 @@ def test_explicit_default_summary_set_matches_count():
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
 
 
+# Head dimension 128
+SMALL_D128 = [
+    (inputs.STRIDED, 1, 2, 300, 128, 16, 0),
+    (inputs.FIXED, 1, 3, 250, 128, 32, 4),
+    (inputs.FIXED_R1, 1, 2, 200, 128, 16, (1, 9)),
+    (inputs.DENSE, 1, 2, 130, 128, 16, 0),
+    (inputs.STRIDED_UNION, 1, 2, 190, 128, 20, 0),
+    (inputs.FIXED_UNION, 1, 2, 200, 128, 16, 3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("case", SMALL_D128, ids=lambda c: f"p{c[0]}_H{c[2]}T{c[3]}l{c[5]}")
+def test_small_head_dim_128(case, dtype):
+    pattern, B, H, T, D, l, c = case
+    if dtype == "f32" and pattern in (inputs.STRIDED_UNION, inputs.FIXED_UNION):
+        pytest.skip("merged heads run on 16-bit inputs only")
+    log(f"small D=128 fwd+bwd {case} {dtype}")
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=41 + T + l, n=4)
+    out, lse = run_fwd(q, k, v, pattern, l, c)
+    qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
+    O, L = oracle.forward(qn, kn, vn, pattern, l, c)
+    assert_close(f64(out), O, dtype, "out")
+    assert_close(f64(lse), L, "f32", "lse")
+    dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+    assert_close(f64(dq), rq, dtype, "dq")
+    assert_close(f64(dk), rk, dtype, "dk")
+    assert_close(f64(dv), rv, dtype, "dv")
+
+
 def test_edge_shapes():
     """T = 1, T < l, l = 1, c = l, a single row block, odd H."""
     cases = [
