@@ -481,7 +481,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = (float*)wb;
+  a.ndelta = (float*)wb;
   a.lse2 = (float*)(wb + delta_bytes);
   a.partial = (float*)(wb + 2 * delta_bytes);
   a.carry_dq = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes) : nullptr;

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_f32_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) part += xor_shfl(part, m);
   if (!valid) return;
-  if (ch == 0) a.delta[row] = part;
+  if (ch == 0) a.ndelta[row] = -part;
   const int bh = (int)(row / a.T), t = (int)(row - (int64_t)bh * a.T);
   const Geometry& g = a.kinds[(bh % a.H) & 1].geo;
   if (!position_is_key(g, t)) {
@@ -121,10 +121,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a) {
   const int wlo = wave_min(lo <= hi ? lo : 0x7fffffff);
   const int whi = wave_max(lo <= hi ? hi : -1);
   const bool wave_active = whi >= 0;
-  float lse2 = 0.f, delta = 0.f;
+  float lse2 = 0.f, ndelta = 0.f;
   if (t >= 0 && lo <= hi) {
     lse2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
-    delta = a.delta[(size_t)bh * a.T + t];
+    ndelta = a.ndelta[(size_t)bh * a.T + t];
   }
 
   float qop[NQ], gop[NQ];
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a) {
         const int Kk = k0 + 16 * b + 4 * lg + i;
         const bool in = full || (Kk >= lo && Kk <= hi);
         const float p = in ? fast_exp2(fmaf(s[b][i], sl2, -lse2)) : 0.f;
-        s[b][i] = p * (dp[b][i] - delta);
+        s[b][i] = p * (dp[b][i] + ndelta);
       }
     // dq^T += K^T ds^T
 #pragma unroll
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
         row_interval(g, R, t, lo, hi);
         if (lo <= hi) {
           l2 = a.lse[(size_t)bh * a.T + t] * kLog2e;
-          de = a.delta[(size_t)bh * a.T + t];
+          de = a.ndelta[(size_t)bh * a.T + t];
         }
       }
       los[tid] = lo;
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
         const bool in = full || (Kl >= loa[i] && Kl <= hia[i]);
         const float p = in ? fast_exp2(fmaf(s[b][i], sl2, -l2a[i])) : 0.f;
         s[b][i] = p;
-        dp[b][i] = p * (dp[b][i] - dea[i]);
+        dp[b][i] = p * (dp[b][i] + dea[i]);
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS
@@ -479,6 +479,8 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
   const float lse2 =
       row_live ? buf_load_f32(make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4), (uint32_t)t * 4) * kLog2e
                : 0.f;
+  // dP^T accumulates onto -Delta, so dS = P * acc (this lane's column is row t)
+  const f32x4 ndelta4 = {-delta, -delta, -delta, -delta};
   // per-lane byte offsets of the MFMA operand reads inside a staged block:
   // row operand k at a_off ^ (64 k) (chunk 4k + lg), transposed read d at
   // t_off ^ (32 d) (chunk 2d + ...): the swizzle XORs only the chunk bits
@@ -501,11 +503,12 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
     if (!(hbits & kPairVisit)) continue;  // the other row block's key block
     const unsigned char* Kt = ring[stg][0];
     const unsigned char* Vt = ring[stg][1];
-    // S^T = K Q^T and dP^T = V dO^T
+    // S^T = K Q^T and dP^T - Delta = V dO^T - Delta
     f32x4 sc[4], dp[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dp[b] = ndelta4;
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
         sc[b] = mfma16(*(const V8*)(Kt + 16 * b * S::RB + (a_off ^ (64 * k))), qop[k], sc[b]);
@@ -527,7 +530,7 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[b][i] *= dp[b][i] - delta;
+      for (int i = 0; i < 4; ++i) sc[b][i] *= dp[b][i];
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -545,7 +548,7 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
   // first pass of a merged head writes them for every row; its second pass
   // holds rows that attend nothing, whose values it would zero)
   if (t >= 0 && lg == 0 && a.out_mode != OUT_MERGE) {
-    a.delta[(size_t)bh * a.T + t] = delta;
+    a.ndelta[(size_t)bh * a.T + t] = -delta;
     a.lse2[(size_t)bh * a.T + t] = lse2;
   }
   // keys nobody attends (positions outside a summary head's key map) get
@@ -589,7 +592,7 @@ struct DkdvStage {
   unsigned char q[TileShape<D>::BYTES];
   unsigned char g[TileShape<D>::BYTES];
   float lse2[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 16)
-  float delta[4 * 64];
+  float ndelta[4 * 64];  // -Delta
   int lo[kBlock];       // masking base of each row
   int span[kBlock];     // masking span (unsigned)
 };
@@ -611,7 +614,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   const Rsrc rv = make_rsrc((const E*)a.v + base, head_bytes);
   const Rsrc rg = make_rsrc((const E*)a.dout + base, head_bytes);
   const Rsrc rl = make_rsrc(a.lse2 + (size_t)bh * a.T, (uint32_t)a.T * 4);
-  const Rsrc rd = make_rsrc(a.delta + (size_t)bh * a.T, (uint32_t)a.T * 4);
+  const Rsrc rd = make_rsrc(a.ndelta + (size_t)bh * a.T, (uint32_t)a.T * 4);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
@@ -635,7 +638,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   // LDS addresses, in stage 0, of this wave's 16 Q rows (dO follows at
   // +BYTES) and of its lse2 slot (Delta follows at +DELTA); stage s at
   // +s*sizeof(Stage)
-  constexpr uint32_t DELTA = offsetof(Stage, delta) - offsetof(Stage, lse2);
+  constexpr uint32_t DELTA = offsetof(Stage, ndelta) - offsetof(Stage, lse2);
   static_assert(offsetof(Stage, g) - offsetof(Stage, q) == S::BYTES, "stage layout");
   const uint32_t lds_rows = lds_address(&ring[0].q[16 * wave * S::RB]);
   const uint32_t lds_vals = lds_address(&ring[0].lse2[64 * wave]);
@@ -689,10 +692,13 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     }
     if (e + NS - 1 < item.e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
     const Stage& st = ring[stg];
+    // S = Q K^T, and dP - Delta = dO V^T - Delta with the accumulators
+    // starting at -Delta of rows 16b + 4lg + i
     f32x4 sc[4], dp[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      sc[b] = dp[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dp[b] = *(const f32x4*)(&st.ndelta[64 * b + 4 * lg]);
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
         sc[b] = mfma16(*(const V8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[b]);
@@ -720,13 +726,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
       }
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float4 de = *(const float4*)(&st.delta[64 * b + 4 * lg]);
-      dp[b][0] = sc[b][0] * (dp[b][0] - de.x);
-      dp[b][1] = sc[b][1] * (dp[b][1] - de.y);
-      dp[b][2] = sc[b][2] * (dp[b][2] - de.z);
-      dp[b][3] = sc[b][3] * (dp[b][3] - de.w);
-    }
+    for (int b = 0; b < 4; ++b) dp[b] *= sc[b];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const V8 p8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);

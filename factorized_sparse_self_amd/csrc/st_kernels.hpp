@@ -95,7 +95,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;    // [B*H*T] workspace: rowsum(dout * out)
+  float* ndelta;   // [B*H*T] workspace: -rowsum(dout * out), the initial dP accumulator
   float* lse2;     // [B*H*T] workspace: lse * log2(e) (16-bit path; written by dq)
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
