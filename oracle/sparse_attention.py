@@ -217,16 +217,28 @@ def forward(q, k, v, pattern, l, c):
 # Backward (weights recomputed from q, k and lse)
 # --------------------------------------------------------------------------
 
-def backward(q, k, v, dO, pattern, l, c):
+def _given_or_forward(q, k, v, pattern, l, c, O, lse):
+    """The forward's output and lse as a backward receives them; exact when not given."""
+    if O is None or lse is None:
+        O2, lse2 = forward(q, k, v, pattern, l, c)
+        O = O2 if O is None else O
+        lse = lse2 if lse is None else lse
+    return O, lse
+
+
+def backward(q, k, v, dO, pattern, l, c, O=None, lse=None):
     """Gradients (dq, dk, dv) of L = <dO, O>, all float64 [B, H, T, D].
 
     For each query t with keys S(t): p_j = exp(s_j - lse_t) is recomputed,
     Delta_t = dO_t . O_t, dp_j = dO_t . v_j, ds_j = p_j (dp_j - Delta_t); then
     dv_j += p_j dO_t, dq_t = sum_j ds_j k_j / sqrt(D), dk_j += ds_j q_t / sqrt(D).
+    O [B, H, T, D] and lse [B, H, T] are the forward results the backward
+    receives (nlp-lineage, "The idea": the weights are rebuilt from the stored
+    row statistics); when not given they are computed exactly here.
     """
     B, H, T, D = q.shape
     scale = 1.0 / math.sqrt(D)
-    O, lse = forward(q, k, v, pattern, l, c)
+    O, lse = _given_or_forward(q, k, v, pattern, l, c, O, lse)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -248,8 +260,20 @@ def backward(q, k, v, dO, pattern, l, c):
     return dq, dk, dv
 
 
-def backward_dq_rows(q, k, v, dO, pattern, l, c, rows, heads=None):
-    """dq at the given query positions only: float64 [B, H, R, D]."""
+def _row_stats(q, k, v, b, h, t, S, scale, O, lse):
+    """(o_t, p over S) of query t: exact, or from the given forward results."""
+    if O is None or lse is None:
+        o, _, p = _attend_row(q[b, h, t], k[b, h, S], v[b, h, S], scale)
+    if O is not None:
+        o = np.asarray(O[b, h, t], dtype=np.float64)
+    if lse is not None:
+        p = np.exp((k[b, h, S] @ q[b, h, t]) * scale - float(lse[b, h, t]))
+    return o, p
+
+
+def backward_dq_rows(q, k, v, dO, pattern, l, c, rows, heads=None, O=None, lse=None):
+    """dq at the given query positions only: float64 [B, H, R, D].  O, lse: as in backward
+    (full [B, H, T, ...] arrays indexed by position), recomputed per row when not given."""
     B, H, T, D = q.shape
     scale = 1.0 / math.sqrt(D)
     rows = np.asarray(rows, dtype=np.int64)
@@ -261,7 +285,7 @@ def backward_dq_rows(q, k, v, dO, pattern, l, c, rows, heads=None):
             if S.size == 0:
                 continue
             for b in range(B):
-                o, lse_t, p = _attend_row(q[b, h, t], k[b, h, S], v[b, h, S], scale)
+                o, p = _row_stats(q, k, v, b, h, int(t), S, scale, O, lse)
                 delta = dO[b, h, t] @ o
                 dp = v[b, h, S] @ dO[b, h, t]
                 ds = p * (dp - delta)
@@ -269,11 +293,12 @@ def backward_dq_rows(q, k, v, dO, pattern, l, c, rows, heads=None):
     return dq
 
 
-def backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys, heads=None):
+def backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys, heads=None, O=None, lse=None):
     """dk, dv at the given key positions only: two float64 arrays [B, H, K, D].
 
     Every query that attends a sampled key is recomputed in full (its own key
     set, softmax and Delta), so the result equals the full backward at j.
+    O, lse: as in backward (used for those queries' Delta and weights when given).
     """
     B, H, T, D = q.shape
     scale = 1.0 / math.sqrt(D)
@@ -287,7 +312,7 @@ def backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys, heads=None):
                 S = key_set(pattern, kind, int(t), T, l, c)
                 pos = int(np.searchsorted(S, j))
                 for b in range(B):
-                    o, lse_t, p = _attend_row(q[b, h, t], k[b, h, S], v[b, h, S], scale)
+                    o, p = _row_stats(q, k, v, b, h, int(t), S, scale, O, lse)
                     delta = dO[b, h, t] @ o
                     dp_j = v[b, h, j] @ dO[b, h, t]
                     ds_j = p[pos] * (dp_j - delta)

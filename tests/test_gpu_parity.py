@@ -5,6 +5,10 @@ inputs and <= 1e-4 for fp32 inputs, on out, lse, dq, dk and dv (fp64 oracle).
 Rows with an empty key set must give out == 0 and lse == -inf exactly, single-
 key rows out == v exactly, and keys nobody attends dk == dv == 0 exactly.
 
+The backward is compared with the oracle's backward on the backward's own inputs:
+the forward's output O and lse as the kernel produced them (Delta = dO . O and the
+weights come from them), while the forward is compared with the exact oracle.
+
 Small cases run the whole oracle and span several 64-row blocks with ragged
 tails; the five workloads run at their full sizes in the launch configuration
 the benchmark times, and are compared on seeded samples of rows (out, lse, dq)
@@ -97,6 +101,9 @@ SMALL = [
     (inputs.FIXED, 1, 2, 250, 64, 64, 4),
     (inputs.FIXED, 1, 2, 260, 64, 5, 1),
     (inputs.FIXED_R1, 1, 2, 300, 64, 16, 3),
+    # l = 128: own-block heads take the local dq items (dq, dk, dv per pair)
+    (inputs.FIXED, 1, 2, 300, 64, 128, 8),
+    (inputs.FIXED_R1, 2, 2, 390, 32, 128, 4),
     (inputs.DENSE, 1, 2, 200, 64, 16, 0),
 ]
 
@@ -114,7 +121,7 @@ def test_small_forward_backward(case, dtype):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -151,7 +158,7 @@ def test_small_merged_heads(case, dtype):
     # position 0 attends only itself in both sets: out == v exactly
     assert torch.equal(out[:, :, 0].cpu(), v[:, :, 0])
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -182,7 +189,7 @@ def test_small_summary_sets(case, dtype):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, S)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, S)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, S, O=f64(out), lse=f64(lse))
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -231,7 +238,7 @@ def test_small_head_dim_128(case, dtype):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -256,7 +263,7 @@ def test_edge_shapes():
             assert_close(f64(out), O, dtype, "out")
             assert_close(f64(lse), L, "f32", "lse")
             dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-            rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+            rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
             assert_close(f64(dq), rq, dtype, "dq")
             assert_close(f64(dk), rk, dtype, "dk")
             assert_close(f64(dv), rv, dtype, "dv")
@@ -378,7 +385,10 @@ def test_workload_forward_backward_sampled(w):
     O, L = oracle.forward_rows(qn, kn, vn, w.pattern, w.l, w.c, rows)
     assert_close(f64(out[:1])[:, :, rows], O, w.dtype, "out")
     assert_close(f64(lse[:1])[:, :, rows], L, "f32", "lse")
-    rq = oracle.backward_dq_rows(qn, kn, vn, don, w.pattern, w.l, w.c, rows)
+    # the backward's own inputs: the forward's output and lse as the kernel gave them
+    # (float32 holds every 16-bit value exactly)
+    On, Ln = out[:1].float().cpu().numpy(), lse[:1].cpu().numpy()
+    rq = oracle.backward_dq_rows(qn, kn, vn, don, w.pattern, w.l, w.c, rows, O=On, lse=Ln)
     assert_close(f64(dq[:1])[:, :, rows], rq, w.dtype, "dq")
     # dense: every head has the same key sets and a key's queries are many, so two heads
     for h in range(2 if w.pattern == inputs.DENSE else w.H):
@@ -386,7 +396,8 @@ def test_workload_forward_backward_sampled(w):
         # long rows (l >= 1024): every attending query is recomputed, so fewer keys
         keys = _keys_for_head(w, kind, 8 if w.l >= 1024 else 24, w.seed + h)
         log(f"  oracle keys head {h}: {len(keys)}")
-        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, w.pattern, w.l, w.c, keys, heads=[h])
+        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, w.pattern, w.l, w.c, keys, heads=[h],
+                                             O=On, lse=Ln)
         assert_close(f64(dk[:1])[:, h, keys], rk[:, h], w.dtype, f"dk head {h}")
         assert_close(f64(dv[:1])[:, h, keys], rv[:, h], w.dtype, f"dv head {h}")
     if w.pattern in (inputs.FIXED, inputs.FIXED_R1):

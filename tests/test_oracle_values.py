@@ -215,3 +215,48 @@ def test_sampled_functions_equal_full_results(pattern, l, c):
     dks, dvs = oracle.backward_dkdv_keys(q, k, v, dO, pattern, l, c, keys)
     np.testing.assert_allclose(dks, dk[:, :, keys], atol=1e-13, rtol=0)
     np.testing.assert_allclose(dvs, dv[:, :, keys], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("pattern,T,l,c", [(STRIDED, 23, 4, 0), (FIXED, 24, 4, 2), (FIXED_R1, 21, 5, 2),
+                                           (FIXED_UNION, 20, 4, 2)])
+def test_backward_given_forward_results(pattern, T, l, c):
+    """The backward takes O and lse as its inputs.  Given the exact ones it is the default;
+    Delta = dO . O enters linearly, so a change E of O moves dq_t by
+    -(dO_t . E_t) sum_j p_tj k_j / sqrt(D), dk_j by -sum_t p_tj (dO_t . E_t) q_t / sqrt(D) and
+    leaves dv; a shift d of every lse scales every weight, hence dq, dk, dv, by exp(-d).
+    The row- and key-sampled variants agree with the full backward on the same inputs."""
+    B, H, D = 1, 2, 5
+    q, k, v, dO = (rand((B, H, T, D), s) for s in (30, 31, 32, 33))
+    O, L = oracle.forward(q, k, v, pattern, l, c)
+    ref = oracle.backward(q, k, v, dO, pattern, l, c)
+    for a, b in zip(ref, oracle.backward(q, k, v, dO, pattern, l, c, O=O, lse=L)):
+        np.testing.assert_array_equal(a, b)
+    E = 1e-3 * rand((B, H, T, D), 34)
+    dq2, dk2, dv2 = oracle.backward(q, k, v, dO, pattern, l, c, O=O + E, lse=L)
+    scale = 1.0 / np.sqrt(D)
+    want_dq = np.zeros_like(q)
+    want_dk = np.zeros_like(k)
+    for h in range(H):
+        kind = oracle.head_kind(h)
+        for t in range(T):
+            S = oracle.key_set(pattern, kind, t, T, l, c)
+            if S.size == 0:
+                continue
+            p = np.exp((k[0, h, S] @ q[0, h, t]) * scale - L[0, h, t])
+            g = float(dO[0, h, t] @ E[0, h, t])
+            want_dq[0, h, t] = -g * scale * (p @ k[0, h, S])
+            want_dk[0, h, S] += -g * scale * np.outer(p, q[0, h, t])
+    np.testing.assert_allclose(dq2 - ref[0], want_dq, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk2 - ref[1], want_dk, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv2, ref[2], rtol=0, atol=1e-14)
+    d = 0.3
+    for a, b in zip(ref, oracle.backward(q, k, v, dO, pattern, l, c, O=O, lse=L + d)):
+        np.testing.assert_allclose(b, np.exp(-d) * a, rtol=1e-12, atol=1e-14)
+    Og, Lg = O + E, L + 0.01 * rand((B, H, T), 35)
+    full = oracle.backward(q, k, v, dO, pattern, l, c, O=Og, lse=Lg)
+    rows = np.array([0, 3, T // 2, T - 1])
+    np.testing.assert_allclose(oracle.backward_dq_rows(q, k, v, dO, pattern, l, c, rows, O=Og, lse=Lg),
+                               full[0][:, :, rows], rtol=1e-12, atol=1e-13)
+    rk, rv = oracle.backward_dkdv_keys(q, k, v, dO, pattern, l, c, rows, O=Og, lse=Lg)
+    np.testing.assert_allclose(rk, full[1][:, :, rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(rv, full[2][:, :, rows], rtol=1e-12, atol=1e-13)
