@@ -173,7 +173,9 @@ void st_layout_free(st_layout* lay);
 
 /* ---------------------------------------------------------------------------
  * Attention.  Shapes: 1 <= B, 1 <= H, B*H <= 2^20, 1 <= T <= 2^24,
- * D in {32, 64, 128}; pattern, l and c as for st_layout_build.  Every pointer must
+ * D in {32, 64, 128}; pattern, l and c as for st_layout_build.  The bf16 and
+ * fp16 entry points also need T*D <= 2^30 (one head within 2^31 bytes; for
+ * D = 128, T <= 2^23), else ST_ERR_UNSUPPORTED.  Every pointer must
  * be non-null and 16-byte aligned, and the tensors must not overlap (except
  * that inputs may alias one another).
  * ------------------------------------------------------------------------- */

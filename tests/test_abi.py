@@ -69,6 +69,11 @@ def test_attention_argument_errors_without_gpu(name):
     assert _call_fwd(name, fake, D=256) == -2
     assert b"D must be 32, 64 or 128" in lib().st_last_error()
     assert _call_fwd(name, fake, pattern=5, c=0) == -1   # merged fixed heads need c too
+    # the 16-bit paths address a head with 32-bit offsets: T*D <= 2^30 (the fp32
+    # path has no such limit, so its call would pass the checks: not made here)
+    if not name.endswith("_f32"):
+        assert _call_fwd(name, fake, T=(1 << 23) + 1, D=128, l=1024) == -2
+        assert b"2^31 bytes" in lib().st_last_error()
 
 
 def test_merged_heads_have_no_fp32_path():
