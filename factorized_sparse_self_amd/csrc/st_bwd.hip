@@ -793,14 +793,25 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
   const int r = (u / CH) % kBlock, ch = u % CH;
   const int kp = block_position(kd.geo, true, item.kb, r);
   if (kp < 0) return;
+  // the item's partials, eight loads in flight at a time (a buffer over its
+  // slots: loads past the last slot return zeros, which add nothing), summed
+  // in slot order
+  constexpr int U = 8;
+  constexpr uint32_t kSlotBytes = 2u * kBlock * D * 4;
+  const Rsrc src = make_rsrc(a.partial + (size_t)item.slot0 * 2 * kBlock * D, (uint32_t)item.nsplit * kSlotBytes);
+  const uint32_t off = (uint32_t)((which * kBlock + r) * D + ch * 4) * 4;
   float4 s = {0.f, 0.f, 0.f, 0.f};
-  const float* src = a.partial + ((size_t)item.slot0 * 2 + which) * kBlock * D + r * D + ch * 4;
-  for (int j = 0; j < item.nsplit; ++j) {
-    const float4 x = *(const float4*)(src + (size_t)j * 2 * kBlock * D);
-    s.x += x.x;
-    s.y += x.y;
-    s.z += x.z;
-    s.w += x.w;
+  for (int j0 = 0; j0 < item.nsplit; j0 += U) {
+    uint4 x[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) x[i] = buf_load16(src, (uint32_t)(j0 + i) * kSlotBytes + off);
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      s.x += __uint_as_float(x[i].x);
+      s.y += __uint_as_float(x[i].y);
+      s.z += __uint_as_float(x[i].z);
+      s.w += __uint_as_float(x[i].w);
+    }
   }
   TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
   if constexpr (Is16<TE>::value) {
