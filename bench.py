@@ -14,7 +14,10 @@ Output: one JSON line.  ``value`` is useful TFLOP/s: 14*D*nnz FLOP per step
 dK) over the step time, nnz = sum over heads of |S(t)|; masked or skipped
 work is never counted (``executed_tflops`` counts every pair of the visited
 64x64 LUT blocks instead, and is labelled as such).  The step time is taken over ``--steps`` steps
-between two HIP events on the launch stream.  ``roofline`` describes the
+between two HIP events on the launch stream, after a warm-up of at least
+``--warmup`` steps and ``--warmup-seconds`` seconds.  ``ms_per_step_median``
+adds the median single-step time back to back (warm) and after a 512 MiB
+write that evicts the last-level cache (cold).  ``roofline`` describes the
 kernel with the largest time per step: its duration comes from HIP events
 that the library records around each kernel launch on the same stream, in a
 second timed pass of the same ``--steps`` steps (those events add a few
@@ -30,6 +33,7 @@ import json
 import math
 import multiprocessing as mp
 import os
+import statistics
 import sys
 import time
 
@@ -284,6 +288,8 @@ def main():
     ap.add_argument("--workload", default="fixed_T12288_bf16_fwdbwd")
     ap.add_argument("--cpu-units", type=int, default=8,
                     help="(batch, head-pair) slices the oracle baseline times, one process each")
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="keep warming up (untimed) until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
@@ -332,9 +338,18 @@ def main():
         if w.backward:
             st_sparse_attn_bwd(q, k, v, out, lse, do, w.pattern, w.l, w.c, dq=dq, dk=dk, dv=dv)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # Warm-up: at least W steps and at least --warmup-seconds of them, so that
+    # the GPU's clocks reach their steady state before the timed steps (after
+    # the ~2 ms of ten steps alone, a step measures about 10% slower than it
+    # does in a running loop).
+    t_warm = time.perf_counter()
+    warm_steps = 0
+    while warm_steps < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds:
+        for _ in range(10):
+            step()
+        warm_steps += 10
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_warm
 
     stream = torch.cuda.current_stream(dev)
 
@@ -354,11 +369,32 @@ def main():
         st_timing_enable(False)
         return start.elapsed_time(end) / args.steps
 
+    def per_step_median(flush):
+        """Median of `steps` single-step times (an event pair around each step).
+        With `flush`, a 512 MiB buffer is written before every step, outside
+        the events, so that no input is left in the 256 MB last-level cache
+        (cold); without it the steps run back to back (warm)."""
+        scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev) if flush else None
+        marks = []
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if flush:
+                scratch.fill_(float(i))
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record(stream)
+            step()
+            e_.record(stream)
+            marks.append((s_, e_))
+        torch.cuda.synchronize()
+        return statistics.median(s_.elapsed_time(e_) for s_, e_ in marks)
+
     # The step time comes from a pass without per-kernel events (each event
     # pair adds a few microseconds between kernels); the per-kernel durations
     # for the roofline come from an identical pass with them.
     ms_per_step = timed_steps(False)
     ms_per_step_instrumented = timed_steps(True)
+    median_warm = per_step_median(False)
+    median_cold = per_step_median(True)
     kernels = {}
     for name in KERNEL_NAMES:
         n, tot = st_timing_read(name)
@@ -397,8 +433,11 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_with_kernel_events": round(ms_per_step_instrumented, 4),
+        "ms_per_step_median": {"warm": round(median_warm, 4), "cold": round(median_cold, 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
