@@ -101,7 +101,7 @@ SMALL = [
     (inputs.FIXED, 1, 2, 250, 64, 64, 4),
     (inputs.FIXED, 1, 2, 260, 64, 5, 1),
     (inputs.FIXED_R1, 1, 2, 300, 64, 16, 3),
-    # l = 128: own-block heads take the local dq items (dq, dk, dv per pair)
+    # l = 128 (the benchmark's fixed configuration) at a size the oracle runs whole
     (inputs.FIXED, 1, 2, 300, 64, 128, 8),
     (inputs.FIXED_R1, 2, 2, 390, 32, 128, 4),
     (inputs.DENSE, 1, 2, 200, 64, 16, 0),
@@ -291,6 +291,36 @@ def test_exact_special_rows():
     os_ = out_s.cpu()
     assert torch.equal(os_[0, 1, :l], v[0, 1, :l])
     assert torch.equal(os_[0, 0, 0], v[0, 0, 0])
+
+
+@pytest.mark.parametrize("pattern", [inputs.FIXED, inputs.FIXED_UNION, inputs.DENSE],
+                         ids=lambda p: inputs.PATTERN_NAMES[p])
+def test_results_repeat_bit_for_bit(pattern):
+    """The same inputs give the same bits on every call, also from another stream: the
+    split key blocks (T = 4096 gives key columns of up to 64 row blocks, split at 32)
+    are summed in slot order, and nothing depends on the order workgroups finish."""
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, T, D, l, c = 1, 4, 4096, 64, 128, 8
+    log(f"repeat: pattern {inputs.PATTERN_NAMES[pattern]} B{B} H{H} T{T} D{D} l{l} c{c}")
+    g = torch.Generator().manual_seed(4242)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g).to(torch.bfloat16).cuda() for _ in range(4))
+
+    def run():
+        out, lse = st_sparse_attn_fwd(q, k, v, pattern, l, c)
+        dq, dk, dv = st_sparse_attn_bwd(q, k, v, out, lse, do, pattern, l, c)
+        return [t.clone() for t in (out, lse, dq, dk, dv)]
+
+    first = run()
+    again = run()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        other = run()
+    torch.cuda.synchronize()
+    for name, a, b, o in zip(("out", "lse", "dq", "dk", "dv"), first, again, other):
+        bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+        assert torch.equal(a.view(bits), b.view(bits)), f"{name}: second call differs"
+        assert torch.equal(a.view(bits), o.view(bits)), f"{name}: call on another stream differs"
 
 
 def test_autograd_wrapper_matches_entry_points():
