@@ -378,13 +378,9 @@ int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, 
   return ST_OK;
 }
 
-// Merged heads run on the 16-bit paths only, and the 16-bit kernels address
-// one head of a tensor through 32-bit buffer offsets: T*D*2 <= 2^31.
-int check_union_dtype(const char* fn, int pattern, bool path16, int T, int D) {
-  if (is_union(pattern) && !path16) {
-    set_error(std::string(fn) + ": merged-head patterns have no fp32 path");
-    return ST_ERR_UNSUPPORTED;
-  }
+// The 16-bit kernels address one head of a tensor through 32-bit buffer
+// offsets: T*D*2 <= 2^31.
+int check_head_size(const char* fn, bool path16, int T, int D) {
   if (path16 && (int64_t)T * D * 2 > ((int64_t)1 << 31)) {
     set_error(std::string(fn) + ": one head of a 16-bit tensor must fit in 2^31 bytes (T*D <= 2^30), got T=" +
               std::to_string(T) + ", D=" + std::to_string(D));
@@ -400,7 +396,7 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   int rc = check_attn_args(fn, ptrs, 5, B, H, T, D, pattern, l, c, summary);
   if (rc != ST_OK) return rc;
   constexpr bool k16 = Is16<TE>::value;
-  rc = check_union_dtype(fn, pattern, k16, T, D);
+  rc = check_head_size(fn, k16, T, D);
   if (rc != ST_OK) return rc;
   if (!uses_summary(pattern)) c = 0;
   int device = 0;
@@ -457,7 +453,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
   int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c, summary);
   if (rc != ST_OK) return rc;
-  rc = check_union_dtype(fn, pattern, Is16<TE>::value, T, D);
+  rc = check_head_size(fn, Is16<TE>::value, T, D);
   if (rc != ST_OK) return rc;
   if (!uses_summary(pattern)) c = 0;
   int device = 0;

@@ -80,6 +80,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_f32_kernel(BwdArgs a) {
   for (int m = TPR / 2; m >= 1; m >>= 1) part += xor_shfl(part, m);
   if (!valid) return;
   if (ch == 0) a.ndelta[row] = -part;
+  // (a merged head's own-window or own-block kind attends every key)
+  if (a.out_mode != OUT_FINAL) return;
   const int bh = (int)(row / a.T), t = (int)(row - (int64_t)bh * a.T);
   const Geometry& g = a.kinds[(bh % a.H) & 1].geo;
   if (!position_is_key(g, t)) {
@@ -87,6 +89,45 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_f32_kernel(BwdArgs a) {
     *(uint4*)((TE*)a.dk + row * D + ch * VEC) = z;
     *(uint4*)((TE*)a.dv + row * D + ch * VEC) = z;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Stores of one gradient row (dq of a query, dk or dv of a key): ND runs of 4
+// floats at element offsets 16 d (the lane's quarter of the row; `dst` and
+// `carry` point at its first element), scaled by `scale`, written as the
+// launch's OutMode says.
+// ---------------------------------------------------------------------------
+template <int ND, typename E>
+__device__ __forceinline__ void store_grad_row(int mode, float* carry, E* dst, const f32x4* x, float scale) {
+  if (mode == OUT_CARRY) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 y = x[d] * scale;
+      *(float4*)(carry + 16 * d) = make_float4(y[0], y[1], y[2], y[3]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    f32x4 y = x[d] * scale;
+    if (mode == OUT_MERGE) {
+      const float4 c = *(const float4*)(carry + 16 * d);
+      y += (f32x4){c.x, c.y, c.z, c.w};
+    }
+    if constexpr (std::is_same<E, float>::value)
+      *(float4*)(dst + 16 * d) = make_float4(y[0], y[1], y[2], y[3]);
+    else
+      *(typename Vec<E>::x4*)(dst + 16 * d) = to_x4<E>(y);
+  }
+}
+
+// Store mode of the dk / dv row of key position p: in the first pass of a
+// merged head, only keys that the second pass holds are carried; the others
+// are final.
+__device__ __forceinline__ int key_out_mode(const BwdArgs& a, int p) {
+  if (a.out_mode != OUT_CARRY) return a.out_mode;
+  const Geometry g1 = load_uniform(&a.kinds[1].geo);
+  return position_is_key(g1, p) ? OUT_CARRY : OUT_FINAL;
 }
 
 // ---------------------------------------------------------------------------
@@ -193,12 +234,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a) {
     }
   }
   if (t < 0) return;
-  TE* dq = (TE*)a.dq + base + (size_t)t * D;
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const f32x4 o = acc[d] * a.scale;
-    *(float4*)(dq + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-  }
+  store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
+                     (TE*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,14 +373,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
 
   if (item.slot < 0) {
     if (kp < 0) return;
-    TE* dkp = (TE*)a.dk + base + (size_t)kp * D;
-    TE* dvp = (TE*)a.dv + base + (size_t)kp * D;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      const f32x4 x = dk[d] * a.scale;
-      *(float4*)(dkp + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
-      *(float4*)(dvp + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
-    }
+    const int mode = key_out_mode(a, kp);
+    const size_t off = ((size_t)bh * a.T + kp) * D + 4 * lg;
+    store_grad_row<ND>(mode, a.carry_dk + off, (TE*)a.dk + off, dk, a.scale);
+    store_grad_row<ND>(mode, a.carry_dv + off, (TE*)a.dv + off, dv, 1.f);
   } else {
     float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
     float* pv = pk + kBlock * D;
@@ -356,41 +389,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Stores of one gradient row (dq of a query, dk or dv of a key): ND runs of 4
-// floats at element offsets 16 d (the lane's quarter of the row; `dst` and
-// `carry` point at its first element), scaled by `scale`, written as the
-// launch's OutMode says.
-// ---------------------------------------------------------------------------
-template <int ND, typename E>
-__device__ __forceinline__ void store_grad_row(int mode, float* carry, E* dst, const f32x4* x, float scale) {
-  if (mode == OUT_CARRY) {
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      const f32x4 y = x[d] * scale;
-      *(float4*)(carry + 16 * d) = make_float4(y[0], y[1], y[2], y[3]);
-    }
-    return;
-  }
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    f32x4 y = x[d] * scale;
-    if (mode == OUT_MERGE) {
-      const float4 c = *(const float4*)(carry + 16 * d);
-      y += (f32x4){c.x, c.y, c.z, c.w};
-    }
-    *(typename Vec<E>::x4*)(dst + 16 * d) = to_x4<E>(y);
-  }
-}
-
-// Store mode of the dk / dv row of key position p: in the first pass of a
-// merged head, only keys that the second pass holds are carried; the others
-// are final.
-__device__ __forceinline__ int key_out_mode(const BwdArgs& a, int p) {
-  if (a.out_mode != OUT_CARRY) return a.out_mode;
-  const Geometry g1 = load_uniform(&a.kinds[1].geo);
-  return position_is_key(g1, p) ? OUT_CARRY : OUT_FINAL;
-}
 
 // ---------------------------------------------------------------------------
 // 16-bit dq and dk/dv.  As in the forward: the streamed blocks (K and V for dq;
@@ -814,14 +812,9 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
     }
   }
   TE* dst = (TE*)(which ? a.dv : a.dk) + base + (size_t)kp * D + ch * 4;
-  if constexpr (Is16<TE>::value) {
-    const int mode = key_out_mode(a, kp);
-    f32x4 x[1] = {(f32x4){s.x, s.y, s.z, s.w}};
-    store_grad_row<1>(mode, (which ? a.carry_dv : a.carry_dk) + base + (size_t)kp * D + ch * 4, dst, x,
-                      1.f);
-  } else {
-    *(float4*)dst = s;
-  }
+  const f32x4 x[1] = {(f32x4){s.x, s.y, s.z, s.w}};
+  store_grad_row<1>(key_out_mode(a, kp), (which ? a.carry_dv : a.carry_dk) + base + (size_t)kp * D + ch * 4, dst,
+                    x, 1.f);
 }
 
 }  // namespace
@@ -834,7 +827,8 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   hipError_t err = hipSuccess;
   // 16-bit: the dq kernel computes Delta and the zero fill itself; it runs
   // before dk/dv, which reads Delta
-  if constexpr (!Is16<TE>::value) {
+  // (a merged head's second pass keeps the first pass's Delta)
+  if (!Is16<TE>::value && a.out_mode != OUT_MERGE) {
     timing_begin(KID_PRE, stream);
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)pre_blocks), dim3(kThreads), 0, stream, a);
     err = hipGetLastError();

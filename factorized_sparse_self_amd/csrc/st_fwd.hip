@@ -59,6 +59,12 @@ __device__ __forceinline__ void stage_kv_f32(const float* __restrict__ K, const 
   }
 }
 
+// a*b - c with the product rounded before the subtraction (never fused)
+__device__ __forceinline__ float mul_unfused(float a, float b, float c) {
+#pragma clang fp contract(off)
+  return a * b - c;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   using L = FwdLdsF32<D>;
@@ -139,14 +145,16 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
       for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[b][i]);
     mt = group4_max(mt);
     const float m_new = fmaxf(m_run, mt);
-    const float mb = (m_new == -INFINITY) ? 0.f : m_new * sl2;
-    const float alpha = fast_exp2(m_run * sl2 - mb);
+    // exponents as rounded products (never fused), so that the row's maximum
+    // logit gets exp2(0) = 1 exactly: a row with one key returns v bit for bit
+    const float mb = (m_new == -INFINITY) ? 0.f : mul_unfused(m_new, sl2, 0.f);
+    const float alpha = fast_exp2(mul_unfused(m_run, sl2, mb));
     float psum = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(fmaf(s[b][i], sl2, -mb));
+        const float p = fast_exp2(mul_unfused(s[b][i], sl2, mb));
         s[b][i] = p;
         psum += p;
       }
@@ -170,14 +178,45 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   const float lsum = group4_sum(l_run);
   if (t < 0) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  float* O = (float*)a.o + base + (size_t)t * D;
+  const float lse2 = lsum > 0.f ? m_run * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
+  const size_t row = (size_t)bh * a.T + t;
+  float* O = (float*)a.o + row * D;
+  if (a.out_mode == OUT_CARRY) {
+    // first pass of a merged head: keep the normalised output and lse
+    float* C = a.carry_o + row * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 o = acc[d] * inv;
+      *(float4*)(C + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (lg == 0) a.carry_lse[row] = lse2;
+    return;
+  }
+  if (a.out_mode == OUT_MERGE) {
+    // softmax over both key sets: the two passes' outputs weighted by
+    // 2^(L_p - L), L = log2(2^L0 + 2^L1) (a pass with no keys has L_p = -inf)
+    const float lse0 = a.carry_lse[row];
+    const float mx = fmaxf(lse0, lse2);
+    const float w0 = mx == -INFINITY ? 0.f : fast_exp2(lse0 - mx);
+    const float w1 = mx == -INFINITY ? 0.f : fast_exp2(lse2 - mx);
+    const float sw = w0 + w1;
+    const float s0 = sw > 0.f ? w0 / sw : 0.f, s1 = sw > 0.f ? w1 * inv / sw : 0.f;
+    const float* C = a.carry_o + row * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const float4 c = *(const float4*)(C + 16 * d + 4 * lg);
+      const f32x4 o = (f32x4){c.x, c.y, c.z, c.w} * s0 + acc[d] * s1;
+      *(float4*)(O + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
+    return;
+  }
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
     const f32x4 o = acc[d] * inv;
     *(float4*)(O + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
   }
-  if (lg == 0)
-    a.lse[(size_t)bh * a.T + t] = lsum > 0.f ? (m_run * sl2 + fast_log2(lsum)) * kLn2 : -INFINITY;
+  if (lg == 0) a.lse[row] = lse2 * kLn2;
 }
 
 // ---------------------------------------------------------------------------

@@ -29,9 +29,8 @@
  *     first keeps fp32 partial results in the workspace, the second merges
  *     its own into them (the two softmaxes by their log-sum-exps, gradients
  *     by addition).  For that split the strided pass leaves out t itself
- *     (already in the window); the fixed sets are disjoint.  16-bit inputs
- *     only: the _f32 attention entry points return ST_ERR_UNSUPPORTED for
- *     them.
+ *     (already in the window); the fixed sets are disjoint.  Every entry
+ *     point (bf16, fp16, fp32) takes them.
  *
  * Conventions (readings where the pages are silent):
  *   - positions are 0-based; T need not be a multiple of l;

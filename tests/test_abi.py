@@ -76,16 +76,6 @@ def test_attention_argument_errors_without_gpu(name):
         assert b"2^31 bytes" in lib().st_last_error()
 
 
-def test_merged_heads_have_no_fp32_path():
-    from factorized_sparse_self_amd import ST_FIXED_UNION, ST_STRIDED_UNION, lib
-    L = lib()
-    fake = 1 << 20
-    for pattern, c in ((ST_STRIDED_UNION, 0), (ST_FIXED_UNION, 2)):
-        assert _call_fwd("st_sparse_attn_fwd_f32", fake, pattern=pattern, c=c) == -2
-        assert b"no fp32 path" in L.st_last_error()
-        assert L.st_sparse_attn_bwd_f32(*([fake] * 9), 1, 2, 64, 64, pattern, 8, c, None) == -2
-
-
 def test_backward_argument_errors_without_gpu():
     from factorized_sparse_self_amd import lib
     L = lib()

@@ -127,7 +127,7 @@ def test_small_forward_backward(case, dtype):
     assert_close(f64(dv), rv, dtype, "dv")
 
 
-# Merged heads (every head attends both sets): 16-bit inputs only
+# Merged heads (every head attends both sets)
 SMALL_UNION = [
     (inputs.STRIDED_UNION, 2, 3, 300, 64, 16, 0),
     (inputs.STRIDED_UNION, 1, 2, 333, 32, 20, 0),
@@ -144,7 +144,7 @@ SMALL_UNION = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("case", SMALL_UNION, ids=lambda c: f"p{c[0]}_B{c[1]}H{c[2]}T{c[3]}D{c[4]}l{c[5]}c{c[6]}")
 def test_small_merged_heads(case, dtype):
     pattern, B, H, T, D, l, c = case
@@ -179,8 +179,6 @@ SMALL_SIGMA = [
 @pytest.mark.parametrize("case", SMALL_SIGMA, ids=lambda c: f"p{c[0]}_H{c[2]}T{c[3]}D{c[4]}l{c[5]}S{'-'.join(map(str, c[6]))}")
 def test_small_summary_sets(case, dtype):
     pattern, B, H, T, D, l, S = case
-    if dtype == "f32" and pattern == inputs.FIXED_UNION:
-        pytest.skip("merged heads run on 16-bit inputs only")
     log(f"small summary set fwd+bwd {case} {dtype}")
     q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=23 + T + l, n=4)
     out, lse = run_fwd(q, k, v, pattern, l, S)
@@ -228,8 +226,6 @@ SMALL_D128 = [
 @pytest.mark.parametrize("case", SMALL_D128, ids=lambda c: f"p{c[0]}_H{c[2]}T{c[3]}l{c[5]}")
 def test_small_head_dim_128(case, dtype):
     pattern, B, H, T, D, l, c = case
-    if dtype == "f32" and pattern in (inputs.STRIDED_UNION, inputs.FIXED_UNION):
-        pytest.skip("merged heads run on 16-bit inputs only")
     log(f"small D=128 fwd+bwd {case} {dtype}")
     q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=41 + T + l, n=4)
     out, lse = run_fwd(q, k, v, pattern, l, c)
@@ -269,11 +265,12 @@ def test_edge_shapes():
             assert_close(f64(dv), rv, dtype, "dv")
 
 
-def test_exact_special_rows():
-    """Empty rows: out == 0, lse == -inf, dq == 0.  Single-key rows: out == v.
-    Keys nobody attends: dk == dv == 0."""
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_special_rows(dtype):
+    """Empty rows: out == 0, lse == -inf, dq == 0.  Single-key rows: out == v (the
+    one weight is exactly 1).  Keys nobody attends: dk == dv == 0."""
     B, H, T, D, l, c = 1, 2, 256, 64, 32, 4
-    q, k, v, do = inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=5, n=4)
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=5, n=4)
     out, lse = run_fwd(q, k, v, inputs.FIXED, l, c)
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, inputs.FIXED, l, c)
     o, L, dq_, dk_, dv_ = (x.cpu() for x in (out, lse, dq, dk, dv))
