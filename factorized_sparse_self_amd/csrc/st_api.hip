@@ -23,9 +23,15 @@ namespace st {
 
 namespace {
 
-// A key block of the dK/dV pass is split so that no work item walks more than
-// this many row blocks (fp32 partials are then summed by the reduce kernel).
+// A key block of the dK/dV pass is split (fp32 partials, summed by the reduce
+// kernel) only where its row-block list would outlast the launch: lists longer
+// than half the average load of kDkdvSlots resident workgroups, and never into
+// pieces shorter than kDkdvSplit row blocks.  Short launches with long columns
+// (summary heads) split at kDkdvSplit; launches with many more items than the
+// GPU holds (full attention, long sequences) are balanced by the schedule alone
+// and split nothing, which spares the partials' workspace and traffic.
 constexpr int kDkdvSplit = 32;
+constexpr int64_t kDkdvSlots = 2048;
 
 struct PlanKey {
   int device, pattern, T, l, c, B, H;
@@ -204,9 +210,17 @@ int build_plan(const PlanKey& key, Plan* plan) {
       hp[p].pairs.push_back(i < 0 ? PairItem{-1, -1, 0, 0, 0, 0u, 0, 0} : pairs[i]);
 
     // dK/dV items: every key block of every head.  A key block whose row-block
-    // list is longer than kDkdvSplit is split at row-block multiples of
-    // kDkdvSplit, so that the splits of different key blocks read the same row
-    // blocks; grouped by (head, first row block read).
+    // list is longer than `split` is split at row-block multiples of `split`,
+    // so that the splits of different key blocks read the same row blocks;
+    // grouped by (head, first row block read).
+    int64_t dwork = 0;
+    for (int bh = 0; bh < BH; ++bh) {
+      const KindLayout& L = lay.kind[kind_of(p, bh)];
+      dwork += L.col_ptr[L.n_kb] + L.n_kb;
+    }
+    const int64_t avg = (dwork + kDkdvSlots - 1) / kDkdvSlots;
+    const int split = (int)std::min<int64_t>(std::max<int64_t>(kDkdvSplit, (avg + kDkdvSplit - 1) / kDkdvSplit * kDkdvSplit),
+                                             1 << 30);
     std::vector<DkdvItem> dkdv;
     std::vector<int64_t> dcost, dgroup;
     int slots = 0;
@@ -216,7 +230,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
       for (int kb = 0; kb < L.n_kb; ++kb) {
         const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
         const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
-        if (e1 - e0 <= kDkdvSplit) {
+        if (e1 - e0 <= split) {
           dkdv.push_back({kb, bh, e0, e1, -1, kind, 0, 0});
           dcost.push_back(e1 - e0 + 1);
           dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
@@ -224,9 +238,9 @@ int build_plan(const PlanKey& key, Plan* plan) {
         }
         const int slot0 = slots;
         for (int a = e0; a < e1;) {
-          const int range = L.row_idx[a] / kDkdvSplit;
+          const int range = L.row_idx[a] / split;
           int b = a;
-          while (b < e1 && L.row_idx[b] / kDkdvSplit == range) ++b;
+          while (b < e1 && L.row_idx[b] / split == range) ++b;
           dkdv.push_back({kb, bh, a, b, slots++, kind, 0, 0});
           dcost.push_back(b - a + 1);
           dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);

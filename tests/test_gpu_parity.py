@@ -320,6 +320,78 @@ def test_results_repeat_bit_for_bit(pattern):
         assert torch.equal(a.view(bits), o.view(bits)), f"{name}: call on another stream differs"
 
 
+class DeviceRows:
+    """A GPU tensor [B, H, T, ...] seen by the oracle as an array: indexing [b, h, t] or
+    [b, h, positions] copies only those rows to the host, as float64.  Lets the oracle
+    sample outputs of tensors too large to copy whole."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, idx):
+        b, h, r = idx
+        if isinstance(r, (int, np.integer)):
+            x = self.t[int(b), int(h), int(r)]
+        else:
+            x = self.t[int(b), int(h)].index_select(0, torch.as_tensor(np.asarray(r), device=self.t.device))
+        return x.double().cpu().numpy()
+
+
+def test_maximum_length():
+    """T = 2^24 at D = 64, the largest head the 16-bit kernels address (T*D*2 = 2^31
+    bytes): sampled rows and keys at both ends of the sequence against the oracle."""
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, T, D, l, c = 1, 2, 1 << 24, 64, 4096, 0
+    pattern = inputs.STRIDED
+    log(f"maximum length: strided B{B} H{H} T{T} D{D} l{l}")
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    out, lse = st_sparse_attn_fwd(q, k, v, pattern, l, c)
+    dq, dk, dv = st_sparse_attn_bwd(q, k, v, out, lse, do, pattern, l, c)
+    torch.cuda.synchronize()
+    for name, x in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(x).all(), name
+    Q, K, V, G, On, Ln = (DeviceRows(x) for x in (q, k, v, do, out, lse))
+    rows = [0, 1, l - 1, l, T // 2 + 3, T - l - 1, T - 2, T - 1]
+    O, L = oracle.forward_rows(Q, K, V, pattern, l, c, rows)
+    assert_close(f64(out[:, :, rows]), O, "bf16", "out")
+    assert_close(f64(lse[:, :, rows]), L, "f32", "lse")
+    rq = oracle.backward_dq_rows(Q, K, V, G, pattern, l, c, rows, O=On, lse=Ln)
+    assert_close(f64(dq[:, :, rows]), rq, "bf16", "dq")
+    keys = [5, T - 100, T - 1]
+    for h in range(H):
+        log(f"  oracle keys head {h}: {keys}")
+        rk, rv = oracle.backward_dkdv_keys(Q, K, V, G, pattern, l, c, keys, heads=[h], O=On, lse=Ln)
+        assert_close(f64(dk[:, h, keys]), rk[:, h], "bf16", f"dk head {h}")
+        assert_close(f64(dv[:, h, keys]), rv[:, h], "bf16", f"dv head {h}")
+
+
+def test_maximum_heads():
+    """B*H = 2^20 (the largest head count): the first and last heads of each kind against
+    the oracle, whole."""
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, T, D, l, c = 1, 1 << 20, 100, 32, 16, 4
+    pattern = inputs.FIXED
+    log(f"maximum heads: fixed B{B} H{H} T{T} D{D} l{l} c{c}")
+    g = torch.Generator(device="cuda").manual_seed(2025)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    out, lse = st_sparse_attn_fwd(q, k, v, pattern, l, c)
+    dq, dk, dv = st_sparse_attn_bwd(q, k, v, out, lse, do, pattern, l, c)
+    torch.cuda.synchronize()
+    # heads 0, 1, H-2, H-1 keep their kinds (h mod 2) as heads 0..3 of a 4-head problem
+    heads = torch.tensor([0, 1, H - 2, H - 1], device="cuda")
+    pick = lambda x: x.index_select(1, heads)
+    qn, kn, vn, don = (f64(pick(x)) for x in (q, k, v, do))
+    O, L = oracle.forward(qn, kn, vn, pattern, l, c)
+    assert_close(f64(pick(out)), O, "bf16", "out")
+    assert_close(f64(pick(lse)), L, "f32", "lse")
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(pick(out)), lse=f64(pick(lse)))
+    assert_close(f64(pick(dq)), rq, "bf16", "dq")
+    assert_close(f64(pick(dk)), rk, "bf16", "dk")
+    assert_close(f64(pick(dv)), rv, "bf16", "dv")
+
+
 def test_autograd_wrapper_matches_entry_points():
     from factorized_sparse_self_amd import sparse_attention
     B, H, T, D, l, c = 1, 2, 200, 64, 16, 3
