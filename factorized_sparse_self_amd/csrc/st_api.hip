@@ -219,8 +219,8 @@ int build_plan(const PlanKey& key, Plan* plan) {
       dwork += L.col_ptr[L.n_kb] + L.n_kb;
     }
     const int64_t avg = (dwork + kDkdvSlots - 1) / kDkdvSlots;
-    const int split = (int)std::min<int64_t>(std::max<int64_t>(kDkdvSplit, (avg + kDkdvSplit - 1) / kDkdvSplit * kDkdvSplit),
-                                             1 << 30);
+    const int64_t avg_up = (avg + kDkdvSplit - 1) / kDkdvSplit * kDkdvSplit;  // a multiple of kDkdvSplit
+    const int split = (int)std::min<int64_t>(std::max<int64_t>(kDkdvSplit, avg_up), 1 << 30);
     std::vector<DkdvItem> dkdv;
     std::vector<int64_t> dcost, dgroup;
     int slots = 0;
