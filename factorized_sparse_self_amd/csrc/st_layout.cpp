@@ -235,7 +235,7 @@ int st_layout_pairs(const st_layout* lay, int kind, int64_t* pairs) {
 
 int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, int32_t* key_pos) {
   const KindLayout* L = kind_of(lay, kind, "st_layout_maps");
-  if (!L || !row_pos || !key_pos) {
+  if (!L || (!row_pos && L->geo.n_rows > 0) || (!key_pos && L->geo.n_keys > 0)) {
     if (L) set_error("st_layout_maps: null output buffer");
     return ST_ERR_INVALID;
   }

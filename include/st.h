@@ -157,14 +157,17 @@ int st_layout_dims(const st_layout* lay, int kind, int32_t* dims);
 /* Total attended (query, key) pairs of one head of this kind, sum_t |S(t)|. */
 int st_layout_pairs(const st_layout* lay, int kind, int64_t* pairs);
 
-/* Copy the coordinate maps: row_pos[ROWS], key_pos[KEYS] (caller buffers). */
+/* Copy the coordinate maps: row_pos[ROWS], key_pos[KEYS] (caller buffers;
+ * either may be NULL when its count is 0, as for the CSR and CSC below). */
 int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, int32_t* key_pos);
 
-/* Copy the CSR: row_ptr[QBLOCKS+1], col_idx[NNZ], flags[NNZ] (caller buffers). */
+/* Copy the CSR: row_ptr[QBLOCKS+1], col_idx[NNZ], flags[NNZ] (caller buffers;
+ * col_idx and flags may be NULL when NNZ is 0). */
 int st_layout_csr(const st_layout* lay, int kind, int32_t* row_ptr, int32_t* col_idx,
                   uint8_t* flags);
 
-/* Copy the CSC: col_ptr[KBLOCKS+1], row_idx[NNZ], flags[NNZ] (caller buffers). */
+/* Copy the CSC: col_ptr[KBLOCKS+1], row_idx[NNZ], flags[NNZ] (caller buffers;
+ * row_idx and flags may be NULL when NNZ is 0). */
 int st_layout_csc(const st_layout* lay, int kind, int32_t* col_ptr, int32_t* row_idx,
                   uint8_t* flags);
 
