@@ -392,6 +392,44 @@ def test_maximum_heads():
     assert_close(f64(pick(dv)), rv, "bf16", "dv")
 
 
+def test_split_columns_of_a_longer_launch():
+    """Fixed pattern, T = 12288, l = 128, with 80 heads: the launch is long enough that
+    the summary heads' key columns (up to 190 row blocks) are split at 64 row blocks
+    rather than 32.  Sampled rows and keys of the first and last heads of each kind
+    against the oracle; the keys cover split and unsplit columns."""
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, T, D, l, c = 1, 80, 12288, 64, 128, 8
+    pattern = inputs.FIXED
+    log(f"split columns: fixed B{B} H{H} T{T} D{D} l{l} c{c}")
+    g = torch.Generator(device="cuda").manual_seed(2026)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    out, lse = st_sparse_attn_fwd(q, k, v, pattern, l, c)
+    dq, dk, dv = st_sparse_attn_bwd(q, k, v, out, lse, do, pattern, l, c)
+    torch.cuda.synchronize()
+    # heads 0, 1, H-2, H-1 keep their kinds (h mod 2) as heads 0..3 of a 4-head problem
+    heads = torch.tensor([0, 1, H - 2, H - 1], device="cuda")
+    pick = lambda x: x.index_select(1, heads)
+    qn, kn, vn, don = (f64(pick(x)) for x in (q, k, v, do))
+    On, Ln = pick(out).float().cpu().numpy(), pick(lse).cpu().numpy()
+    rows = sample_rows(T, l, 64, 7)
+    O, L = oracle.forward_rows(qn, kn, vn, pattern, l, c, rows)
+    assert_close(f64(pick(out))[:, :, rows], O, "bf16", "out")
+    assert_close(f64(pick(lse))[:, :, rows], L, "f32", "lse")
+    rq = oracle.backward_dq_rows(qn, kn, vn, don, pattern, l, c, rows, O=On, lse=Ln)
+    assert_close(f64(pick(dq))[:, :, rows], rq, "bf16", "dq")
+    S = inputs.summary_offsets(l, c)
+    nb = T // l
+    # summary keys: block 0 (a column of 190 row blocks, three splits), the middle,
+    # and block nb - 3 (a column of 4 row blocks, one piece); own-block keys
+    keys = {1: [S[0], (nb // 2) * l + S[3], (nb - 3) * l + S[-1]], 0: [0, 127, T // 2 + 5, T - 1]}
+    for h in range(4):
+        log(f"  oracle keys head {h}")
+        kk = keys[h % 2]
+        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, pattern, l, c, kk, heads=[h], O=On, lse=Ln)
+        assert_close(f64(pick(dk))[:, h, kk], rk[:, h], "bf16", f"dk head {h}")
+        assert_close(f64(pick(dv))[:, h, kk], rv[:, h], "bf16", f"dv head {h}")
+
+
 def test_autograd_wrapper_matches_entry_points():
     from factorized_sparse_self_amd import sparse_attention
     B, H, T, D, l, c = 1, 2, 200, 64, 16, 3
