@@ -265,6 +265,48 @@ def test_edge_shapes():
             assert_close(f64(dv), rv, dtype, "dv")
 
 
+def _random_cases(n, seed):
+    """n seeded random small problems: pattern, B, H, T, D, l, summary (a count or a set), dtype."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        pattern = int(rng.integers(0, 6))
+        dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
+        D = [32, 64, 128][int(rng.integers(0, 3))]
+        T = int(rng.integers(1, 420))
+        l = int(rng.integers(1, 150))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        c = 0
+        if pattern in (inputs.FIXED, inputs.FIXED_R1, inputs.FIXED_UNION):
+            if rng.random() < 0.5:
+                c = int(rng.integers(1, l + 1))
+            else:
+                k = int(rng.integers(1, l + 1))
+                c = tuple(int(x) for x in sorted(rng.choice(l, size=k, replace=False)))
+        cases.append((pattern, B, H, T, D, l, c, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(100, 31337),
+                         ids=lambda c: f"p{c[0]}_B{c[1]}H{c[2]}T{c[3]}D{c[4]}l{c[5]}_{c[7]}")
+def test_random_shapes(case):
+    """Seeded random patterns, dtypes, head dims, lengths, strides and summary sets (counts
+    or explicit offsets), each against the whole oracle."""
+    pattern, B, H, T, D, l, c, dtype = case
+    log(f"random shape {case}")
+    q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=T * 131 + l, n=4)
+    out, lse = run_fwd(q, k, v, pattern, l, c)
+    qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
+    O, L = oracle.forward(qn, kn, vn, pattern, l, c)
+    assert_close(f64(out), O, dtype, "out")
+    assert_close(f64(lse), L, "f32", "lse")
+    dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
+    assert_close(f64(dq), rq, dtype, "dq")
+    assert_close(f64(dk), rk, dtype, "dk")
+    assert_close(f64(dv), rv, dtype, "dv")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_exact_special_rows(dtype):
     """Empty rows: out == 0, lse == -inf, dq == 0.  Single-key rows: out == v (the
