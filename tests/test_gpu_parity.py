@@ -10,9 +10,11 @@ the forward's output O and lse as the kernel produced them (Delta = dO . O and t
 weights come from them), while the forward is compared with the exact oracle.
 
 Small cases run the whole oracle and span several 64-row blocks with ragged
-tails; the five workloads run at their full sizes in the launch configuration
-the benchmark times, and are compared on seeded samples of rows (out, lse, dq)
-and keys (dk, dv) that the oracle computes one by one.
+tails, hand-picked and seeded-random (pattern, dtype, D, T, l, summary set; a
+second random set is long enough for split key columns); the workloads run at
+their full sizes in the launch configuration the benchmark times, and are
+compared on seeded samples of rows (out, lse, dq) and keys (dk, dv) that the
+oracle computes one by one, as are the largest T and B*H the library accepts.
 """
 import math
 import sys
@@ -287,11 +289,37 @@ def _random_cases(n, seed):
     return cases
 
 
+def _random_long_cases(n, seed):
+    """n seeded random problems long enough (T > 2048) that key columns of more than 32
+    row blocks exist, so that dk/dv runs its split partials and reduction."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        pattern = [inputs.FIXED, inputs.FIXED_R1, inputs.DENSE, inputs.FIXED_UNION][int(rng.integers(0, 4))]
+        T = int(rng.integers(2100, 3300))
+        l = int(rng.integers(8, 130))
+        c = int(rng.integers(1, l + 1)) if pattern != inputs.DENSE else 0
+        dtype = ["bf16", "f32"][int(rng.integers(0, 2))]
+        cases.append((pattern, 1, 2, T, 64, l, c, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_long_cases(6, 4711),
+                         ids=lambda c: f"p{c[0]}_T{c[3]}l{c[5]}c{c[6]}_{c[7]}")
+def test_random_long_shapes(case):
+    """As test_random_shapes, at lengths where long key columns are split."""
+    _check_random(case)
+
+
 @pytest.mark.parametrize("case", _random_cases(100, 31337),
                          ids=lambda c: f"p{c[0]}_B{c[1]}H{c[2]}T{c[3]}D{c[4]}l{c[5]}_{c[7]}")
 def test_random_shapes(case):
     """Seeded random patterns, dtypes, head dims, lengths, strides and summary sets (counts
     or explicit offsets), each against the whole oracle."""
+    _check_random(case)
+
+
+def _check_random(case):
     pattern, B, H, T, D, l, c, dtype = case
     log(f"random shape {case}")
     q, k, v, do = inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=T * 131 + l, n=4)
