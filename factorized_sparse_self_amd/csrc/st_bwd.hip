@@ -728,6 +728,21 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const V8 p8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
+      // bf16 summary heads carry P to dV as hi + lo: a summary key is
+      // attended by many rows that each see few keys, so its dv sums many
+      // large weights, and bf16 rounding of each (relative 2^-9) could add up
+      // past the error bound; elsewhere weights spread thinly over the keys
+      constexpr bool kPLo = std::is_same<E, bf16>::value && (KC == K_SUMMARY || KC == K_SUMMARY_R1);
+      V8 p8lo{};
+      if constexpr (kPLo) {
+        f32x4 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r0[i] = sc[2 * kk][i] - (float)p8[i];
+          r1[i] = sc[2 * kk + 1][i] - (float)p8[4 + i];
+        }
+        p8lo = pack_b_operand<E>(r0, r1);
+      }
       const V8 ds8 = pack_b_operand<E>(dp[2 * kk], dp[2 * kk + 1]);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
@@ -736,6 +751,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
         const V8 ag = concat(lds_read_tr<E>((const E*)rg0), lds_read_tr<E>((const E*)(rg0 + 16 * S::RB)));
         const V8 aq = concat(lds_read_tr<E>((const E*)rq0), lds_read_tr<E>((const E*)(rq0 + 16 * S::RB)));
         dv[d] = mfma16(ag, p8, dv[d]);
+        if constexpr (kPLo) dv[d] = mfma16(ag, p8lo, dv[d]);
         dk[d] = mfma16(aq, ds8, dk[d]);
       }
     }

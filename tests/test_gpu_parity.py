@@ -289,6 +289,14 @@ def _random_cases(n, seed):
     return cases
 
 
+def test_summary_key_weight_rounding():
+    """A bf16 case where a summary key's dv sums 145 rows' weights, most of them large
+    (rows that see only four summary keys).  Rounding each weight to bf16 before the dV
+    product moved dv[0, 1, 74, 23] by 0.029, past the bound (0.0278); the summary heads
+    carry the weights to dV in two parts instead.  Found by the seeded random sweep."""
+    _check_random((inputs.FIXED, 2, 3, 249, 32, 104, (13, 23, 74, 96), "bf16"))
+
+
 def _random_long_cases(n, seed):
     """n seeded random problems long enough (T > 2048) that key columns of more than 32
     row blocks exist, so that dk/dv runs its split partials and reduction."""
