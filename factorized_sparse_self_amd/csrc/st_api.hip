@@ -166,6 +166,25 @@ int build_plan(const PlanKey& key, Plan* plan) {
       pair_ptr[kind][pb + 1] = (int32_t)pair_entry[kind].size();
     }
   }
+  // Rows whose weights enter dV of a 16-bit summary head with their low part
+  // too: the first K l-blocks, K = max(8, ceil(l / c^2)).  A row in l-block b
+  // sees about c*b summary keys, so a summary key's weights from rows past K
+  // add at most about (l / c^2) * sum_{b>K} 1/b^2 ~ l / (c^2 K) to the sum of
+  // squared weights whose bf16 rounding errors walk randomly: at most ~1, far
+  // inside the error bound.
+  int64_t plo_rows = 0;
+  if (uses_summary(key.pattern)) {
+    const int64_t cc = std::max(1, key.c);
+    const int64_t K = std::max<int64_t>(8, (key.l + cc * cc - 1) / (cc * cc));
+    plo_rows = (K + 1) * key.l;
+  }
+  // first CSC entry in [a, b) of a summary kind whose row block starts at or
+  // past plo_rows (rows of summary kinds are positions)
+  auto entry_lo = [&](const KindLayout& L, int a, int b) {
+    if (L.geo.code != K_SUMMARY && L.geo.code != K_SUMMARY_R1) return a;
+    while (a < b && (int64_t)L.row_idx[a] * kBlock < plo_rows) ++a;
+    return a;
+  };
   const bool merged = is_union(key.pattern);
   const int n_pass = merged ? 2 : 1;
   // kind of head bh in pass p
@@ -231,7 +250,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
         const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
         const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
         if (e1 - e0 <= split) {
-          dkdv.push_back({kb, bh, e0, e1, -1, kind, 0, 0});
+          dkdv.push_back({kb, bh, e0, e1, -1, kind, entry_lo(L, e0, e1), 0});
           dcost.push_back(e1 - e0 + 1);
           dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
           continue;
@@ -241,7 +260,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
           const int range = L.row_idx[a] / split;
           int b = a;
           while (b < e1 && L.row_idx[b] / split == range) ++b;
-          dkdv.push_back({kb, bh, a, b, slots++, kind, 0, 0});
+          dkdv.push_back({kb, bh, a, b, slots++, kind, entry_lo(L, a, b), 0});
           dcost.push_back(b - a + 1);
           dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);
           a = b;

@@ -673,8 +673,10 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (item.e0 + j < item.e1) issue(item.e0 + j, j);
-  // One code path for every block: PARTIAL blocks only add the mask.
-  for (int e = item.e0, stg = 0; e < item.e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
+  // One code path for every block (PARTIAL blocks only add the mask), in two
+  // copies: with and without the low part of P in dV.
+  auto step = [&](auto with_lo, int e, int stg) __attribute__((always_inline)) {
+    constexpr bool LO = decltype(with_lo)::value;
     const bool full = (entries[e] & kFullBit) != 0;
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, item.e1 - 1 - e));
     __syncthreads();
@@ -728,13 +730,8 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const V8 p8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
-      // bf16 summary heads carry P to dV as hi + lo: a summary key is
-      // attended by many rows that each see few keys, so its dv sums many
-      // large weights, and bf16 rounding of each (relative 2^-9) could add up
-      // past the error bound; elsewhere weights spread thinly over the keys
-      constexpr bool kPLo = std::is_same<E, bf16>::value && (KC == K_SUMMARY || KC == K_SUMMARY_R1);
       V8 p8lo{};
-      if constexpr (kPLo) {
+      if constexpr (LO) {
         f32x4 r0, r1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -751,10 +748,25 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
         const V8 ag = concat(lds_read_tr<E>((const E*)rg0), lds_read_tr<E>((const E*)(rg0 + 16 * S::RB)));
         const V8 aq = concat(lds_read_tr<E>((const E*)rq0), lds_read_tr<E>((const E*)(rq0 + 16 * S::RB)));
         dv[d] = mfma16(ag, p8, dv[d]);
-        if constexpr (kPLo) dv[d] = mfma16(ag, p8lo, dv[d]);
+        if constexpr (LO) dv[d] = mfma16(ag, p8lo, dv[d]);
         dk[d] = mfma16(aq, ds8, dk[d]);
       }
     }
+  };
+  // bf16 summary heads carry P to dV as hi + lo for the rows that see few
+  // summary keys (entries [e0, e_lo): the CSC lists row blocks in order).  A
+  // summary key is attended by every later row, and a row in l-block b sees
+  // about c*b summary keys, so the early rows give it large weights whose bf16
+  // rounding (relative 2^-9) can add up past the error bound; later rows' and
+  // other kinds' weights spread thinly.
+  constexpr bool kPLo = std::is_same<E, bf16>::value && (KC == K_SUMMARY || KC == K_SUMMARY_R1);
+  if constexpr (kPLo) {
+    int e = item.e0, stg = 0;
+    for (; e < imin(item.e_lo, item.e1); ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) step(std::true_type(), e, stg);
+    for (; e < item.e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) step(std::false_type(), e, stg);
+  } else {
+    for (int e = item.e0, stg = 0; e < item.e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1)
+      step(std::false_type(), e, stg);
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
 

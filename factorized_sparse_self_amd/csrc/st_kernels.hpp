@@ -43,8 +43,10 @@ enum OutMode : int { OUT_FINAL = 0, OUT_CARRY = 1, OUT_MERGE = 2 };
 // Work item of the dK/dV pass: key block kb of head bh, CSC entries [e0, e1).
 // slot >= 0: the key block is split over several items and this one writes
 // fp32 partial sums to workspace slot `slot`; slot < 0: write dk / dv directly.
+// 16-bit summary heads: entries [e0, e_lo) are row blocks whose weights enter
+// dV with their low part too.
 struct DkdvItem {
-  int kb, bh, e0, e1, slot, kind, pad0, pad1;
+  int kb, bh, e0, e1, slot, kind, e_lo, pad;
 };
 
 // Work item of the forward and dq passes: row block qb of head bh, whose
