@@ -788,8 +788,8 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   }
 }
 
-// At most 168 VGPRs: three waves per SIMD (three workgroups per CU with the
-// two-stage ring) beat two waves with deeper prefetch; four waves would spill.
+// At least three waves per SIMD (at most 168 VGPRs), which beat two waves with
+// deeper prefetch; at D <= 64 the kernel needs about 120, so four fit.
 template <typename E, int D, int NS, int C0, int C1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_b16_kernel(
     BwdArgs a) {
