@@ -147,7 +147,7 @@ def st_release() -> None:
     lib().st_release()
 
 
-KERNEL_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce")
+KERNEL_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce", "bwd_delta")
 
 
 def st_timing_enable(on: bool) -> None:
@@ -182,6 +182,17 @@ def _shape_check(name, x, like):
         raise ValueError(f"{name} must be on q's device")
 
 
+def _lse_check(lse, q):
+    import torch
+    B, H, T, _ = q.shape
+    if not isinstance(lse, torch.Tensor) or not lse.is_cuda:
+        raise ValueError("lse must be a GPU tensor")
+    if lse.device != q.device:
+        raise ValueError("lse must be on q's device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+
+
 def _dtype_code(dtype):
     import torch
     codes = {torch.bfloat16: ST_BF16, torch.float16: ST_F16, torch.float32: ST_F32}
@@ -209,8 +220,7 @@ def st_sparse_attn_fwd(q, k, v, pattern: int, l: int, c=0, out=None, lse=None):
     if lse is None:
         lse = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
     _shape_check("out", out, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    _lse_check(lse, q)
     n, offs = _summary(c)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -231,8 +241,7 @@ def st_sparse_attn_bwd(q, k, v, out, lse, dout, pattern: int, l: int, c=0,
     B, H, T, D = q.shape
     for name, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
         _shape_check(name, x, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    _lse_check(lse, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv

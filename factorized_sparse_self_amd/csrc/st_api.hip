@@ -48,9 +48,10 @@ struct PlanKey {
 struct PassItems {
   RowItem* row_items = nullptr;    // row blocks: fp32 forward and dq
   PairItem* pair_items = nullptr;  // row-block pairs: 16-bit forward and dq
+  PairItem* pre_items = nullptr;   // the pairs with kPairPre: 16-bit delta pre-pass
   DkdvItem* dkdv_items = nullptr;
   ReduceItem* red_items = nullptr;
-  int n_row_items = 0, n_pair_items = 0, n_dkdv_items = 0, n_red_items = 0;
+  int n_row_items = 0, n_pair_items = 0, n_pre_items = 0, n_dkdv_items = 0, n_red_items = 0;
 };
 
 struct Plan {
@@ -166,32 +167,105 @@ int build_plan(const PlanKey& key, Plan* plan) {
       pair_ptr[kind][pb + 1] = (int32_t)pair_entry[kind].size();
     }
   }
-  // Rows whose weights enter dV of a 16-bit summary head with their low part
-  // too: the first K l-blocks, K = max(8, ceil(l / c^2)).  A row in l-block b
-  // sees about c*b summary keys, so a summary key's weights from rows past K
-  // add at most about (l / c^2) * sum_{b>K} 1/b^2 ~ l / (c^2 K) to the sum of
-  // squared weights whose bf16 rounding errors walk randomly: at most ~1, far
-  // inside the error bound.
-  int64_t plo_rows = 0;
-  if (uses_summary(key.pattern)) {
-    const int64_t cc = std::max(1, key.c);
-    const int64_t K = std::max<int64_t>(8, (key.l + cc * cc - 1) / (cc * cc));
-    plo_rows = (K + 1) * key.l;
+  // Row blocks whose weights and dS enter the bf16 dV and dK products with
+  // their low parts too: those with a row that attends at most n_lo keys.  A
+  // row with n keys gives each weights of about 1/n, and the bf16 rounding
+  // errors of the weights a key receives walk randomly, with a variance
+  // proportional to the sum of their squares.  Where each row adds one key to
+  // the next (window, strided, own-block and full attention) the rows past
+  // n_lo = 64 keys add about e/n_lo to that sum (e for the spread of softmax
+  // weights under Gaussian logits); a summary row in l-block b attends c*b
+  // keys and l rows share that count, so rows past K blocks add about
+  // e l / (c^2 K), and K = ceil(8 l / c^2) keeps it at about 1/3 too.
+  auto lo_keys = [&](const Geometry& g) -> int64_t {
+    if (g.code != K_SUMMARY && g.code != K_SUMMARY_R1) return 64;
+    const int64_t cc = std::max(1, g.c);
+    return std::max<int64_t>(64, cc * ((8 * (int64_t)g.l + cc * cc - 1) / (cc * cc)));
+  };
+  std::vector<uint8_t> lo_block[2];
+  for (int kind = 0; kind < 2; ++kind) {
+    const KindLayout& L = lay.kind[kind];
+    const int64_t n_lo = lo_keys(L.geo);
+    lo_block[kind].assign(L.n_qb, 0);
+    for (int qb = 0; qb < L.n_qb; ++qb)
+      for (int i = 0; i < kBlock; ++i) {
+        const int R = qb * kBlock + i;
+        const int t = row_position(L.geo, R);
+        if (t < 0) continue;
+        int lo = 1, hi = 0;
+        row_interval(L.geo, R, t, lo, hi);
+        if (lo <= hi && hi - lo + 1 <= n_lo) {
+          lo_block[kind][qb] = 1;
+          break;
+        }
+      }
   }
-  // first CSC entry in [a, b) of a summary kind whose row block starts at or
-  // past plo_rows (rows of summary kinds are positions)
-  auto entry_lo = [&](const KindLayout& L, int a, int b) {
-    if (L.geo.code != K_SUMMARY && L.geo.code != K_SUMMARY_R1) return a;
-    while (a < b && (int64_t)L.row_idx[a] * kBlock < plo_rows) ++a;
+  // first CSC entry in [a, b) whose row block needs no low part (along a key
+  // block's list the rows' key counts only grow, so the others precede it)
+  auto entry_lo = [&](int kind, int a, int b) {
+    const KindLayout& L = lay.kind[kind];
+    while (a < b && lo_block[kind][L.row_idx[a]]) ++a;
     return a;
   };
   const bool merged = is_union(key.pattern);
   const int n_pass = merged ? 2 : 1;
+  // Per position: the keys each kind gives it, whether they lie in one 64-key
+  // block, and from these the RowFlag bits of the 16-bit dq (a merged head
+  // counts both kinds' keys; its Delta always comes from the pre-pass, since
+  // each dq pass sees only one kind's keys).
+  std::vector<int32_t> n_keys[2];
+  std::vector<uint8_t> one_block[2], row_flags[2];
+  for (int kind = 0; kind < 2; ++kind) {
+    const KindLayout& L = lay.kind[kind];
+    n_keys[kind].assign(key.T, 0);
+    one_block[kind].assign(key.T, 0);
+    for (int R = 0; R < L.geo.n_rows; ++R) {
+      const int t = row_position(L.geo, R);
+      if (t < 0) continue;
+      int lo = 1, hi = 0;
+      row_interval(L.geo, R, t, lo, hi);
+      if (lo > hi) continue;
+      n_keys[kind][t] = hi - lo + 1;
+      one_block[kind][t] = lo / kBlock == hi / kBlock;
+    }
+  }
+  for (int kind = 0; kind < 2; ++kind) {
+    row_flags[kind].assign(key.T, 0);
+    for (int t = 0; t < key.T; ++t) {
+      const int n = merged ? n_keys[0][t] + n_keys[1][t] : n_keys[kind][t];
+      if (n == 0 || n > kDqLoKeys) continue;
+      uint8_t f = ROW_LO;
+      if (!merged && one_block[kind][t])
+        f |= ROW_INBLOCK;
+      else
+        f |= ROW_PRE;
+      row_flags[kind][t] = f;
+    }
+  }
+  // kPairLo / kPairPre of the pair of row blocks (2pb, 2pb+1) of a kind: rows
+  // that attend keys of that kind only count
+  auto pair_flags = [&](int kind, int pb) {
+    const KindLayout& L = lay.kind[kind];
+    int f = 0;
+    for (int R = 2 * pb * kBlock; R < std::min(L.geo.n_rows, (2 * pb + 2) * kBlock); ++R) {
+      const int t = row_position(L.geo, R);
+      if (t < 0 || n_keys[kind][t] == 0) continue;
+      if (row_flags[kind][t] & ROW_LO) f |= kPairLo;
+      if (row_flags[kind][t] & ROW_PRE) f |= kPairPre;
+    }
+    return f;
+  };
+  std::vector<int> pflags[2];
+  for (int kind = 0; kind < 2; ++kind) {
+    const int n_pairs = (int)pair_ptr[kind].size() - 1;
+    pflags[kind].resize(n_pairs);
+    for (int pb = 0; pb < n_pairs; ++pb) pflags[kind][pb] = pair_flags(kind, pb);
+  }
   // kind of head bh in pass p
   auto kind_of = [&](int p, int bh) { return merged ? p : (bh % key.H) & 1; };
   struct HostPass {
     std::vector<RowItem> rows;
-    std::vector<PairItem> pairs;
+    std::vector<PairItem> pairs, pre;
     std::vector<DkdvItem> dkdv;
     std::vector<ReduceItem> red;
   } hp[2];
@@ -220,13 +294,27 @@ int build_plan(const PlanKey& key, Plan* plan) {
       const int n_pairs = (int)pair_ptr[kind].size() - 1;
       for (int pb = 0; pb < n_pairs; ++pb) {
         const int e0 = pair_ptr[kind][pb], e1 = pair_ptr[kind][pb + 1];
-        pairs.push_back({pb, bh, kind, e0, e1, e1 > e0 ? pair_entry[kind][e0] : 0u, 0, 0});
+        pairs.push_back({pb, bh, kind, e0, e1, e1 > e0 ? pair_entry[kind][e0] : 0u, pflags[kind][pb], 0});
         pcost.push_back(e1 - e0 + 1);
         pgroup.push_back((int64_t)bh * 65536 + 2 * pb / chunk[kind]);
       }
     }
     for (int i : xcd_order(pcost, pgroup))
       hp[p].pairs.push_back(i < 0 ? PairItem{-1, -1, 0, 0, 0, 0u, 0, 0} : pairs[i]);
+    // the delta pre-pass: pairs that hold a ROW_PRE row
+    {
+      std::vector<PairItem> pre;
+      std::vector<int64_t> cost, group;
+      for (const PairItem& it : pairs)
+        if (it.flags & kPairPre) {
+          pre.push_back(it);
+          cost.push_back(it.e1 - it.e0 + 1);
+          group.push_back((int64_t)it.bh * 65536 + 2 * it.pb / chunk[it.kind]);
+        }
+      if (!pre.empty())
+        for (int i : xcd_order(cost, group))
+          hp[p].pre.push_back(i < 0 ? PairItem{-1, -1, 0, 0, 0, 0u, 0, 0} : pre[i]);
+    }
 
     // dK/dV items: every key block of every head.  A key block whose row-block
     // list is longer than `split` is split at row-block multiples of `split`,
@@ -250,7 +338,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
         const int e0 = L.col_ptr[kb], e1 = L.col_ptr[kb + 1];
         const int first_q = e1 > e0 ? L.row_idx[e0] : 0;
         if (e1 - e0 <= split) {
-          dkdv.push_back({kb, bh, e0, e1, -1, kind, entry_lo(L, e0, e1), 0});
+          dkdv.push_back({kb, bh, e0, e1, -1, kind, entry_lo(kind, e0, e1), 0});
           dcost.push_back(e1 - e0 + 1);
           dgroup.push_back((int64_t)bh * 65536 + first_q / chunk[kind]);
           continue;
@@ -260,7 +348,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
           const int range = L.row_idx[a] / split;
           int b = a;
           while (b < e1 && L.row_idx[b] / split == range) ++b;
-          dkdv.push_back({kb, bh, a, b, slots++, kind, entry_lo(L, a, b), 0});
+          dkdv.push_back({kb, bh, a, b, slots++, kind, entry_lo(kind, a, b), 0});
           dcost.push_back(b - a + 1);
           dgroup.push_back((int64_t)bh * 65536 + L.row_idx[a] / chunk[kind]);
           a = b;
@@ -276,7 +364,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   KindDev kinds_host[2];
   size_t off_kinds = blob.add(kinds_host, sizeof(kinds_host));
   const size_t off_sigma = blob.add(lay.summary.data(), lay.summary.size() * sizeof(int32_t));
-  size_t offs[2][10];
+  size_t offs[2][11];
   for (int kind = 0; kind < 2; ++kind) {
     const KindLayout& L = lay.kind[kind];
     offs[kind][0] = blob.add(L.row_ptr.data(), L.row_ptr.size() * 4);
@@ -292,11 +380,13 @@ int build_plan(const PlanKey& key, Plan* plan) {
     offs[kind][7] = blob.add(csc.data(), csc.size() * 4);
     offs[kind][8] = blob.add(pair_ptr[kind].data(), pair_ptr[kind].size() * 4);
     offs[kind][9] = blob.add(pair_entry[kind].data(), pair_entry[kind].size() * 4);
+    offs[kind][10] = blob.add(row_flags[kind].data(), row_flags[kind].size());
   }
-  size_t off_items[2][4];
+  size_t off_items[2][5];
   for (int p = 0; p < n_pass; ++p) {
     off_items[p][0] = blob.add(hp[p].rows.data(), hp[p].rows.size() * sizeof(RowItem));
     off_items[p][1] = blob.add(hp[p].pairs.data(), hp[p].pairs.size() * sizeof(PairItem));
+    off_items[p][4] = blob.add(hp[p].pre.data(), hp[p].pre.size() * sizeof(PairItem));
     off_items[p][2] = blob.add(hp[p].dkdv.data(), hp[p].dkdv.size() * sizeof(DkdvItem));
     off_items[p][3] = blob.add(hp[p].red.data(), hp[p].red.size() * sizeof(ReduceItem));
   }
@@ -323,6 +413,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
     k.csc_entry = (const uint32_t*)(dbase + offs[kind][7]);
     k.pair_ptr = (const int32_t*)(dbase + offs[kind][8]);
     k.pair_entry = (const uint32_t*)(dbase + offs[kind][9]);
+    k.row_flags = (const uint8_t*)(dbase + offs[kind][10]);
   }
   std::memcpy(blob.bytes.data() + off_kinds, kinds_host, sizeof(kinds_host));
   e = hipMemcpy(plan->dmem, blob.bytes.data(), blob.bytes.size(), hipMemcpyHostToDevice);
@@ -333,10 +424,12 @@ int build_plan(const PlanKey& key, Plan* plan) {
     PassItems& P = plan->pass[p];
     P.row_items = (RowItem*)(dbase + off_items[p][0]);
     P.pair_items = (PairItem*)(dbase + off_items[p][1]);
+    P.pre_items = (PairItem*)(dbase + off_items[p][4]);
     P.dkdv_items = (DkdvItem*)(dbase + off_items[p][2]);
     P.red_items = (ReduceItem*)(dbase + off_items[p][3]);
     P.n_row_items = (int)hp[p].rows.size();
     P.n_pair_items = (int)hp[p].pairs.size();
+    P.n_pre_items = (int)hp[p].pre.size();
     P.n_dkdv_items = (int)hp[p].dkdv.size();
     P.n_red_items = (int)hp[p].red.size();
   }
@@ -496,14 +589,14 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   Plan* plan = nullptr;
   rc = get_plan({device, pattern, T, l, c, B, H, canonical_summary(pattern, l, c, summary)}, &plan);
   if (rc != ST_OK) return rc;
-  // workspace: Delta, lse2, split partials, and for merged heads the first
-  // pass's fp32 dq, dk, dv
+  // workspace: Delta, lse2, split partials, for merged heads the first pass's
+  // fp32 dq, dk, dv, and the pre-pass Delta
   const size_t rows = (size_t)B * H * T;
   const size_t delta_bytes = align_up(rows * sizeof(float), 256);
   const size_t partial_bytes = align_up((size_t)plan->n_slots * 2 * kBlock * D * sizeof(float), 256);
   const size_t carry_bytes = plan->n_pass == 2 ? align_up(rows * D * sizeof(float), 256) : 0;
   void* ws = nullptr;
-  rc = get_workspace(device, 2 * delta_bytes + partial_bytes + 3 * carry_bytes, &ws);
+  rc = get_workspace(device, 3 * delta_bytes + partial_bytes + 3 * carry_bytes, &ws);
   if (rc != ST_OK) return rc;
   unsigned char* wb = (unsigned char*)ws;
   BwdArgs a;
@@ -522,6 +615,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.carry_dq = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes) : nullptr;
   a.carry_dk = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes + carry_bytes) : nullptr;
   a.carry_dv = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes + 2 * carry_bytes) : nullptr;
+  a.ndelta_pre = (float*)(wb + 2 * delta_bytes + partial_bytes + 3 * carry_bytes);
   a.BH = B * H;
   a.H = H;
   a.T = T;
@@ -531,20 +625,46 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.pattern = pattern;
   a.out_mode = OUT_FINAL;
   hipStream_t s = (hipStream_t)stream;
-  // merged heads: every launch of the first pass (carry) precedes the second
-  // (merge) on the stream
-  for (int p = 0; p < plan->n_pass; ++p) {
+  // Every dq launch precedes every dk/dv launch on the stream: the 16-bit dq
+  // passes complete Delta, which dk/dv reads.  Merged heads: within each
+  // stage the first pass (carry) precedes the second (merge).
+  auto set_pass = [&](int p) {
     const PassItems& P = plan->pass[p];
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
     // 16-bit dq: one workgroup per pair of row blocks; fp32: per row block
     a.dq_items = P.row_items;
     a.dq_pairs = P.pair_items;
-    const int n_dq = Is16<TE>::value ? P.n_pair_items : P.n_row_items;
     a.dkdv_items = P.dkdv_items;
     a.red_items = P.red_items;
-    e = D == 32 ? launch_bwd<TE, 32>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
-        : D == 64 ? launch_bwd<TE, 64>(a, n_dq, P.n_dkdv_items, P.n_red_items, s)
-                  : launch_bwd<TE, 128>(a, n_dq, P.n_dkdv_items, P.n_red_items, s);
+  };
+  // 16-bit: the delta pre-pass of every pass first (rows with few keys whose
+  // exact Delta the dq pass cannot form inside one key block)
+  if (Is16<TE>::value)
+    for (int p = 0; p < plan->n_pass; ++p) {
+      set_pass(p);
+      const PassItems& P = plan->pass[p];
+      if (P.n_pre_items == 0) continue;
+      a.dq_pairs = P.pre_items;
+      e = D == 32 ? launch_bwd_delta<TE, 32>(a, P.n_pre_items, s)
+          : D == 64 ? launch_bwd_delta<TE, 64>(a, P.n_pre_items, s)
+                    : launch_bwd_delta<TE, 128>(a, P.n_pre_items, s);
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+  for (int p = 0; p < plan->n_pass; ++p) {
+    set_pass(p);
+    const PassItems& P = plan->pass[p];
+    const int n_dq = Is16<TE>::value ? P.n_pair_items : P.n_row_items;
+    e = D == 32 ? launch_bwd_dq<TE, 32>(a, n_dq, s)
+        : D == 64 ? launch_bwd_dq<TE, 64>(a, n_dq, s)
+                  : launch_bwd_dq<TE, 128>(a, n_dq, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  for (int p = 0; p < plan->n_pass; ++p) {
+    set_pass(p);
+    const PassItems& P = plan->pass[p];
+    e = D == 32 ? launch_bwd_dkdv<TE, 32>(a, P.n_dkdv_items, P.n_red_items, s)
+        : D == 64 ? launch_bwd_dkdv<TE, 64>(a, P.n_dkdv_items, P.n_red_items, s)
+                  : launch_bwd_dkdv<TE, 128>(a, P.n_dkdv_items, P.n_red_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return ST_OK;
@@ -597,7 +717,7 @@ int drain_records() {
 
 }  // namespace
 
-const char* const kKernelNames[KID_COUNT] = {"fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce"};
+const char* const kKernelNames[KID_COUNT] = {"fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce", "bwd_delta"};
 
 void timing_begin(int kid, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_timing_mutex);

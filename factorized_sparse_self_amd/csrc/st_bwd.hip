@@ -8,9 +8,10 @@
 //   dq_t = sum_j ds_tj k_j / sqrt(D),  dk_j = sum_t ds_tj q_t / sqrt(D),
 //   dv_j = sum_t p_tj dO_t.
 // In the 16-bit kernels (bf16 or fp16 inputs) P and dS enter the dV, dK and
-// dQ products in the input's type (fp32 accumulation); their rounding is well
-// inside the output tolerance, which the rounding of the stored output O
-// (through Delta) dominates.
+// dQ products in the input's type (fp32 accumulation); bf16 dV and dK add the
+// low parts of P and dS for rows whose weights are large.  Delta for dk / dv
+// is exact: the dq pass adds to dO . O (O rounded to the output type) the sum
+// of its fp32 dS over the row's keys, which is the rounding's contribution.
 // Kernels (one stream, in order):
 //   pre   Delta for every row; zero dk / dv at positions no query attends
 //         (fp32 only: the 16-bit dq kernel does both for its own rows)
@@ -403,7 +404,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
 // first block, 4-7 the second).  Every K and V block is staged once for both
 // row blocks; a wave skips (uniformly) the blocks its own row block does not
 // visit.
-template <typename E, int D, int NS, int KC>
+//
+// Delta.  The dP accumulators start at -Delta_O, with Delta_O = dO . O from
+// the stored (rounded) output.  The fp32 dS summed over a row's keys is then
+// sum_j p_j dp_j - Delta_O, the rounding's share of Delta (the weights sum to
+// 1), so Delta_O plus that sum is the exact Delta, which the dk/dv pass gets.
+// A row with few keys (pairs with kPairLo) gives each of them a large weight,
+// so its own dq needs the exact Delta and dS as hi + lo too: a row whose keys
+// lie in one 64-key block forms the exact Delta from that block's sum before
+// its dQ product (ROW_INBLOCK); for the other such rows (ROW_PRE) a pre-pass
+// of this kernel (DQ_DELTA: no dQ product, no stores but Delta) computes it.
+enum DqMode : int { DQ_MAIN = 0, DQ_DELTA = 1 };
+
+template <typename E, int D, int NS, int KC, int MODE>
 __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem& item,
                                                 unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
@@ -458,7 +471,7 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
   const bool row_live = lo <= hi;
   const int mlo = row_live ? lo : -(1 << 30);
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
-  // Delta_t = dO_t . O_t: each of the row's four lanes holds a quarter of the
+  // Delta_O = dO_t . O_t: each of the row's four lanes holds a quarter of the
   // row of dO (the MFMA operand) and loads the same quarter of O
   const Rsrc ro = make_rsrc((const E*)a.o + base, head_bytes);
   V8 qop[NQ], gop[NQ];
@@ -473,10 +486,17 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
     for (int i = 0; i < 8; ++i) dpart = fmaf((float)gop[s][i], (float)o8[i], dpart);
   }
   // (rows that attend nothing get 0: no pass reads them)
-  const float delta = row_live ? group4_sum(dpart) : 0.f;
+  float delta = row_live ? group4_sum(dpart) : 0.f;
   const float lse2 =
       row_live ? buf_load_f32(make_rsrc(a.lse + (size_t)bh * a.T, (uint32_t)a.T * 4), (uint32_t)t * 4) * kLog2e
                : 0.f;
+  const bool lo_pair = MODE == DQ_MAIN && (item.flags & kPairLo) != 0;  // uniform
+  float inblock = 0.f;  // 1: the row forms its exact Delta inside its one key block
+  if (lo_pair && row_live) {
+    const int rf = kd.row_flags[t];
+    if (rf & ROW_PRE) delta = -a.ndelta_pre[(size_t)bh * a.T + t];
+    if (rf & ROW_INBLOCK) inblock = 1.f;
+  }
   // dP^T accumulates onto -Delta, so dS = P * acc (this lane's column is row t)
   const f32x4 ndelta4 = {-delta, -delta, -delta, -delta};
   // per-lane byte offsets of the MFMA operand reads inside a staged block:
@@ -489,16 +509,21 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
 #pragma unroll
   for (int d = 0; d < ND; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
+  // sum over the row's keys of dS against the Delta in use (fp32, before
+  // rounding): the Delta for dk/dv is that Delta plus this sum
+  float dsum = 0.f;
 
-  // One code path for every block: PARTIAL blocks only add the mask.
-  for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) {
+  // One code path for every block (PARTIAL blocks only add the mask), in two
+  // copies: plain, and for pairs with rows of few keys.
+  auto step = [&](auto lo_c, int e, int stg) __attribute__((always_inline)) {
+    constexpr bool LO = decltype(lo_c)::value;
     const uint32_t entry = e == e0 ? item.first : entries[e];
     const int k0 = (int)(entry & kPairBlockMask) * kBlock;
     const uint32_t hbits = (entry >> (28 + 2 * half)) & 3u;  // this row block's visit / FULL bits
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, e1 - 1 - e));
     __syncthreads();
     if (e + NS - 1 < e1) issue(entries[e + NS - 1], stg == 0 ? NS - 1 : stg - 1);
-    if (!(hbits & kPairVisit)) continue;  // the other row block's key block
+    if (!(hbits & kPairVisit)) return;  // the other row block's key block
     const unsigned char* Kt = ring[stg][0];
     const unsigned char* Vt = ring[stg][1];
     // S^T = K Q^T and dP^T - Delta = V dO^T - Delta
@@ -525,60 +550,127 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
         for (int i = 0; i < 4; ++i)
           if ((uint32_t)(m0 + 16 * b + i) > mspan) sc[b][i] = 0.f;
     }
+    if constexpr (!LO) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[b][i] *= dp[b][i];
-    // dQ^T += K^T dS^T
+        for (int i = 0; i < 4; ++i) {
+          sc[b][i] *= dp[b][i];
+          dsum += sc[b][i];
+        }
+      if constexpr (MODE == DQ_MAIN) {
+        // dQ^T += K^T dS^T
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const V8 ds8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
+        for (int kk = 0; kk < 2; ++kk) {
+          const V8 ds8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const unsigned char* r = Kt + 32 * kk * S::RB + (t_off ^ (32 * d));
-        const V8 ak = concat(lds_read_tr<E>((const E*)r), lds_read_tr<E>((const E*)(r + 16 * S::RB)));
-        acc[d] = mfma16(ak, ds8, acc[d]);
-      }
-    }
-  }
-  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
-  // Delta and lse*log2(e) of every row, for the dk/dv pass that follows (the
-  // first pass of a merged head writes them for every row; its second pass
-  // holds rows that attend nothing, whose values it would zero)
-  if (t >= 0 && lg == 0 && a.out_mode != OUT_MERGE) {
-    a.ndelta[(size_t)bh * a.T + t] = -delta;
-    a.lse2[(size_t)bh * a.T + t] = lse2;
-  }
-  // keys nobody attends (positions outside a summary head's key map) get
-  // dk = dv = 0; each row block's positions cover every such position
-  // (in a merged head the first pass writes them)
-  if constexpr (KC == K_SUMMARY || KC == K_SUMMARY_R1) {
-    if (a.out_mode == OUT_FINAL)
-      for (int u = tid & 255; u < kBlock * CH; u += 256) {
-        const int r = u / CH, ch = u % CH;
-        const int tp = block_position(g, false, qb, r);
-        if (tp >= 0 && !position_is_key(g, tp)) {
-          const uint4 z = {0, 0, 0, 0};
-          *(uint4*)((E*)a.dk + base + (size_t)tp * D + ch * 8) = z;
-          *(uint4*)((E*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+          for (int d = 0; d < ND; ++d) {
+            const unsigned char* r = Kt + 32 * kk * S::RB + (t_off ^ (32 * d));
+            const V8 ak = concat(lds_read_tr<E>((const E*)r), lds_read_tr<E>((const E*)(r + 16 * S::RB)));
+            acc[d] = mfma16(ak, ds8, acc[d]);
+          }
         }
       }
+    } else {
+      // dp <- dS against the Delta in use; sc keeps P
+      float bs = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dp[b][i] *= sc[b][i];
+          bs += dp[b][i];
+        }
+      // a ROW_INBLOCK row has all its keys in this block (else P = 0 here and
+      // bs = 0): bs is then its exact Delta's difference from Delta_O
+      const float corr = inblock * group4_sum(bs);
+      dsum += bs;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[b][i] = fmaf(-sc[b][i], corr, dp[b][i]);
+      // dQ^T += K^T (dS_hi + dS_lo)^T
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const V8 ds8 = pack_b_operand<E>(dp[2 * kk], dp[2 * kk + 1]);
+        f32x4 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r0[i] = dp[2 * kk][i] - (float)ds8[i];
+          r1[i] = dp[2 * kk + 1][i] - (float)ds8[4 + i];
+        }
+        const V8 ds8lo = pack_b_operand<E>(r0, r1);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const unsigned char* r = Kt + 32 * kk * S::RB + (t_off ^ (32 * d));
+          const V8 ak = concat(lds_read_tr<E>((const E*)r), lds_read_tr<E>((const E*)(r + 16 * S::RB)));
+          acc[d] = mfma16(ak, ds8, acc[d]);
+          acc[d] = mfma16(ak, ds8lo, acc[d]);
+        }
+      }
+    }
+  };
+  if (lo_pair) {
+    for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) step(std::true_type(), e, stg);
+  } else {
+    for (int e = e0, stg = 0; e < e1; ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) step(std::false_type(), e, stg);
   }
-  if (t < 0) return;
-  store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
-                     (E*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
+  const float dsum_row = group4_sum(dsum);
+  if constexpr (MODE == DQ_DELTA) {
+    // the pre-pass: exact -Delta of the item's rows (a merged head's second
+    // pass adds its keys' share to the rows it holds; its first pass, whose
+    // kind attends every position, wrote every row)
+    if (t >= 0 && lg == 0) {
+      if (a.out_mode != OUT_MERGE)
+        a.ndelta_pre[(size_t)bh * a.T + t] = -(delta + dsum_row);
+      else if (row_live)
+        a.ndelta_pre[(size_t)bh * a.T + t] -= dsum_row;
+    }
+    return;
+  } else {
+    // -Delta (exact) and lse*log2(e) of every row for the dk/dv pass, which
+    // runs after every dq pass: the first pass of a merged head writes them,
+    // its second adds its own keys' sum to the rows it holds
+    if (t >= 0 && lg == 0) {
+      if (a.out_mode != OUT_MERGE) {
+        a.ndelta[(size_t)bh * a.T + t] = -(delta + dsum_row);
+        a.lse2[(size_t)bh * a.T + t] = lse2;
+      } else if (row_live) {
+        a.ndelta[(size_t)bh * a.T + t] -= dsum_row;
+      }
+    }
+    // keys nobody attends (positions outside a summary head's key map) get
+    // dk = dv = 0; each row block's positions cover every such position
+    // (in a merged head the first pass writes them)
+    if constexpr (KC == K_SUMMARY || KC == K_SUMMARY_R1) {
+      if (a.out_mode == OUT_FINAL)
+        for (int u = tid & 255; u < kBlock * CH; u += 256) {
+          const int r = u / CH, ch = u % CH;
+          const int tp = block_position(g, false, qb, r);
+          if (tp >= 0 && !position_is_key(g, tp)) {
+            const uint4 z = {0, 0, 0, 0};
+            *(uint4*)((E*)a.dk + base + (size_t)tp * D + ch * 8) = z;
+            *(uint4*)((E*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+          }
+        }
+    }
+    if (t < 0) return;
+    store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
+                       (E*)a.dq + base + (size_t)t * D + 4 * lg, acc, a.scale);
+  }
 }
 
-// One kernel per pattern; each workgroup branches once on its head's kind.
-template <typename E, int D, int NS, int C0, int C1>
+// One kernel per pattern and mode; each workgroup branches once on its head's kind.
+template <typename E, int D, int NS, int C0, int C1, int MODE>
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_b16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
   const PairItem item = load_uniform(&a.dq_pairs[blockIdx.x]);
   if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    bwd_dq_b16_body<E, D, NS, C0>(a, item, ring);
+    bwd_dq_b16_body<E, D, NS, C0, MODE>(a, item, ring);
   else
-    bwd_dq_b16_body<E, D, NS, C1>(a, item, ring);
+    bwd_dq_b16_body<E, D, NS, C1, MODE>(a, item, ring);
 }
 
 // dk/dv: Q and dO blocks with their lse*log2(e) and Delta are staged by
@@ -692,74 +784,89 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     }
     if (e + NS - 1 < item.e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
     const Stage& st = ring[stg];
-    // S = Q K^T, and dP - Delta = dO V^T - Delta with the accumulators
-    // starting at -Delta of rows 16b + 4lg + i
-    f32x4 sc[4], dp[4];
+    // The block's 64 rows as NG groups of 16-row sub-blocks: one group with
+    // P and dS in the input type; two with their low parts too, so that the
+    // extra operands fit the same registers.
+    constexpr int NG = LO ? 2 : 1, NB = 4 / NG;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      dp[b] = *(const f32x4*)(&st.ndelta[64 * b + 4 * lg]);
+    for (int gi = 0; gi < NG; ++gi) {
+      // S = Q K^T, and dP - Delta = dO V^T - Delta with the accumulators
+      // starting at -Delta of rows 16b + 4lg + i
+      f32x4 sc[NB], dp[NB];
 #pragma unroll
-      for (int k = 0; k < NQ; ++k) {
-        sc[b] = mfma16(*(const V8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[b]);
-        dp[b] = mfma16(*(const V8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[b]);
-      }
-    }
-    // rows 16b + 4lg + i of this lane's values
+      for (int j = 0; j < NB; ++j) {
+        const int b = gi * NB + j;
+        sc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        dp[j] = *(const f32x4*)(&st.ndelta[64 * b + 4 * lg]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float4 l2 = *(const float4*)(&st.lse2[64 * b + 4 * lg]);
-      sc[b][0] = fast_exp2(fmaf(sc[b][0], sl2, -l2.x));
-      sc[b][1] = fast_exp2(fmaf(sc[b][1], sl2, -l2.y));
-      sc[b][2] = fast_exp2(fmaf(sc[b][2], sl2, -l2.z));
-      sc[b][3] = fast_exp2(fmaf(sc[b][3], sl2, -l2.w));
-    }
-    if (!full) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int4 lo4 = *(const int4*)(&st.lo[16 * b + 4 * lg]);
-        const int4 sp4 = *(const int4*)(&st.span[16 * b + 4 * lg]);
-        if ((uint32_t)(Kl - lo4.x) > (uint32_t)sp4.x) sc[b][0] = 0.f;
-        if ((uint32_t)(Kl - lo4.y) > (uint32_t)sp4.y) sc[b][1] = 0.f;
-        if ((uint32_t)(Kl - lo4.z) > (uint32_t)sp4.z) sc[b][2] = 0.f;
-        if ((uint32_t)(Kl - lo4.w) > (uint32_t)sp4.w) sc[b][3] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) dp[b] *= sc[b];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const V8 p8 = pack_b_operand<E>(sc[2 * kk], sc[2 * kk + 1]);
-      V8 p8lo{};
-      if constexpr (LO) {
-        f32x4 r0, r1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          r0[i] = sc[2 * kk][i] - (float)p8[i];
-          r1[i] = sc[2 * kk + 1][i] - (float)p8[4 + i];
+        for (int k = 0; k < NQ; ++k) {
+          sc[j] = mfma16(*(const V8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[j]);
+          dp[j] = mfma16(*(const V8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[j]);
         }
-        p8lo = pack_b_operand<E>(r0, r1);
       }
-      const V8 ds8 = pack_b_operand<E>(dp[2 * kk], dp[2 * kk + 1]);
+      // rows 16b + 4lg + i of this lane's values
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
-        const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
-        const V8 ag = concat(lds_read_tr<E>((const E*)rg0), lds_read_tr<E>((const E*)(rg0 + 16 * S::RB)));
-        const V8 aq = concat(lds_read_tr<E>((const E*)rq0), lds_read_tr<E>((const E*)(rq0 + 16 * S::RB)));
-        dv[d] = mfma16(ag, p8, dv[d]);
-        if constexpr (LO) dv[d] = mfma16(ag, p8lo, dv[d]);
-        dk[d] = mfma16(aq, ds8, dk[d]);
+      for (int j = 0; j < NB; ++j) {
+        const int b = gi * NB + j;
+        const float4 l2 = *(const float4*)(&st.lse2[64 * b + 4 * lg]);
+        sc[j][0] = fast_exp2(fmaf(sc[j][0], sl2, -l2.x));
+        sc[j][1] = fast_exp2(fmaf(sc[j][1], sl2, -l2.y));
+        sc[j][2] = fast_exp2(fmaf(sc[j][2], sl2, -l2.z));
+        sc[j][3] = fast_exp2(fmaf(sc[j][3], sl2, -l2.w));
+      }
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int b = gi * NB + j;
+          const int4 lo4 = *(const int4*)(&st.lo[16 * b + 4 * lg]);
+          const int4 sp4 = *(const int4*)(&st.span[16 * b + 4 * lg]);
+          if ((uint32_t)(Kl - lo4.x) > (uint32_t)sp4.x) sc[j][0] = 0.f;
+          if ((uint32_t)(Kl - lo4.y) > (uint32_t)sp4.y) sc[j][1] = 0.f;
+          if ((uint32_t)(Kl - lo4.z) > (uint32_t)sp4.z) sc[j][2] = 0.f;
+          if ((uint32_t)(Kl - lo4.w) > (uint32_t)sp4.w) sc[j][3] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) dp[j] *= sc[j];
+#pragma unroll
+      for (int jj = 0; jj < NB / 2; ++jj) {
+        const int kk = gi * (NB / 2) + jj;  // 32-row step
+        const V8 p8 = pack_b_operand<E>(sc[2 * jj], sc[2 * jj + 1]);
+        const V8 ds8 = pack_b_operand<E>(dp[2 * jj], dp[2 * jj + 1]);
+        V8 p8lo{}, ds8lo{};
+        if constexpr (LO) {
+          f32x4 r0, r1, u0, u1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r0[i] = sc[2 * jj][i] - (float)p8[i];
+            r1[i] = sc[2 * jj + 1][i] - (float)p8[4 + i];
+            u0[i] = dp[2 * jj][i] - (float)ds8[i];
+            u1[i] = dp[2 * jj + 1][i] - (float)ds8[4 + i];
+          }
+          p8lo = pack_b_operand<E>(r0, r1);
+          ds8lo = pack_b_operand<E>(u0, u1);
+        }
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const unsigned char* rg0 = st.g + 32 * kk * S::RB + t_off[d];
+          const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
+          const V8 ag = concat(lds_read_tr<E>((const E*)rg0), lds_read_tr<E>((const E*)(rg0 + 16 * S::RB)));
+          const V8 aq = concat(lds_read_tr<E>((const E*)rq0), lds_read_tr<E>((const E*)(rq0 + 16 * S::RB)));
+          dv[d] = mfma16(ag, p8, dv[d]);
+          if constexpr (LO) dv[d] = mfma16(ag, p8lo, dv[d]);
+          dk[d] = mfma16(aq, ds8, dk[d]);
+          if constexpr (LO) dk[d] = mfma16(aq, ds8lo, dk[d]);
+        }
       }
     }
   };
-  // bf16 summary heads carry P to dV as hi + lo for the rows that see few
-  // summary keys (entries [e0, e_lo): the CSC lists row blocks in order).  A
-  // summary key is attended by every later row, and a row in l-block b sees
-  // about c*b summary keys, so the early rows give it large weights whose bf16
-  // rounding (relative 2^-9) can add up past the error bound; later rows' and
-  // other kinds' weights spread thinly.
-  constexpr bool kPLo = std::is_same<E, bf16>::value && (KC == K_SUMMARY || KC == K_SUMMARY_R1);
+  // bf16 carries P to dV and dS to dK as hi + lo for the row blocks whose rows
+  // attend few keys (entries [e0, e_lo): along a key block's CSC list the rows'
+  // key counts only grow).  Such rows give a key large weights, and the bf16
+  // rounding of a large weight (relative 2^-9) summed over the many rows that
+  // share the key can add up past the error bound; rows with many keys spread
+  // their weights thinly.  fp16 rounds 8 times finer and needs no low part.
+  constexpr bool kPLo = std::is_same<E, bf16>::value;
   if constexpr (kPLo) {
     int e = item.e0, stg = 0;
     for (; e < imin(item.e_lo, item.e1); ++e, stg = (stg + 1 == NS) ? 0 : stg + 1) step(std::true_type(), e, stg);
@@ -848,7 +955,24 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(BwdArgs a) {
 }  // namespace
 
 template <typename TE, int D>
-hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStream_t stream) {
+hipError_t launch_bwd_delta(const BwdArgs& a, int n_items, hipStream_t stream) {
+  if constexpr (!Is16<TE>::value) {
+    return hipErrorInvalidValue;  // the fp32 path takes Delta from its fp32 output
+  } else {
+    if (n_items <= 0) return hipSuccess;
+    timing_begin(KID_DELTA, stream);
+    const hipError_t err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
+      hipLaunchKernelGGL((bwd_dq_b16_kernel<TE, D, kDqStages, decltype(c0)::value, decltype(c1)::value, DQ_DELTA>),
+                         dim3(n_items), dim3(kDqThreads), 0, stream, a);
+      return hipGetLastError();
+    });
+    timing_end(KID_DELTA, stream);
+    return err;
+  }
+}
+
+template <typename TE, int D>
+hipError_t launch_bwd_dq(const BwdArgs& a, int n_dq, hipStream_t stream) {
   constexpr int TPR = D / (16 / sizeof(TE));
   const int64_t rows = (int64_t)a.BH * a.T;
   const int64_t pre_blocks = (rows * TPR + kThreads - 1) / kThreads;
@@ -867,8 +991,8 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
     timing_begin(KID_DQ, stream);
     if constexpr (Is16<TE>::value) {
       err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
-        hipLaunchKernelGGL((bwd_dq_b16_kernel<TE, D, kDqStages, decltype(c0)::value, decltype(c1)::value>), dim3(n_dq),
-                           dim3(kDqThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_b16_kernel<TE, D, kDqStages, decltype(c0)::value, decltype(c1)::value, DQ_MAIN>),
+                           dim3(n_dq), dim3(kDqThreads), 0, stream, a);
         return hipGetLastError();
       });
     } else {
@@ -878,6 +1002,12 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
     timing_end(KID_DQ, stream);
     if (err != hipSuccess) return err;
   }
+  return hipSuccess;
+}
+
+template <typename TE, int D>
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, hipStream_t stream) {
+  hipError_t err = hipSuccess;
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
     if constexpr (Is16<TE>::value) {
@@ -904,14 +1034,32 @@ hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStre
   return hipSuccess;
 }
 
-template hipError_t launch_bwd<bf16, 32>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<f16, 32>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<f16, 64>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<f16, 128>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<float, 32>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<float, 64>(const BwdArgs&, int, int, int, hipStream_t);
-template hipError_t launch_bwd<float, 128>(const BwdArgs&, int, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<bf16, 32>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<bf16, 32>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<bf16, 32>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<bf16, 64>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<bf16, 64>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<bf16, 64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<bf16, 128>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<bf16, 128>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<bf16, 128>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<f16, 32>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<f16, 32>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<f16, 32>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<f16, 64>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<f16, 64>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<f16, 64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<f16, 128>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<f16, 128>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<f16, 128>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<float, 32>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<float, 32>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<float, 32>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<float, 64>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<float, 64>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<float, 64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_delta<float, 128>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dq<float, 128>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<float, 128>(const BwdArgs&, int, int, hipStream_t);
 
 }  // namespace st

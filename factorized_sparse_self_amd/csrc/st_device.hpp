@@ -234,6 +234,7 @@ struct KindDev {
   // kPairFull (it is FULL for that row block).
   const int32_t* pair_ptr;
   const uint32_t* pair_entry;
+  const uint8_t* row_flags;  // [T] per position: RowFlag bits of the 16-bit dq
 };
 constexpr uint32_t kPairVisit = 1u, kPairFull = 2u, kPairBlockMask = 0x0fffffffu;
 

@@ -43,8 +43,8 @@ enum OutMode : int { OUT_FINAL = 0, OUT_CARRY = 1, OUT_MERGE = 2 };
 // Work item of the dK/dV pass: key block kb of head bh, CSC entries [e0, e1).
 // slot >= 0: the key block is split over several items and this one writes
 // fp32 partial sums to workspace slot `slot`; slot < 0: write dk / dv directly.
-// 16-bit summary heads: entries [e0, e_lo) are row blocks whose weights enter
-// dV with their low part too.
+// bf16: entries [e0, e_lo) are row blocks whose weights and dS enter dV and dK
+// with their low parts too.
 struct DkdvItem {
   int kb, bh, e0, e1, slot, kind, e_lo, pad;
 };
@@ -59,11 +59,23 @@ struct RowItem {
 // 2pb and 2pb+1 of head bh (head kind `kind`).  Its key-block list is the
 // kind's pair_entry[e0, e1); `first` repeats pair_entry[e0] (when e0 < e1) so
 // that the first tile load is issued without reading the list.
+// `flags`: kPairLo when a row of the pair attends at most kDqLoKeys keys (the
+// dq pass then takes such rows' Delta exactly and carries dS to dQ as hi + lo),
+// kPairPre when such a row's exact Delta comes from the delta pre-pass.
 struct PairItem {
   int pb, bh, kind, e0, e1;
   uint32_t first;
-  int pad0, pad1;
+  int flags, pad;
 };
+constexpr int kPairLo = 1, kPairPre = 2;
+
+// Rows (per position, per head kind) that attend at most kDqLoKeys keys
+// (merged heads: both passes together).  Their bf16 weights and dS are large,
+// so the dq pass gives them an exact Delta and dS as hi + lo.  ROW_INBLOCK:
+// the row's keys lie in one 64-key block, so the dq pass computes its exact
+// Delta inside that block; ROW_PRE: the delta pre-pass computes it.
+constexpr int kDqLoKeys = 32;
+enum RowFlag : uint8_t { ROW_LO = 1, ROW_INBLOCK = 2, ROW_PRE = 4 };
 
 // Reduction of a split key block: partial slots [slot0, slot0 + nsplit).
 struct ReduceItem {
@@ -97,7 +109,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* ndelta;   // [B*H*T] workspace: -rowsum(dout * out), the initial dP accumulator
+  float* ndelta;   // [B*H*T] workspace: -Delta for the dk/dv pass (exact)
+  float* ndelta_pre;  // [B*H*T] workspace: -Delta of ROW_PRE rows, from the delta pre-pass
   float* lse2;     // [B*H*T] workspace: lse * log2(e) (16-bit path; written by dq)
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
@@ -116,7 +129,7 @@ struct BwdArgs {
 };
 
 // Kernel ids for the optional launch timing (names in kKernelNames).
-enum KernelId : int { KID_FWD = 0, KID_PRE, KID_DQ, KID_DKDV, KID_RED, KID_COUNT };
+enum KernelId : int { KID_FWD = 0, KID_PRE, KID_DQ, KID_DKDV, KID_RED, KID_DELTA, KID_COUNT };
 extern const char* const kKernelNames[KID_COUNT];
 
 // Record timing events around a launch when timing is enabled (no-op otherwise).
@@ -126,7 +139,13 @@ void timing_end(int kid, hipStream_t stream);
 template <typename TE, int D>
 hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream);
 
+// The backward in two stages: Delta (fp32) and dq, then dk / dv and the
+// reduction of split key blocks, which read the Delta the first stage wrote.
 template <typename TE, int D>
-hipError_t launch_bwd(const BwdArgs& a, int n_dq, int n_dkdv, int n_red, hipStream_t stream);
+hipError_t launch_bwd_delta(const BwdArgs& a, int n_items, hipStream_t stream);  // 16-bit only
+template <typename TE, int D>
+hipError_t launch_bwd_dq(const BwdArgs& a, int n_dq, hipStream_t stream);
+template <typename TE, int D>
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, hipStream_t stream);
 
 }  // namespace st

@@ -25,3 +25,21 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+# Worst error / bound ratio of each parity check, per test (filled by the GPU
+# parity tests, printed at the end of the run).
+PARITY_RATIOS: dict = {}
+
+
+def pytest_terminal_summary(terminalreporter):
+    if not PARITY_RATIOS:
+        return
+    tr = terminalreporter
+    tr.section("worst error / bound per parity test")
+    for test, checks in PARITY_RATIOS.items():
+        worst = max(checks.values())
+        detail = ", ".join(f"{k} {v:.3f}" for k, v in checks.items())
+        tr.write_line(f"{worst:.3f}  {test}: {detail}")
+    overall = max(max(c.values()) for c in PARITY_RATIOS.values())
+    tr.write_line(f"overall worst error / bound: {overall:.3f}")

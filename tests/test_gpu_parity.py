@@ -1,13 +1,17 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Tolerances are the ones the hot path is held to: max |error| <= 2e-2 for bf16 and fp16
-inputs and <= 1e-4 for fp32 inputs, on out, lse, dq, dk and dv (fp64 oracle).
+Every comparison is end to end: the oracle computes its own fp64 forward (O and
+lse) from q, k and v, and its own backward from q, k, v and dO alone, and the
+library's out, lse, dq, dk and dv are held to it element by element.  The bound
+is max |error| <= 2e-2 for bf16 and fp16 inputs and <= 1e-4 for fp32 inputs,
+and 1e-4 for lse everywhere.  It is the bound itself wherever a result rounded
+correctly to the output type can meet it; only where half an output ulp of the
+exact value is larger than the bound (bf16 values of magnitude 8 or more, whose
+spacing is 1/16) is that half ulp added.  Each check prints its worst ratio of
+error to bound.
+
 Rows with an empty key set must give out == 0 and lse == -inf exactly, single-
 key rows out == v exactly, and keys nobody attends dk == dv == 0 exactly.
-
-The backward is compared with the oracle's backward on the backward's own inputs:
-the forward's output O and lse as the kernel produced them (Delta = dO . O and the
-weights come from them), while the forward is compared with the exact oracle.
 
 Small cases run the whole oracle and span several 64-row blocks with ragged
 tails, hand-picked and seeded-random (pattern, dtype, D, T, l, summary set; a
@@ -34,13 +38,35 @@ TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float3
 
 
 def allowed_error(ref, dtype):
-    """The stated bound on the arithmetic, plus the rounding of the exact value to the
-    output format (half an ulp), which no implementation storing bf16 can avoid: a bf16
-    value in [8, 16) is a multiple of 1/16."""
+    """The stated bound, widened by half an output ulp of the exact value only where
+    that half ulp exceeds the bound: there even the correctly rounded result can miss
+    the bound (a bf16 value in [8, 16) is a multiple of 1/16)."""
     mag = np.abs(np.where(np.isfinite(ref), ref, 0.0))
     e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
     half_ulp = np.where(mag > 0, np.exp2(e - SIGNIFICAND_BITS[dtype]), 0.0)
-    return TOL[dtype] + half_ulp
+    base = TOL[dtype]
+    return np.where(half_ulp > base, base + half_ulp, base)
+
+
+@pytest.fixture(autouse=True)
+def _parity_record(request):
+    """Name the running test for the per-test ratio record."""
+    global _CURRENT
+    _CURRENT = request.node.name
+    yield
+    _CURRENT = None
+
+
+_CURRENT = None
+
+
+def _record(what, ratio):
+    import conftest
+    if _CURRENT is None:
+        return
+    checks = conftest.PARITY_RATIOS.setdefault(_CURRENT, {})
+    key = what.split()[0]
+    checks[key] = max(checks.get(key, 0.0), ratio)
 
 
 def log(msg):
@@ -53,6 +79,7 @@ def f64(x):
 
 
 def assert_close(got, ref, dtype, what):
+    """Element-by-element check against the bound; returns the worst error / bound."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     tol = allowed_error(ref, dtype)
@@ -64,14 +91,17 @@ def assert_close(got, ref, dtype, what):
     if not fin.any():
         return 0.0
     err = np.where(fin, np.abs(got - np.where(fin, ref, 0)), 0)
+    ratio = err / tol
     i = np.unravel_index(int(np.argmax(err)), err.shape)
-    worst = np.unravel_index(int(np.argmax(err - tol)), err.shape)
+    worst = np.unravel_index(int(np.argmax(ratio)), err.shape)
     mag = float(np.max(np.abs(np.where(fin, ref, 0))))
     print(f"  {what}: max abs err {err[i]:.3e} at {tuple(int(x) for x in i)} (got {got[i]:.6g}, "
-          f"ref {ref[i]:.6g}); max |ref| {mag:.3g}; over bound: {int((err > tol).sum())}", flush=True)
-    assert err[worst] <= tol[worst], (f"{what}: error {err[worst]:.3e} at {tuple(int(x) for x in worst)} "
-                                      f"(ref {ref[worst]:.6g}) exceeds {tol[worst]:.3e}")
-    return float(err[i])
+          f"ref {ref[i]:.6g}); max |ref| {mag:.3g}; worst err/bound {ratio[worst]:.3f} "
+          f"(ref {ref[worst]:.6g}); over bound: {int((ratio > 1).sum())}", flush=True)
+    _record(what, float(ratio[worst]))
+    assert ratio[worst] <= 1.0, (f"{what}: error {err[worst]:.3e} at {tuple(int(x) for x in worst)} "
+                                 f"(ref {ref[worst]:.6g}) exceeds {tol[worst]:.3e}")
+    return float(ratio[worst])
 
 
 def run_fwd(q, k, v, pattern, l, c):
@@ -123,7 +153,7 @@ def test_small_forward_backward(case, dtype):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -160,7 +190,7 @@ def test_small_merged_heads(case, dtype):
     # position 0 attends only itself in both sets: out == v exactly
     assert torch.equal(out[:, :, 0].cpu(), v[:, :, 0])
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -189,7 +219,7 @@ def test_small_summary_sets(case, dtype):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, S)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, S, O=f64(out), lse=f64(lse))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, S)
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -236,7 +266,7 @@ def test_small_head_dim_128(case, dtype):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -261,7 +291,7 @@ def test_edge_shapes():
             assert_close(f64(out), O, dtype, "out")
             assert_close(f64(lse), L, "f32", "lse")
             dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-            rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
+            rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
             assert_close(f64(dq), rq, dtype, "dq")
             assert_close(f64(dk), rk, dtype, "dk")
             assert_close(f64(dv), rv, dtype, "dv")
@@ -337,7 +367,7 @@ def _check_random(case):
     assert_close(f64(out), O, dtype, "out")
     assert_close(f64(lse), L, "f32", "lse")
     dq, dk, dv = run_bwd(q, k, v, out, lse, do, pattern, l, c)
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(out), lse=f64(lse))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
     assert_close(f64(dq), rq, dtype, "dq")
     assert_close(f64(dk), rk, dtype, "dk")
     assert_close(f64(dv), rv, dtype, "dv")
@@ -430,17 +460,17 @@ def test_maximum_length():
     torch.cuda.synchronize()
     for name, x in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.isfinite(x).all(), name
-    Q, K, V, G, On, Ln = (DeviceRows(x) for x in (q, k, v, do, out, lse))
+    Q, K, V, G = (DeviceRows(x) for x in (q, k, v, do))
     rows = [0, 1, l - 1, l, T // 2 + 3, T - l - 1, T - 2, T - 1]
     O, L = oracle.forward_rows(Q, K, V, pattern, l, c, rows)
     assert_close(f64(out[:, :, rows]), O, "bf16", "out")
     assert_close(f64(lse[:, :, rows]), L, "f32", "lse")
-    rq = oracle.backward_dq_rows(Q, K, V, G, pattern, l, c, rows, O=On, lse=Ln)
+    rq = oracle.backward_dq_rows(Q, K, V, G, pattern, l, c, rows)
     assert_close(f64(dq[:, :, rows]), rq, "bf16", "dq")
     keys = [5, T - 100, T - 1]
     for h in range(H):
         log(f"  oracle keys head {h}: {keys}")
-        rk, rv = oracle.backward_dkdv_keys(Q, K, V, G, pattern, l, c, keys, heads=[h], O=On, lse=Ln)
+        rk, rv = oracle.backward_dkdv_keys(Q, K, V, G, pattern, l, c, keys, heads=[h])
         assert_close(f64(dk[:, h, keys]), rk[:, h], "bf16", f"dk head {h}")
         assert_close(f64(dv[:, h, keys]), rv[:, h], "bf16", f"dv head {h}")
 
@@ -464,7 +494,7 @@ def test_maximum_heads():
     O, L = oracle.forward(qn, kn, vn, pattern, l, c)
     assert_close(f64(pick(out)), O, "bf16", "out")
     assert_close(f64(pick(lse)), L, "f32", "lse")
-    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c, O=f64(pick(out)), lse=f64(pick(lse)))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
     assert_close(f64(pick(dq)), rq, "bf16", "dq")
     assert_close(f64(pick(dk)), rk, "bf16", "dk")
     assert_close(f64(pick(dv)), rv, "bf16", "dv")
@@ -488,12 +518,11 @@ def test_split_columns_of_a_longer_launch():
     heads = torch.tensor([0, 1, H - 2, H - 1], device="cuda")
     pick = lambda x: x.index_select(1, heads)
     qn, kn, vn, don = (f64(pick(x)) for x in (q, k, v, do))
-    On, Ln = pick(out).float().cpu().numpy(), pick(lse).cpu().numpy()
     rows = sample_rows(T, l, 64, 7)
     O, L = oracle.forward_rows(qn, kn, vn, pattern, l, c, rows)
     assert_close(f64(pick(out))[:, :, rows], O, "bf16", "out")
     assert_close(f64(pick(lse))[:, :, rows], L, "f32", "lse")
-    rq = oracle.backward_dq_rows(qn, kn, vn, don, pattern, l, c, rows, O=On, lse=Ln)
+    rq = oracle.backward_dq_rows(qn, kn, vn, don, pattern, l, c, rows)
     assert_close(f64(pick(dq))[:, :, rows], rq, "bf16", "dq")
     S = inputs.summary_offsets(l, c)
     nb = T // l
@@ -503,7 +532,7 @@ def test_split_columns_of_a_longer_launch():
     for h in range(4):
         log(f"  oracle keys head {h}")
         kk = keys[h % 2]
-        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, pattern, l, c, kk, heads=[h], O=On, lse=Ln)
+        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, pattern, l, c, kk, heads=[h])
         assert_close(f64(pick(dk))[:, h, kk], rk[:, h], "bf16", f"dk head {h}")
         assert_close(f64(pick(dv))[:, h, kk], rv[:, h], "bf16", f"dv head {h}")
 
@@ -600,10 +629,7 @@ def test_workload_forward_backward_sampled(w):
     O, L = oracle.forward_rows(qn, kn, vn, w.pattern, w.l, w.c, rows)
     assert_close(f64(out[:1])[:, :, rows], O, w.dtype, "out")
     assert_close(f64(lse[:1])[:, :, rows], L, "f32", "lse")
-    # the backward's own inputs: the forward's output and lse as the kernel gave them
-    # (float32 holds every 16-bit value exactly)
-    On, Ln = out[:1].float().cpu().numpy(), lse[:1].cpu().numpy()
-    rq = oracle.backward_dq_rows(qn, kn, vn, don, w.pattern, w.l, w.c, rows, O=On, lse=Ln)
+    rq = oracle.backward_dq_rows(qn, kn, vn, don, w.pattern, w.l, w.c, rows)
     assert_close(f64(dq[:1])[:, :, rows], rq, w.dtype, "dq")
     # dense: every head has the same key sets and a key's queries are many, so two heads
     for h in range(2 if w.pattern == inputs.DENSE else w.H):
@@ -611,8 +637,7 @@ def test_workload_forward_backward_sampled(w):
         # long rows (l >= 1024): every attending query is recomputed, so fewer keys
         keys = _keys_for_head(w, kind, 8 if w.l >= 1024 else 24, w.seed + h)
         log(f"  oracle keys head {h}: {len(keys)}")
-        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, w.pattern, w.l, w.c, keys, heads=[h],
-                                             O=On, lse=Ln)
+        rk, rv = oracle.backward_dkdv_keys(qn, kn, vn, don, w.pattern, w.l, w.c, keys, heads=[h])
         assert_close(f64(dk[:1])[:, h, keys], rk[:, h], w.dtype, f"dk head {h}")
         assert_close(f64(dv[:1])[:, h, keys], rv[:, h], w.dtype, f"dv head {h}")
     if w.pattern in (inputs.FIXED, inputs.FIXED_R1):
