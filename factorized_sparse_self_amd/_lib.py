@@ -31,14 +31,15 @@ def _summary(c):
 # name -> (restype, argtypes) of every exported symbol
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_Z = ctypes.c_size_t
 _SIG = {
     "st_layout_build": (_I, [_I, _I, _I, _I, ctypes.POINTER(_P)]),
     "st_layout_build_ex": (_I, [_I, _I, _I, _I, _P, ctypes.POINTER(_P)]),
     "st_layout_dims": (_I, [_P, _I, ctypes.POINTER(ctypes.c_int32)]),
     "st_layout_pairs": (_I, [_P, _I, ctypes.POINTER(ctypes.c_int64)]),
-    "st_layout_maps": (_I, [_P, _I, _P, _P]),
-    "st_layout_csr": (_I, [_P, _I, _P, _P, _P]),
-    "st_layout_csc": (_I, [_P, _I, _P, _P, _P]),
+    "st_layout_maps": (_I, [_P, _I, _P, _Z, _P, _Z]),
+    "st_layout_csr": (_I, [_P, _I, _P, _Z, _P, _Z, _P, _Z]),
+    "st_layout_csc": (_I, [_P, _I, _P, _Z, _P, _Z, _P, _Z]),
     "st_layout_free": (None, [_P]),
     "st_sparse_attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "st_sparse_attn_fwd_f16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
@@ -123,10 +124,10 @@ def st_layout_build(pattern: int, T: int, l: int, c=0) -> list[dict]:
             col_ptr = np.zeros(dims[ST_DIM_KBLOCKS] + 1, np.int32)
             row_idx = np.zeros(max(nnz, 1), np.int32)
             csc_flags = np.zeros(max(nnz, 1), np.uint8)
-            ptr = lambda a: a.ctypes.data_as(_P)  # noqa: E731
-            _check("st_layout_maps", L.st_layout_maps(handle, kind, ptr(row_pos), ptr(key_pos)))
-            _check("st_layout_csr", L.st_layout_csr(handle, kind, ptr(row_ptr), ptr(col_idx), ptr(flags)))
-            _check("st_layout_csc", L.st_layout_csc(handle, kind, ptr(col_ptr), ptr(row_idx), ptr(csc_flags)))
+            buf = lambda a: (a.ctypes.data_as(_P), a.size)  # noqa: E731  (pointer, capacity)
+            _check("st_layout_maps", L.st_layout_maps(handle, kind, *buf(row_pos), *buf(key_pos)))
+            _check("st_layout_csr", L.st_layout_csr(handle, kind, *buf(row_ptr), *buf(col_idx), *buf(flags)))
+            _check("st_layout_csc", L.st_layout_csc(handle, kind, *buf(col_ptr), *buf(row_idx), *buf(csc_flags)))
             out.append({
                 "block": dims[ST_DIM_BLOCK], "n_rows": dims[ST_DIM_ROWS], "n_keys": dims[ST_DIM_KEYS],
                 "n_qb": dims[ST_DIM_QBLOCKS], "n_kb": dims[ST_DIM_KBLOCKS], "nnz": nnz,

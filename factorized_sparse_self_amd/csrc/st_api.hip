@@ -65,13 +65,25 @@ struct Plan {
   }
 };
 
+// Per-device workspace.  Calls on different streams are ordered on it: each
+// call that uses it records `done` on its stream, and a call on another stream
+// first makes its stream wait for that event.
 struct Workspace {
   void* p = nullptr;
   size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  hipStream_t stream = nullptr;  // stream of the last call that used it
+  bool used = false;
 };
+
+// At most kMaxPlans cached plans (per process); past that the least recently
+// used one is dropped, after its device has finished every queued kernel.
+constexpr size_t kMaxPlans = 64;
 
 std::mutex g_mutex;
 std::map<PlanKey, std::unique_ptr<Plan>> g_plans;
+std::map<PlanKey, uint64_t> g_plan_use;  // last use (a counter) of each cached plan
+uint64_t g_plan_clock = 0;
 std::map<int, Workspace> g_workspace;
 
 int hip_fail(const char* what, hipError_t e) {
@@ -437,37 +449,88 @@ int build_plan(const PlanKey& key, Plan* plan) {
   return ST_OK;
 }
 
-// Caller holds g_mutex.
-int get_plan(const PlanKey& key, Plan** out) {
+// Caller holds g_mutex.  A cached plan, or (build == true) a new one.
+int get_plan(const PlanKey& key, Plan** out, bool build = true) {
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
+    g_plan_use[key] = ++g_plan_clock;
     *out = it->second.get();
     return ST_OK;
+  }
+  if (!build) {
+    set_error("no cached plan for this shape and pattern: one call of another attention entry point with "
+              "the same shapes builds it");
+    return ST_ERR_UNSUPPORTED;
+  }
+  if (g_plans.size() >= kMaxPlans) {
+    auto lru = std::min_element(g_plan_use.begin(), g_plan_use.end(),
+                                [](const auto& x, const auto& y) { return x.second < y.second; });
+    const PlanKey old = lru->first;
+    int current = 0;
+    if (hipGetDevice(&current) != hipSuccess) return hip_fail("plan cache", hipErrorInvalidDevice);
+    // kernels still queued may read the plan: let its device drain first
+    hipError_t e = hipSetDevice(old.device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail("plan cache eviction", e);
+    g_plans.erase(old);
+    g_plan_use.erase(old);
+    e = hipSetDevice(current);
+    if (e != hipSuccess) return hip_fail("plan cache eviction", e);
   }
   std::unique_ptr<Plan> plan(new Plan);
   const int rc = build_plan(key, plan.get());
   if (rc != ST_OK) return rc;
   *out = plan.get();
   g_plans[key] = std::move(plan);
+  g_plan_use[key] = ++g_plan_clock;
   return ST_OK;
 }
 
-// Caller holds g_mutex.
-int get_workspace(int device, size_t bytes, void** out) {
+// Caller holds g_mutex.  The device's workspace, at least `bytes` large, made
+// safe for kernels on `stream`: if the last call that used it ran on another
+// stream, `stream` first waits for that call's kernels.  Pair with
+// workspace_done() once the call's kernels are queued.
+int get_workspace(int device, size_t bytes, hipStream_t stream, void** out) {
   Workspace& w = g_workspace[device];
+  hipError_t e = hipSuccess;
+  if (!w.done) {
+    e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      w.done = nullptr;
+      return hip_fail("workspace event", e);
+    }
+  }
   if (w.bytes < bytes) {
+    // the old buffer may still be in use by queued kernels
+    if (w.used) {
+      e = hipEventSynchronize(w.done);
+      if (e != hipSuccess) return hip_fail("workspace", e);
+    }
     if (w.p) (void)hipFree(w.p);
     w.p = nullptr;
     w.bytes = 0;
-    const hipError_t e = hipMalloc(&w.p, bytes);
+    e = hipMalloc(&w.p, bytes);
     if (e != hipSuccess) {
       w.p = nullptr;
       set_error(std::string("workspace allocation: ") + hipGetErrorString(e));
       return ST_ERR_NOMEM;
     }
     w.bytes = bytes;
+  } else if (w.used && w.stream != stream) {
+    e = hipStreamWaitEvent(stream, w.done, 0);
+    if (e != hipSuccess) return hip_fail("workspace", e);
   }
   *out = w.p;
+  return ST_OK;
+}
+
+// Caller holds g_mutex: the call's kernels that use the workspace are queued on `stream`.
+int workspace_done(int device, hipStream_t stream) {
+  Workspace& w = g_workspace[device];
+  const hipError_t e = hipEventRecord(w.done, stream);
+  if (e != hipSuccess) return hip_fail("workspace", e);
+  w.stream = stream;
+  w.used = true;
   return ST_OK;
 }
 
@@ -551,7 +614,7 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
     const size_t rows = (size_t)B * H * T;
     const size_t o_bytes = align_up(rows * D * sizeof(float), 256);
     void* ws = nullptr;
-    rc = get_workspace(device, o_bytes + rows * sizeof(float), &ws);
+    rc = get_workspace(device, o_bytes + rows * sizeof(float), (hipStream_t)stream, &ws);
     if (rc != ST_OK) return rc;
     a.carry_o = (float*)ws;
     a.carry_lse = (float*)((unsigned char*)ws + o_bytes);
@@ -569,6 +632,7 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
                   : launch_fwd<TE, 128>(a, n_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
+  if (plan->n_pass == 2) return workspace_done(device, s);
   return ST_OK;
 }
 
@@ -595,8 +659,9 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   const size_t delta_bytes = align_up(rows * sizeof(float), 256);
   const size_t partial_bytes = align_up((size_t)plan->n_slots * 2 * kBlock * D * sizeof(float), 256);
   const size_t carry_bytes = plan->n_pass == 2 ? align_up(rows * D * sizeof(float), 256) : 0;
+  const size_t ws_bytes = 3 * delta_bytes + partial_bytes + 3 * carry_bytes;
   void* ws = nullptr;
-  rc = get_workspace(device, 3 * delta_bytes + partial_bytes + 3 * carry_bytes, &ws);
+  rc = get_workspace(device, ws_bytes, (hipStream_t)stream, &ws);
   if (rc != ST_OK) return rc;
   unsigned char* wb = (unsigned char*)ws;
   BwdArgs a;
@@ -667,7 +732,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
                   : launch_bwd_dkdv<TE, 128>(a, P.n_dkdv_items, P.n_red_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
-  return ST_OK;
+  return workspace_done(device, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -853,11 +918,11 @@ void st_release(void) {
     kv.second.reset();
   }
   g_plans.clear();
+  g_plan_use.clear();
   for (auto& kv : g_workspace) {
-    if (kv.second.p) {
-      if (have_device) (void)hipSetDevice(kv.first);
-      (void)hipFree(kv.second.p);
-    }
+    if (have_device) (void)hipSetDevice(kv.first);
+    if (kv.second.p) (void)hipFree(kv.second.p);
+    if (kv.second.done) (void)hipEventDestroy(kv.second.done);
   }
   g_workspace.clear();
   if (have_device) (void)hipSetDevice(current);

@@ -233,45 +233,64 @@ int st_layout_pairs(const st_layout* lay, int kind, int64_t* pairs) {
   return ST_OK;
 }
 
-int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, int32_t* key_pos) {
-  const KindLayout* L = kind_of(lay, kind, "st_layout_maps");
-  if (!L || (!row_pos && L->geo.n_rows > 0) || (!key_pos && L->geo.n_keys > 0)) {
-    if (L) set_error("st_layout_maps: null output buffer");
+// A caller buffer for n elements: `cap` (in elements) must hold them, and the
+// pointer may be null only when n is 0.  Nothing is written on failure.
+static int check_out(const char* fn, const char* what, const void* p, size_t cap, size_t n) {
+  if (n > 0 && !p) {
+    set_error(std::string(fn) + ": " + what + " is null");
     return ST_ERR_INVALID;
   }
+  if (cap < n) {
+    set_error(std::string(fn) + ": " + what + " holds " + std::to_string(cap) + " elements, needs " +
+              std::to_string(n));
+    return ST_ERR_BUFFER_TOO_SMALL;
+  }
+  return ST_OK;
+}
+
+int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, size_t row_pos_cap, int32_t* key_pos,
+                   size_t key_pos_cap) {
+  const char* fn = "st_layout_maps";
+  const KindLayout* L = kind_of(lay, kind, fn);
+  if (!L) return ST_ERR_INVALID;
+  int rc = check_out(fn, "row_pos", row_pos, row_pos_cap, (size_t)L->geo.n_rows);
+  if (rc == ST_OK) rc = check_out(fn, "key_pos", key_pos, key_pos_cap, (size_t)L->geo.n_keys);
+  if (rc != ST_OK) return rc;
   for (int R = 0; R < L->geo.n_rows; ++R) row_pos[R] = row_position(L->geo, R);
   for (int K = 0; K < L->geo.n_keys; ++K) key_pos[K] = key_position(L->geo, K);
   return ST_OK;
 }
 
-int st_layout_csr(const st_layout* lay, int kind, int32_t* row_ptr, int32_t* col_idx,
-                  uint8_t* flags) {
-  const KindLayout* L = kind_of(lay, kind, "st_layout_csr");
-  if (!L || !row_ptr || (!L->col_idx.empty() && (!col_idx || !flags))) {
-    if (L) set_error("st_layout_csr: null output buffer");
-    return ST_ERR_INVALID;
-  }
-  std::memcpy(row_ptr, L->row_ptr.data(), L->row_ptr.size() * sizeof(int32_t));
-  if (!L->col_idx.empty()) {
-    std::memcpy(col_idx, L->col_idx.data(), L->col_idx.size() * sizeof(int32_t));
-    std::memcpy(flags, L->flags.data(), L->flags.size());
+// CSR or CSC copy-out: ptr[n_blocks + 1], idx[nnz], flags[nnz].
+static int copy_sparse(const char* fn, const std::vector<int32_t>& ptr_src, const std::vector<int32_t>& idx_src,
+                       const std::vector<uint8_t>& flag_src, int32_t* ptr, size_t ptr_cap, int32_t* idx,
+                       size_t idx_cap, uint8_t* flags, size_t flags_cap) {
+  int rc = check_out(fn, "pointer array", ptr, ptr_cap, ptr_src.size());
+  if (rc == ST_OK) rc = check_out(fn, "index array", idx, idx_cap, idx_src.size());
+  if (rc == ST_OK) rc = check_out(fn, "flags", flags, flags_cap, flag_src.size());
+  if (rc != ST_OK) return rc;
+  std::memcpy(ptr, ptr_src.data(), ptr_src.size() * sizeof(int32_t));
+  if (!idx_src.empty()) {
+    std::memcpy(idx, idx_src.data(), idx_src.size() * sizeof(int32_t));
+    std::memcpy(flags, flag_src.data(), flag_src.size());
   }
   return ST_OK;
 }
 
-int st_layout_csc(const st_layout* lay, int kind, int32_t* col_ptr, int32_t* row_idx,
-                  uint8_t* flags) {
+int st_layout_csr(const st_layout* lay, int kind, int32_t* row_ptr, size_t row_ptr_cap, int32_t* col_idx,
+                  size_t col_idx_cap, uint8_t* flags, size_t flags_cap) {
+  const KindLayout* L = kind_of(lay, kind, "st_layout_csr");
+  if (!L) return ST_ERR_INVALID;
+  return copy_sparse("st_layout_csr", L->row_ptr, L->col_idx, L->flags, row_ptr, row_ptr_cap, col_idx, col_idx_cap,
+                     flags, flags_cap);
+}
+
+int st_layout_csc(const st_layout* lay, int kind, int32_t* col_ptr, size_t col_ptr_cap, int32_t* row_idx,
+                  size_t row_idx_cap, uint8_t* flags, size_t flags_cap) {
   const KindLayout* L = kind_of(lay, kind, "st_layout_csc");
-  if (!L || !col_ptr || (!L->row_idx.empty() && (!row_idx || !flags))) {
-    if (L) set_error("st_layout_csc: null output buffer");
-    return ST_ERR_INVALID;
-  }
-  std::memcpy(col_ptr, L->col_ptr.data(), L->col_ptr.size() * sizeof(int32_t));
-  if (!L->row_idx.empty()) {
-    std::memcpy(row_idx, L->row_idx.data(), L->row_idx.size() * sizeof(int32_t));
-    std::memcpy(flags, L->csc_flags.data(), L->csc_flags.size());
-  }
-  return ST_OK;
+  if (!L) return ST_ERR_INVALID;
+  return copy_sparse("st_layout_csc", L->col_ptr, L->row_idx, L->csc_flags, col_ptr, col_ptr_cap, row_idx,
+                     row_idx_cap, flags, flags_cap);
 }
 
 void st_layout_free(st_layout* lay) { delete lay; }
@@ -285,6 +304,7 @@ const char* st_status_string(int status) {
     case ST_ERR_UNSUPPORTED: return "unsupported configuration";
     case ST_ERR_HIP: return "HIP runtime error";
     case ST_ERR_NOMEM: return "out of memory";
+    case ST_ERR_BUFFER_TOO_SMALL: return "caller buffer too small";
     default: return "unknown status";
   }
 }

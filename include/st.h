@@ -55,8 +55,11 @@
  * hipStream_t; NULL means the default stream) and return without waiting.
  * A call that has to build a LUT or grow the workspace performs blocking
  * host-to-device copies or allocations first.  Calls that use the workspace
- * (every backward call; forward calls with a merged-head pattern) and overlap
- * in time on one device share it and race; serialise them.
+ * (every backward call; forward calls with a merged-head pattern) are ordered
+ * on it across streams: a call on a stream other than the last user's makes
+ * its stream wait (hipStreamWaitEvent) for that user's kernels.  At most 64
+ * plans are cached per process; a new one past that drops the least recently
+ * used, after synchronising that plan's device.
  *
  * Errors.  Every entry point returns ST_OK (0) or a negative st_status; no
  * C++ exception crosses the ABI.  The message of the last failure on the
@@ -77,7 +80,8 @@ typedef enum st_status {
   ST_ERR_INVALID = -1,     /* bad argument: null/misaligned pointer, size out of range */
   ST_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (e.g. D not 32, 64 or 128) */
   ST_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
-  ST_ERR_NOMEM = -4        /* host or device allocation failed */
+  ST_ERR_NOMEM = -4,       /* host or device allocation failed */
+  ST_ERR_BUFFER_TOO_SMALL = -5 /* a caller buffer's capacity is below what the call writes */
 } st_status;
 
 /* Element type of the tensors, for the _ex attention entry points. */
@@ -157,19 +161,23 @@ int st_layout_dims(const st_layout* lay, int kind, int32_t* dims);
 /* Total attended (query, key) pairs of one head of this kind, sum_t |S(t)|. */
 int st_layout_pairs(const st_layout* lay, int kind, int64_t* pairs);
 
-/* Copy the coordinate maps: row_pos[ROWS], key_pos[KEYS] (caller buffers;
- * either may be NULL when its count is 0, as for the CSR and CSC below). */
-int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, int32_t* key_pos);
+/* Copy-outs into caller buffers (host memory).  Each buffer comes with its
+ * capacity in elements; a capacity below the element count the call writes
+ * gives ST_ERR_BUFFER_TOO_SMALL and nothing is written.  A buffer may be NULL
+ * only when its element count is 0 (else ST_ERR_INVALID).  The counts come
+ * from st_layout_dims. */
 
-/* Copy the CSR: row_ptr[QBLOCKS+1], col_idx[NNZ], flags[NNZ] (caller buffers;
- * col_idx and flags may be NULL when NNZ is 0). */
-int st_layout_csr(const st_layout* lay, int kind, int32_t* row_ptr, int32_t* col_idx,
-                  uint8_t* flags);
+/* The coordinate maps: row_pos[ROWS], key_pos[KEYS]. */
+int st_layout_maps(const st_layout* lay, int kind, int32_t* row_pos, size_t row_pos_cap, int32_t* key_pos,
+                   size_t key_pos_cap);
 
-/* Copy the CSC: col_ptr[KBLOCKS+1], row_idx[NNZ], flags[NNZ] (caller buffers;
- * row_idx and flags may be NULL when NNZ is 0). */
-int st_layout_csc(const st_layout* lay, int kind, int32_t* col_ptr, int32_t* row_idx,
-                  uint8_t* flags);
+/* The CSR: row_ptr[QBLOCKS+1], col_idx[NNZ], flags[NNZ]. */
+int st_layout_csr(const st_layout* lay, int kind, int32_t* row_ptr, size_t row_ptr_cap, int32_t* col_idx,
+                  size_t col_idx_cap, uint8_t* flags, size_t flags_cap);
+
+/* The CSC: col_ptr[KBLOCKS+1], row_idx[NNZ], flags[NNZ]. */
+int st_layout_csc(const st_layout* lay, int kind, int32_t* col_ptr, size_t col_ptr_cap, int32_t* row_idx,
+                  size_t row_idx_cap, uint8_t* flags, size_t flags_cap);
 
 void st_layout_free(st_layout* lay);
 
@@ -229,7 +237,7 @@ int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const vo
  * on its launch stream.  st_timing_read() waits for those events and returns,
  * for one kernel, the number of launches and their summed duration in
  * milliseconds since the last st_timing_reset().  Kernel names: "fwd",
- * "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce".  Unknown names give
+ * "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce", "bwd_delta".  Unknown names give
  * ST_ERR_INVALID; a failing event call gives ST_ERR_HIP.
  * ------------------------------------------------------------------------- */
 int st_timing_enable(int on);

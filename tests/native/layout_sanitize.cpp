@@ -39,7 +39,7 @@ void check_kind(const st_layout* lay, int kind, int pattern, int T, int l, int c
   if (st_layout_pairs(lay, kind, &pairs) != ST_OK || pairs < 0) return fail("pairs", pattern, T, l, c, kind);
   // exact-size heap buffers: a write past any of them is reported
   std::vector<int32_t> row_pos(rows), key_pos(keys);
-  if (st_layout_maps(lay, kind, row_pos.data(), key_pos.data()) != ST_OK)
+  if (st_layout_maps(lay, kind, row_pos.data(), row_pos.size(), key_pos.data(), key_pos.size()) != ST_OK)
     return fail("maps", pattern, T, l, c, kind);
   for (int32_t p : row_pos)
     if (p < -1 || p >= T) return fail("row map range", pattern, T, l, c, kind);
@@ -47,10 +47,28 @@ void check_kind(const st_layout* lay, int kind, int pattern, int T, int l, int c
     if (p < -1 || p >= T) return fail("key map range", pattern, T, l, c, kind);
   std::vector<int32_t> row_ptr(nq + 1), col_idx(nnz), col_ptr(nk + 1), row_idx(nnz);
   std::vector<uint8_t> cflags(nnz), kflags(nnz);
-  if (st_layout_csr(lay, kind, row_ptr.data(), col_idx.data(), cflags.data()) != ST_OK)
+  if (st_layout_csr(lay, kind, row_ptr.data(), row_ptr.size(), col_idx.data(), col_idx.size(), cflags.data(),
+                    cflags.size()) != ST_OK)
     return fail("csr", pattern, T, l, c, kind);
-  if (st_layout_csc(lay, kind, col_ptr.data(), row_idx.data(), kflags.data()) != ST_OK)
+  if (st_layout_csc(lay, kind, col_ptr.data(), col_ptr.size(), row_idx.data(), row_idx.size(), kflags.data(),
+                    kflags.size()) != ST_OK)
     return fail("csc", pattern, T, l, c, kind);
+  // one element short in any buffer: refused, nothing written
+  {
+    if (st_layout_csr(lay, kind, row_ptr.data(), row_ptr.size() - 1, col_idx.data(), col_idx.size(), cflags.data(),
+                      cflags.size()) != ST_ERR_BUFFER_TOO_SMALL)
+      return fail("csr short row_ptr", pattern, T, l, c, kind);
+  }
+  if (nnz > 0) {
+    if (st_layout_csc(lay, kind, col_ptr.data(), col_ptr.size(), row_idx.data(), row_idx.size() - 1, kflags.data(),
+                      kflags.size()) != ST_ERR_BUFFER_TOO_SMALL)
+      return fail("csc short row_idx", pattern, T, l, c, kind);
+  }
+  if (rows > 0) {
+    if (st_layout_maps(lay, kind, row_pos.data(), row_pos.size() - 1, key_pos.data(), key_pos.size()) !=
+        ST_ERR_BUFFER_TOO_SMALL)
+      return fail("maps short row_pos", pattern, T, l, c, kind);
+  }
   if (row_ptr[0] != 0 || row_ptr[nq] != nnz || col_ptr[0] != 0 || col_ptr[nk] != nnz)
     return fail("pointer ends", pattern, T, l, c, kind);
   std::vector<std::tuple<int, int, int>> a, b;  // (row block, key block, flag)

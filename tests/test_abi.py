@@ -99,3 +99,48 @@ def test_extended_entry_points_check_dtype_and_summary_without_gpu():
     assert b"ascending" in L.st_last_error()
     assert L.st_sparse_attn_bwd_ex(1, *([fake] * 9), 1, 2, 64, 64, 0, 8, 0, good, None) == -1
     assert b"only taken by the fixed patterns" in L.st_last_error()
+
+
+def test_layout_copy_outs_check_capacity():
+    """A buffer one element short is refused with ST_ERR_BUFFER_TOO_SMALL and left
+    untouched; a null buffer for a non-empty table is ST_ERR_INVALID."""
+    import numpy as np
+    from factorized_sparse_self_amd import lib
+    L = lib()
+    P = ctypes.c_void_p
+    handle = P()
+    assert L.st_layout_build(1, 300, 16, 3, ctypes.byref(handle)) == 0
+    try:
+        dims = (ctypes.c_int32 * 6)()
+        assert L.st_layout_dims(handle, 1, dims) == 0
+        nq, nnz, rows, keys = dims[3], dims[5], dims[1], dims[2]
+        ptr = np.full(nq + 1, -7, np.int32)
+        idx = np.full(nnz, -7, np.int32)
+        flg = np.full(nnz, 9, np.uint8)
+        buf = lambda a, n=None: (a.ctypes.data_as(P), a.size if n is None else n)  # noqa: E731
+        assert L.st_layout_csr(handle, 1, *buf(ptr, nq), *buf(idx), *buf(flg)) == -5
+        assert b"needs" in L.st_last_error()
+        assert (ptr == -7).all() and (idx == -7).all() and (flg == 9).all()
+        assert L.st_layout_csc(handle, 1, *buf(ptr), *buf(idx, nnz - 1), *buf(flg)) == -5
+        assert L.st_layout_csc(handle, 1, *buf(ptr), *buf(idx), *buf(flg, nnz - 1)) == -5
+        assert L.st_layout_csr(handle, 1, *buf(ptr), None, nnz, *buf(flg)) == -1
+        rp, kp = np.zeros(rows, np.int32), np.zeros(keys, np.int32)
+        assert L.st_layout_maps(handle, 1, *buf(rp), *buf(kp, keys - 1)) == -5
+        assert L.st_layout_maps(handle, 1, *buf(rp), *buf(kp)) == 0
+        assert L.st_layout_csr(handle, 1, *buf(ptr), *buf(idx), *buf(flg)) == 0
+        assert ptr[0] == 0 and ptr[-1] == nnz
+        assert L.st_status_string(-5) == b"caller buffer too small"
+    finally:
+        L.st_layout_free(handle)
+
+
+def test_binding_rejects_an_lse_off_the_gpu():
+    """The binding checks lse like the other tensors: a host tensor never reaches
+    the library (checked here without a GPU on the lse check itself)."""
+    import torch
+    from factorized_sparse_self_amd._lib import _lse_check
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lse_check(torch.zeros(1, 2, 8), q)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lse_check(None, q)

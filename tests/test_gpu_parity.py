@@ -428,6 +428,35 @@ def test_results_repeat_bit_for_bit(pattern):
         assert torch.equal(a.view(bits), o.view(bits)), f"{name}: call on another stream differs"
 
 
+def test_two_streams_share_the_workspace_safely():
+    """Backward calls on two streams with no ordering between them give the same bits
+    as the same calls made one after the other: the library orders its workspace
+    across streams (each call waits for the last user's kernels on another stream)."""
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, T, D, l, c = 2, 8, 4096, 64, 128, 8
+    log(f"two streams: fixed B{B} H{H} T{T} D{D} l{l} c{c}")
+    problems = []
+    for seed in (77, 78):
+        q, k, v, do = (x.cuda() for x in inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=seed, n=4))
+        out, lse = st_sparse_attn_fwd(q, k, v, inputs.FIXED, l, c)
+        problems.append((q, k, v, out, lse, do))
+    torch.cuda.synchronize()
+    serial = [[g.clone() for g in st_sparse_attn_bwd(*p, inputs.FIXED, l, c)] for p in problems]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    results = []
+    for rep in range(3):
+        for p, s_ in zip(problems, streams):
+            with torch.cuda.stream(s_):
+                results.append(st_sparse_attn_bwd(*p, inputs.FIXED, l, c))
+    torch.cuda.synchronize()
+    for i, got in enumerate(results):
+        for name, a, b in zip(("dq", "dk", "dv"), serial[i % 2], got):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} of call {i} differs"
+
+
 class DeviceRows:
     """A GPU tensor [B, H, T, ...] seen by the oracle as an array: indexing [b, h, t] or
     [b, h, positions] copies only those rows to the host, as float64.  Lets the oracle
