@@ -49,6 +49,7 @@ _SIG = {
     "st_sparse_attn_bwd_f32": (_I, [_P] * 9 + [_I] * 7 + [_P]),
     "st_sparse_attn_fwd_ex": (_I, [_I] + [_P] * 5 + [_I] * 7 + [_P, _P]),
     "st_sparse_attn_bwd_ex": (_I, [_I] + [_P] * 9 + [_I] * 7 + [_P, _P]),
+    "st_sparse_attn_bwd_noalloc": (_I, [_I] + [_P] * 9 + [_I] * 7 + [_P, _P]),
     "st_timing_enable": (_I, [_I]),
     "st_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
     "st_timing_reset": (None, []),
@@ -259,6 +260,30 @@ def st_sparse_attn_bwd(q, k, v, out, lse, dout, pattern: int, l: int, c=0,
         else:
             _check("st_sparse_attn_bwd_ex", lib().st_sparse_attn_bwd_ex(
                 _dtype_code(q.dtype), *ptrs, B, H, T, D, pattern, l, n, offs.ctypes.data_as(_P), stream))
+    return dq, dk, dv
+
+
+def st_sparse_attn_bwd_noalloc(q, k, v, out, lse, dout, pattern: int, l: int, c=0, dq=None, dk=None, dv=None):
+    """st_sparse_attn_bwd through the entry point that allocates nothing in the library
+    (its workspace is a static device array; the plan must already be cached)."""
+    import torch
+    B, H, T, D = q.shape
+    for name, x in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _shape_check(name, x, q)
+    _lse_check(lse, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _shape_check(name, x, q)
+    n, offs = _summary(c)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+        _check("st_sparse_attn_bwd_noalloc", lib().st_sparse_attn_bwd_noalloc(
+            _dtype_code(q.dtype), *ptrs, B, H, T, D, pattern, l, n,
+            None if offs is None else offs.ctypes.data_as(_P), stream))
     return dq, dk, dv
 
 

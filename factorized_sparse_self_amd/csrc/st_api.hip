@@ -534,6 +534,27 @@ int workspace_done(int device, hipStream_t stream) {
   return ST_OK;
 }
 
+// The static scratch of st_sparse_attn_bwd_noalloc: one copy per device, held
+// until the process ends.  Host code never uses the symbol itself as an
+// address: scratch_address() returns this device's copy, looked up once per
+// device with hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::map<int, void*> g_scratch;  // device -> address of its copy
+
+// Caller holds g_mutex; `device` is current.
+int scratch_address(int device, void** out) {
+  auto it = g_scratch.find(device);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail("static scratch address", e != hipSuccess ? e : hipErrorUnknown);
+    it = g_scratch.emplace(device, ptr).first;
+  }
+  *out = it->second;
+  return ST_OK;
+}
+
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 int check_attn_args(const char* fn, const void* const* ptrs, int n_ptrs, int B, int H, int T, int D,
@@ -636,10 +657,12 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
   return ST_OK;
 }
 
+// Backward.  static_ws: the workspace is this device's static scratch and
+// nothing is allocated (the plan must be cached already).
 template <typename TE>
 int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const void* out,
              const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H, int T,
-             int D, int pattern, int l, int c, const int32_t* summary, void* stream) {
+             int D, int pattern, int l, int c, const int32_t* summary, void* stream, bool static_ws = false) {
   const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
   int rc = check_attn_args(fn, ptrs, 9, B, H, T, D, pattern, l, c, summary);
   if (rc != ST_OK) return rc;
@@ -651,7 +674,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   if (e != hipSuccess) return hip_fail(fn, e);
   std::lock_guard<std::mutex> lock(g_mutex);
   Plan* plan = nullptr;
-  rc = get_plan({device, pattern, T, l, c, B, H, canonical_summary(pattern, l, c, summary)}, &plan);
+  rc = get_plan({device, pattern, T, l, c, B, H, canonical_summary(pattern, l, c, summary)}, &plan, !static_ws);
   if (rc != ST_OK) return rc;
   // workspace: Delta, lse2, split partials, for merged heads the first pass's
   // fp32 dq, dk, dv, and the pre-pass Delta
@@ -661,7 +684,16 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   const size_t carry_bytes = plan->n_pass == 2 ? align_up(rows * D * sizeof(float), 256) : 0;
   const size_t ws_bytes = 3 * delta_bytes + partial_bytes + 3 * carry_bytes;
   void* ws = nullptr;
-  rc = get_workspace(device, ws_bytes, (hipStream_t)stream, &ws);
+  if (static_ws) {
+    if (ws_bytes > kScratchBytes) {
+      set_error(std::string(fn) + ": needs " + std::to_string(ws_bytes) + " bytes of scratch; the static scratch holds " +
+                std::to_string(kScratchBytes));
+      return ST_ERR_UNSUPPORTED;
+    }
+    rc = scratch_address(device, &ws);
+  } else {
+    rc = get_workspace(device, ws_bytes, (hipStream_t)stream, &ws);
+  }
   if (rc != ST_OK) return rc;
   unsigned char* wb = (unsigned char*)ws;
   BwdArgs a;
@@ -732,7 +764,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
                   : launch_bwd_dkdv<TE, 128>(a, P.n_dkdv_items, P.n_red_items, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
-  return workspace_done(device, s);
+  return static_ws ? ST_OK : workspace_done(device, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -870,6 +902,24 @@ int st_sparse_attn_bwd_ex(int dtype, const void* q, const void* k, const void* v
     case ST_F32:
       return attn_bwd<float>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary,
                              stream);
+    default: set_error(std::string(fn) + ": unknown dtype " + std::to_string(dtype)); return ST_ERR_INVALID;
+  }
+}
+
+int st_sparse_attn_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* out,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
+                               int T, int D, int pattern, int l, int c, const int32_t* summary, void* stream) {
+  const char* fn = "st_sparse_attn_bwd_noalloc";
+  switch (dtype) {
+    case ST_BF16:
+      return attn_bwd<bf16>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary, stream,
+                            true);
+    case ST_F16:
+      return attn_bwd<f16>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary, stream,
+                           true);
+    case ST_F32:
+      return attn_bwd<float>(fn, q, k, v, out, lse, dout, dq, dk, dv, B, H, T, D, pattern, l, c, summary, stream,
+                             true);
     default: set_error(std::string(fn) + ": unknown dtype " + std::to_string(dtype)); return ST_ERR_INVALID;
   }
 }

@@ -224,6 +224,25 @@ int st_sparse_attn_bwd_ex(int dtype, const void* q, const void* k, const void* v
                           int H, int T, int D, int pattern, int l, int c, const int32_t* summary,
                           void* stream);
 
+/* Backward that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as st_sparse_attn_bwd_ex.
+ * Instead of the library's workspace it uses a static device array of 64 MiB
+ * (one per device, held until the process ends) and calls no hipMalloc or
+ * hipFree.  It needs the plan of its shapes to be cached: one earlier call of
+ * any other attention entry point with the same (pattern, B, H, T, l, c,
+ * summary set) on this device builds it; otherwise ST_ERR_UNSUPPORTED.  A
+ * call whose workspace would exceed 64 MiB (about B*H*T*12 bytes, plus the
+ * split partials, plus B*H*T*D*12 bytes for merged heads) gives
+ * ST_ERR_UNSUPPORTED.  Nothing in the array needs to start at zero; it keeps
+ * the last call's contents.  Every call on one device shares the array:
+ * calls that overlap in time on one device (any streams) race -- serialise
+ * them. */
+int st_sparse_attn_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* out,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                               int H, int T, int D, int pattern, int l, int c, const int32_t* summary,
+                               void* stream);
+
 /* fp32 twins: same arguments, fp32 tensors. */
 int st_sparse_attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream);
