@@ -156,9 +156,12 @@ def accounting(w):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
-# Slices whose oracle time is estimated above ORACLE_SLICE_S seconds are timed
-# on a subset of their rows instead.
-ORACLE_SLICE_S = 20.0
+# The oracle timing is bounded: when the whole workload would take the pool more
+# than about ORACLE_BUDGET_S seconds, every slice is timed on an evenly spaced
+# subset of its rows instead (and only those rows' FLOP are counted).
+ORACLE_BUDGET_S = 20.0
+# Worker processes: the host's cores, at most this many (a GPU machine's CPU share).
+ORACLE_MAX_WORKERS = 16
 
 
 def _one_thread():
@@ -189,33 +192,38 @@ def _oracle_unit(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(w, acct, units):
-    """Time the oracle on `units` (batch, head-pair) slices, one worker process each.
+def cpu_baseline(w, acct):
+    """Time the oracle on every (batch, head-pair) slice of the workload with a pool of
+    one single-threaded process per host core (at most ORACLE_MAX_WORKERS).
 
-    A slice is the full sequence of two heads (one of each kind), forward and
-    (if the workload has one) backward.  When a slice would take more than
-    about ORACLE_SLICE_S seconds, each worker times the forward and the dq part
-    of the backward on an evenly spaced subset of the rows instead, and only
-    the FLOP of those rows is counted.
+    A slice is the full sequence of two heads (one of each kind), forward and (if the
+    workload has one) backward.  value = the FLOP of the timed work over the pool's
+    wall time.  When the whole workload would take more than about ORACLE_BUDGET_S
+    seconds, each slice is timed on an evenly spaced subset of its rows (forward and
+    the dq part of the backward at those rows) and only those rows' FLOP count.
     """
     import numpy as np
     import oracle
     flop_per_pair = (14 if w.backward else 4) * w.D
     slice_flops = sum(acct["head_pairs"]) * flop_per_pair
+    workers = max(1, min(os.cpu_count() or 1, ORACLE_MAX_WORKERS))
+    slices = [(b, h0) for b in range(w.B) for h0 in range(0, w.H - 1, 2)]
     rows = None
-    slices = [(b, h0) for b in range(w.B) for h0 in range(0, w.H - 1, 2)][:units]
     ctx = mp.get_context("spawn")
-    with ctx.Pool(len(slices), initializer=_one_thread) as pool:
-        # pilot: the forward (+ dq part of the backward) on 16 evenly spaced rows of
-        # every slice at once (the processes slow each other down), the slowest
-        # scaled to a whole slice (the full backward adds the dk/dv part: x 1.4)
+    with ctx.Pool(min(workers, len(slices)), initializer=_one_thread) as pool:
+        n_pool = min(workers, len(slices))
+        # pilot: 16 evenly spaced rows of the first n_pool slices at once (the
+        # processes slow each other down), scaled to whole slices (the full backward
+        # adds the dk/dv part: x 1.4) and to the pool's rounds over all slices
         pilot = np.unique(np.linspace(0, w.T - 1, 16).astype(np.int64))
-        per_row = max(pool.map(_oracle_unit, [(w.name, b, h0, pilot) for b, h0 in slices])) / len(pilot)
-        estimate = per_row * w.T * (1.4 if w.backward else 1.0)
-        print(f"cpu baseline: oracle slice estimated at {estimate:.1f} s", file=sys.stderr, flush=True)
-        if estimate > ORACLE_SLICE_S:
-            n = max(16, int(ORACLE_SLICE_S / 2 / per_row))
-            rows = np.unique(np.linspace(0, w.T - 1, n).astype(np.int64))
+        per_row = max(pool.map(_oracle_unit, [(w.name, b, h0, pilot) for b, h0 in slices[:n_pool]])) / len(pilot)
+        rounds = -(-len(slices) // n_pool)
+        estimate = per_row * w.T * (1.4 if w.backward else 1.0) * rounds
+        print(f"cpu baseline: whole workload estimated at {estimate:.1f} s on {n_pool} processes",
+              file=sys.stderr, flush=True)
+        if estimate > ORACLE_BUDGET_S:
+            n = max(16, int(ORACLE_BUDGET_S / 2 / per_row / rounds))
+            rows = np.unique(np.linspace(0, w.T - 1, min(n, w.T)).astype(np.int64))
             row_pairs = sum(oracle.key_set(w.pattern, kind, int(t), w.T, w.l, w.c).size
                             for kind in (0, 1) for t in rows)
             slice_flops = row_pairs * (10 if w.backward else 4) * w.D
@@ -226,30 +234,37 @@ def cpu_baseline(w, acct, units):
         per_unit = pool.map(_oracle_unit, jobs)
         wall = time.perf_counter() - t0
     flops = len(jobs) * slice_flops
-    busy = max(per_unit)
     what = ("full T={}, {}".format(w.T, "forward + backward" if w.backward else "forward") if rows is None else
-            "{} evenly spaced rows of T={}, forward{} at those rows".format(
+            "{} evenly spaced rows of T={} per slice, forward{} at those rows (a row sample: the rate is "
+            "extrapolated to the workload as FLOP per second)".format(
                 len(rows), w.T, " + the dq part of the backward" if w.backward else ""))
     return {
-        "value": flops / busy / 1e12, "unit": "TFLOP/s", "cores": len(jobs), "kind": "oracle",
-        "sample": (f"{len(jobs)} of {w.B * (w.H // 2)} (batch, head-pair) slices of {w.name}: "
-                   f"batch {jobs[0][1]}, heads {jobs[0][2]}-{jobs[-1][2] + 1}, {what}, fp64 numpy, "
-                   f"one single-threaded process per slice; value = sampled useful FLOP / slowest "
-                   f"slice time"),
+        "value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": n_pool, "kind": "oracle",
+        "sample": (f"all {len(jobs)} (batch, head-pair) slices of {w.name}: {what}; fp64 numpy, one "
+                   f"single-threaded process per core ({n_pool} processes); value = timed useful FLOP / "
+                   f"pool wall time"),
         "seconds_per_slice": [round(x, 3) for x in per_unit], "wall_s": round(wall, 3),
-        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
     }
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family / model / stepping."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    return (f"{name} (family {info.get('cpu family', '?')}, model {info.get('model', '?')}, "
+            f"stepping {info.get('stepping', '?')})")
 
 
 # ---------------------------------------------------------------------------
@@ -286,11 +301,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fixed_T12288_bf16_fwdbwd")
-    ap.add_argument("--cpu-units", type=int, default=8,
-                    help="(batch, head-pair) slices the oracle baseline times, one process each")
     ap.add_argument("--warmup-seconds", type=float, default=0.3,
                     help="keep warming up (untimed) until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="evict the last-level cache before every step, warm-up and timed ones (for counter "
+                         "runs of cold traffic; the JSON line's timings then include the eviction writes)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -333,7 +349,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    flush_buf = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+
+    def evict(i):
+        """Write 512 MiB, which leaves none of the inputs in the 256 MB last-level cache."""
+        flush_buf.fill_(float(i))
+
     def step():
+        if args.cold:
+            evict(0)
         st_sparse_attn_fwd(q, k, v, w.pattern, w.l, w.c, out=out, lse=lse)
         if w.backward:
             st_sparse_attn_bwd(q, k, v, out, lse, do, w.pattern, w.l, w.c, dq=dq, dk=dk, dv=dv)
@@ -369,38 +393,48 @@ def main():
         st_timing_enable(False)
         return start.elapsed_time(end) / args.steps
 
-    def per_step_median(flush):
+    def per_step_median(flush, instrumented=False):
         """Median of `steps` single-step times (an event pair around each step).
         With `flush`, a 512 MiB buffer is written before every step, outside
         the events, so that no input is left in the 256 MB last-level cache
-        (cold); without it the steps run back to back (warm)."""
-        scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev) if flush else None
+        (cold); without it the steps run back to back (warm).  With
+        `instrumented`, the library also times each kernel (read afterwards)."""
         marks = []
+        st_timing_reset()
+        st_timing_enable(instrumented)
         torch.cuda.synchronize()
         for i in range(args.steps):
             if flush:
-                scratch.fill_(float(i))
+                evict(i)
             s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s_.record(stream)
             step()
             e_.record(stream)
             marks.append((s_, e_))
         torch.cuda.synchronize()
+        st_timing_enable(False)
         return statistics.median(s_.elapsed_time(e_) for s_, e_ in marks)
+
+    def kernel_times():
+        out = {}
+        for name in KERNEL_NAMES:
+            n, tot = st_timing_read(name)
+            if n:
+                out[name] = {"launches_per_step": n / args.steps, "avg_ms": tot / n,
+                             "ms_per_step": tot / args.steps}
+        return out
 
     # The step time comes from a pass without per-kernel events (each event
     # pair adds a few microseconds between kernels); the per-kernel durations
-    # for the roofline come from an identical pass with them.
+    # for the roofline come from an identical pass with them.  The same for
+    # single steps after a last-level-cache eviction (cold).
     ms_per_step = timed_steps(False)
     ms_per_step_instrumented = timed_steps(True)
+    kernels = kernel_times()
     median_warm = per_step_median(False)
     median_cold = per_step_median(True)
-    kernels = {}
-    for name in KERNEL_NAMES:
-        n, tot = st_timing_read(name)
-        if n:
-            kernels[name] = {"launches_per_step": n / args.steps, "avg_ms": tot / n,
-                             "ms_per_step": tot / args.steps}
+    per_step_median(True, instrumented=True)
+    kernels_cold = kernel_times()
 
     useful_tflops = acct["useful_flops"] / (ms_per_step * 1e-3) / 1e12
     executed_tflops = acct["executed_flops"] / (ms_per_step * 1e-3) / 1e12
@@ -425,6 +459,14 @@ def main():
         "useful_tflops": round(dom_flops / dur_s / 1e12, 2),
         "mfma_frac": round(dom_flops / dur_s / 1e12 / peak_flops, 4),
     }
+    # the same kernel with its inputs evicted from the last-level cache before every step
+    roofline_cold = None
+    if dom in kernels_cold:
+        dur_c = kernels_cold[dom]["avg_ms"] * 1e-3
+        ach_c = (dom_bytes / dur_c / 1e9) if bound == "hbm" else (dom_flops / dur_c / 1e12)
+        roofline_cold = {"kernel": dom, "bound": bound, "achieved": round(ach_c, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach_c / peak, 4), "traffic": measured_traffic(dom, w.name + "_cold"),
+                         "avg_ms": round(kernels_cold[dom]["avg_ms"], 4)}
 
     result = {
         "metric": "sparse-attn fwd+bwd useful TFLOP/s & tokens/s at T=12288, % of bf16 MFMA peak",
@@ -453,11 +495,13 @@ def main():
         "executed_gflop_per_step": round(acct["executed_flops"] / 1e9, 3),
         "nnz_pairs": acct["pairs"],
         "kernels": {k_: {kk: round(vv, 5) for kk, vv in v_.items()} for k_, v_ in kernels.items()},
+        "kernels_cold": {k_: round(v_["avg_ms"], 5) for k_, v_ in kernels_cold.items()},
         "layout_build_ms": round(layout_ms, 3),
         "roofline": roofline,
+        "roofline_cold": roofline_cold,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, acct, args.cpu_units)
+        result["cpu_baseline"] = cpu_baseline(w, acct)
     print(json.dumps(result), flush=True)
 
 

@@ -86,6 +86,8 @@ EXTRA_WORKLOADS = [
              True, 1011, note="the fixed workload with 8 summary offsets spread over each block"),
     Workload("fixed_D128_T12288_bf16_fwdbwd", FIXED, 4, 8, 12288, 128, 128, 8, "bf16", True, 1012,
              note="the fixed workload with head dimension 128"),
+    Workload("fixed_T12287_bf16_fwdbwd", FIXED, 4, 8, 12287, 64, 128, 8, "bf16", True, 1013,
+             note="the fixed workload one position short: T a multiple of neither l nor the 64-row block"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
