@@ -146,7 +146,7 @@ struct StageRows {
       const BlockPart bp = block_part(g, keys, blk);
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int q = bp.base + off[i];
+        const int q = (residue_major(g) && row[i] >= bp.split ? bp.base2 : bp.base) + off[i];
         p[i] = (row[i] < bp.limit && q < g.T) ? q : -1;
       }
     } else {

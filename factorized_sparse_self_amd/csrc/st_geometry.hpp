@@ -8,7 +8,10 @@
 // attends a single contiguous run [lo, hi] of kernel keys:
 //   K_LOCAL       rows = keys = positions; [max(0, t-l+1), t]
 //   K_STRIDE      residue-major: position m*l + r <-> r*n_pad + m; the strided
-//                 set of t is the class prefix [r*n_pad, R]
+//                 set of t is the class prefix [r*n_pad, R].  n_pad is the
+//                 class length rounded up to kClassGran = kBlock / 2, so a
+//                 64-block holds one class, or the tail of one and the head
+//                 of the next (96-long classes fill 64-blocks three to two)
 //   K_BLOCK       rows = keys = positions; [l*floor(t/l), t]
 //   K_SUMMARY     compact summary keys b*c + o <-> b*l + S[o] for blocks
 //                 b < ceil(T/l) - 1, S the summary offsets (by default the last
@@ -42,6 +45,7 @@ enum KindCode : int {
 };
 
 constexpr int kBlock = 64;  // LUT block size, rows and keys
+constexpr int kClassGran = kBlock / 2;  // residue-major class padding granule
 
 // Division of a non-negative int by a fixed divisor as multiply-shift
 // (Granlund and Montgomery, 1994): with s = 31 + ceil(log2 d) and
@@ -63,7 +67,7 @@ struct Geometry {
   int T, l, c;
   int n_rows;  // kernel rows, padding included
   int n_keys;  // kernel keys, padding included
-  int n_pad;   // K_STRIDE: class length rounded up to kBlock
+  int n_pad;   // K_STRIDE: class length rounded up to kClassGran
   int n_cls;   // K_STRIDE: number of residue classes, min(l, T)
   FastDiv div_l, div_c, div_pad;  // division by l, c (>= 1) and n_pad (>= 1)
   int blk_c;   // kBlock / c when c divides kBlock (summary blocks per LUT block), else 0
@@ -152,14 +156,12 @@ ST_HD int key_position(const G& g, int K) {
 // the kind is uniform; only the compact summary map divides, by multiply-shift.
 template <class G>
 ST_HD int block_position(const G& g, bool keys, int blk, int i) {
+  const int R = blk * kBlock + i;
   if (residue_major(g)) {
-    // n_pad is a multiple of kBlock, so a block lies inside one residue class
-    const int cls = fdiv(blk * kBlock, g.div_pad);
-    const int m = blk * kBlock - cls * g.n_pad + i;
-    const int p = m * g.l + cls;
+    const int cls = fdiv(R, g.div_pad);
+    const int p = (R - cls * g.n_pad) * g.l + cls;
     return (cls < g.n_cls && p < g.T) ? p : -1;
   }
-  const int R = blk * kBlock + i;
   if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1)) {
     if (R >= g.n_keys) return -1;
     const int q = fdiv(R, g.div_c);
@@ -171,14 +173,16 @@ ST_HD int block_position(const G& g, bool keys, int blk, int i) {
 
 // block_position() split into a part that depends only on the block (uniform)
 // and a part that depends only on the row offset i (per thread, fixed for a
-// kernel's staging rows): position = base + off, valid iff i < limit and
-// position < T.  Available when the map allows it: always for the identity and
-// residue-major maps, and for the compact summary map when c divides kBlock.
+// kernel's staging rows): position = (i < split ? base : base2) + off, valid
+// iff i < limit and position < T.  Only a residue-major block has split <
+// kBlock: its rows from `split` on belong to the next class.  Available when
+// the map allows it: always for the identity and residue-major maps, and for
+// the compact summary map when c divides kBlock.
 struct RowPart {
   int off;
 };
 struct BlockPart {
-  int base, limit;
+  int base, limit, split, base2;
 };
 template <class G>
 ST_HD bool split_position_ok(const G& g, bool keys) {
@@ -196,13 +200,19 @@ ST_HD RowPart row_part(const G& g, bool keys, int i) {
 template <class G>
 ST_HD BlockPart block_part(const G& g, bool keys, int blk) {
   if (residue_major(g)) {
+    // rows [0, split) hold class cls from index m0 on; n_pad and m0 are
+    // multiples of kClassGran, so split >= kClassGran and the remaining
+    // kBlock - split <= n_pad rows hold class cls + 1 from index 0:
+    // position (i - split) * l + cls + 1 = i * l + base2
     const int cls = fdiv(blk * kBlock, g.div_pad);
     const int m0 = blk * kBlock - cls * g.n_pad;
-    return {m0 * g.l + cls, cls < g.n_cls ? kBlock : 0};
+    const int split = imin(kBlock, g.n_pad - m0);
+    const int limit = cls >= g.n_cls ? 0 : (cls + 1 >= g.n_cls ? split : kBlock);
+    return {m0 * g.l + cls, limit, split, cls + 1 - split * g.l};
   }
   if (keys && (g.code == K_SUMMARY || g.code == K_SUMMARY_R1))
-    return {blk * g.blk_c * g.l, g.n_keys - blk * kBlock};
-  return {blk * kBlock, kBlock};
+    return {blk * g.blk_c * g.l, g.n_keys - blk * kBlock, kBlock, 0};
+  return {blk * kBlock, kBlock, kBlock, 0};
 }
 
 // True when position t of this kind is some kernel key (else nobody attends it).

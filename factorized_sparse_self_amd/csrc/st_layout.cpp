@@ -50,7 +50,7 @@ bool make_geometry(int pattern, int kind, int T, int l, int c, const int32_t* si
   g->n_keys = T;
   const int nb = (T + l - 1) / l;  // l-blocks, last one possibly short
   if (g->code == K_STRIDE || g->code == K_STRIDE_X) {
-    g->n_pad = (nb + kBlock - 1) / kBlock * kBlock;
+    g->n_pad = (nb + kClassGran - 1) / kClassGran * kClassGran;
     g->n_cls = l < T ? l : T;
     g->n_rows = g->n_cls * g->n_pad;
     g->n_keys = g->n_rows;

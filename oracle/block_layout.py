@@ -24,9 +24,10 @@ The maps:
 * identity (strided kind 0, fixed kinds 0, dense): R = t and K = j.
 * strided kind 1, residue-major: the positions t = m*l + r of residue class
   r = t mod l become the contiguous run R = r*n_pad + m, with n = ceil(T/l)
-  and n_pad = n rounded up to a multiple of ``bs`` (so no block straddles two
-  classes); rows and keys share the map.  The strided set of t is then the
-  class-r prefix m' <= m.
+  and n_pad = n rounded up to a multiple of ``bs // 2`` (a block then holds
+  one class, or the end of one class and the start of the next); rows and
+  keys share the map.  The strided set of t is then the class-r prefix
+  m' <= m.
 * fixed kind 1, compacted summary keys: K = b*c + o holds position
   b*l + S[o], S the sorted summary offsets (c = |S|; for the default set the
   last c offsets, b*l + (l - c) + o).  Under the strictly-earlier-block reading (FIXED) only
@@ -59,7 +60,8 @@ def kernel_maps(pattern: int, kind: int, T: int, l: int, c: int, bs: int):
     identity = np.arange(T, dtype=np.int64)
     if pattern == STRIDED and kind == 1:
         n = _ceil_div(T, l)
-        n_pad = _ceil_div(n, bs) * bs
+        gran = max(1, bs // 2)
+        n_pad = _ceil_div(n, gran) * gran
         n_cls = min(l, T)
         rows = np.full(n_cls * n_pad, -1, dtype=np.int64)
         for r in range(n_cls):

@@ -59,7 +59,7 @@ int main() {
               for (int b = 0; b < nb_; ++b) {
                 const BlockPart bp = block_part(g, keys, b);
                 for (int i = 0; i < kBlock; ++i) {
-                  const int q = bp.base + row_part(g, keys, i).off;
+                  const int q = (residue_major(g) && i >= bp.split ? bp.base2 : bp.base) + row_part(g, keys, i).off;
                   const int got = (i < bp.limit && q < g.T) ? q : -1;
                   const int want = block_position(g, keys, b, i);
                   if (want != got) {

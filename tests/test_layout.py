@@ -52,8 +52,10 @@ def test_layout_block_counts_of_the_workloads():
     from factorized_sparse_self_amd import st_layout_build
     strided = st_layout_build(inputs.STRIDED, 12288, 128, 0)
     assert strided[0]["nnz"] == 573 and int(strided[0]["flags"].sum()) == 191
-    # strided kind 1: 128 residue classes of 96 positions, padded to 128 rows: 3 pairs each
-    assert strided[1]["nnz"] == 128 * 3
+    # strided kind 1: 128 residue classes of 96 positions, packed back to back (four
+    # classes fill six row blocks, with 10 block pairs: 1, 2, 2, 1, 2, 2)
+    assert strided[1]["n_rows"] == 128 * 96 and strided[1]["nnz"] == 32 * 10
+    assert int(strided[1]["flags"].sum()) == 0  # no block is all one class and causal-free
     fixed = st_layout_build(inputs.FIXED, 12288, 128, 8)
     assert fixed[0]["nnz"] == 288 and int(fixed[0]["flags"].sum()) == 96
     assert fixed[1]["nnz"] == 1224 and int(fixed[1]["flags"].sum()) == 1056
