@@ -86,9 +86,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_f32_kernel(BwdArgs a) {
   const int bh = (int)(row / a.T), t = (int)(row - (int64_t)bh * a.T);
   const Geometry& g = a.kinds[(bh % a.H) & 1].geo;
   if (!position_is_key(g, t)) {
-    const uint4 z = {0, 0, 0, 0};
-    *(uint4*)((TE*)a.dk + row * D + ch * VEC) = z;
-    *(uint4*)((TE*)a.dv + row * D + ch * VEC) = z;
+    store_zero16_nt((TE*)a.dk + row * D + ch * VEC);
+    store_zero16_nt((TE*)a.dv + row * D + ch * VEC);
   }
 }
 
@@ -649,11 +648,27 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
           const int r = u / CH, ch = u % CH;
           const int tp = block_position(g, false, qb, r);
           if (tp >= 0 && !position_is_key(g, tp)) {
-            const uint4 z = {0, 0, 0, 0};
-            *(uint4*)((E*)a.dk + base + (size_t)tp * D + ch * 8) = z;
-            *(uint4*)((E*)a.dv + base + (size_t)tp * D + ch * 8) = z;
+            store_zero16_nt((E*)a.dk + base + (size_t)tp * D + ch * 8);
+            store_zero16_nt((E*)a.dv + base + (size_t)tp * D + ch * 8);
           }
         }
+    }
+    if (a.out_mode == OUT_FINAL) {
+      // whole-line dq rows through LDS (free once every wave is past its last
+      // block), non-temporal
+      using Rows = RowStage<E, D, 16>;
+      static_assert(kDqThreads / 64 * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
+      __syncthreads();
+      Rows rows(&ring[0][0][0] + wave * Rows::BYTES);
+      rows.template put<ND>(0, li, lg, acc, a.scale);
+#pragma unroll
+      for (int j = 0; j < Rows::ROUNDS; ++j) {
+        const int tr = block_position(g, false, qb, sub * 16 + rows.row_of(lane, j));
+        const u32x4 x = rows.get(lane, j);
+        if (tr >= 0)
+          __builtin_nontemporal_store(x, (u32x4*)((E*)a.dq + base + (size_t)tr * D + rows.col_of(lane, j)));
+      }
+      return;
     }
     if (t < 0) return;
     store_grad_row<ND>(a.out_mode, a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg,
@@ -877,6 +892,28 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
 
+  if (item.slot < 0 && a.out_mode == OUT_FINAL) {
+    // whole-line dk and dv rows through LDS (free once every wave is past its
+    // last block), non-temporal
+    using Rows = RowStage<E, D, 16>;
+    static_assert(4 * 2 * Rows::BYTES <= NS * sizeof(Stage), "row staging fits the ring");
+    __syncthreads();
+    unsigned char* wbuf = (unsigned char*)(void*)ring + wave * 2 * Rows::BYTES;
+    Rows rk(wbuf), rv(wbuf + Rows::BYTES);
+    rk.template put<ND>(0, li, lg, dk, a.scale);
+    rv.template put<ND>(0, li, lg, dv, 1.f);
+#pragma unroll
+    for (int j = 0; j < Rows::ROUNDS; ++j) {
+      const int kr = block_position(g, true, kb, wave * 16 + rk.row_of(lane, j));
+      const u32x4 xk = rk.get(lane, j), xv = rv.get(lane, j);
+      if (kr >= 0) {
+        const size_t off = base + (size_t)kr * D + rk.col_of(lane, j);
+        __builtin_nontemporal_store(xk, (u32x4*)((E*)a.dk + off));
+        __builtin_nontemporal_store(xv, (u32x4*)((E*)a.dv + off));
+      }
+    }
+    return;
+  }
   if (item.slot < 0) {
     if (kp < 0) return;
     const int mode = key_out_mode(a, kp);

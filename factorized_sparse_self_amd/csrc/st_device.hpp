@@ -112,6 +112,46 @@ __device__ __forceinline__ typename Vec<E>::x4 lds_read_tr(const E* p) {
 
 __device__ __forceinline__ bool wave_any(bool v) { return __ballot(v) != 0ull; }
 
+// Output rows are written as whole 128-byte lines, 16 bytes per lane.  Rows
+// written once and not read again in the step (dq, dk, dv, and the zero dk /
+// dv rows of keys nobody attends) use non-temporal stores: streamed past the
+// caches, they do not evict the lines of Q, K, V and dO still being read.  A
+// non-temporal store of part of a line costs more than an ordinary one, so
+// only whole lines take them.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_zero16_nt(void* p) {
+  __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, (u32x4*)p);
+}
+
+// Whole-row output of a wave's rows through LDS.  An MFMA output tile leaves
+// each row in four lanes, lane (li, lg) holding elements 16 d + 4 lg .. + 3 of
+// row li, i.e. 8-byte pieces of a line.  RowStage puts a wave's NR rows (NR/16
+// such tiles) into an LDS buffer of the wave at a padded stride, then reads
+// them back as 16-byte chunks, D/8 consecutive lanes per row.
+template <typename E, int D, int NR>
+struct RowStage {
+  static constexpr int RS = D + 8;             // row stride, elements (16 B of padding)
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int BYTES = NR * RS * (int)sizeof(E);
+  static constexpr int ROUNDS = NR * CH / 64;  // chunks per lane
+  static_assert(NR % 16 == 0 && (NR * CH) % 64 == 0, "whole chunks per lane");
+  E* buf;
+  __device__ __forceinline__ explicit RowStage(void* p) : buf((E*)p) {}
+  // rows 16 g + li of the buffer from one tile's ND accumulators, times scale
+  template <int ND>
+  __device__ __forceinline__ void put(int g, int li, int lg, const f32x4* x, float scale) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+      *(typename Vec<E>::x4*)(buf + (16 * g + li) * RS + 16 * d + 4 * lg) = to_x4<E>(x[d] * scale);
+  }
+  // chunk `round` of this lane: its row and the chunk's element offset
+  __device__ __forceinline__ int row_of(int lane, int round) const { return (lane + 64 * round) / CH; }
+  __device__ __forceinline__ int col_of(int lane, int round) const { return (lane + 64 * round) % CH * 8; }
+  __device__ __forceinline__ u32x4 get(int lane, int round) const {
+    return *(const u32x4*)(buf + row_of(lane, round) * RS + col_of(lane, round));
+  }
+};
+
 // Read-only tables (LUTs, schedules) are read through the constant address
 // space: a uniform load from it is a scalar load, so values such as a block
 // index or its FULL flag stay in scalar registers and branches on them are

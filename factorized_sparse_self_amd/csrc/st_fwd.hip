@@ -421,6 +421,32 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
 
+  if (!M || a.out_mode == OUT_FINAL) {
+    // whole-line output rows through LDS (free once every wave is past its
+    // last block); ordinary stores, since the backward reads O again
+    using Rows = RowStage<E, D, 32>;
+    static_assert(4 * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
+    __syncthreads();
+    Rows rows(&ring[0][0][0] + wave * Rows::BYTES);
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const float lsum = group4_sum(l_run[G]);
+      // the output is rounded to 16 bits, so the hardware reciprocal (1 ulp) suffices
+      const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
+      rows.template put<ND>(G, li, lg, acc[G], inv);
+      if (t[G] >= 0 && lg == 0)
+        a.lse[(size_t)bh * a.T + t[G]] = (lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY) * kLn2;
+    }
+#pragma unroll
+    for (int j = 0; j < Rows::ROUNDS; ++j) {
+      const int tr = block_position(g, false, qb, r0 + rows.row_of(lane, j));
+      const u32x4 x = rows.get(lane, j);
+      if (tr >= 0) *(u32x4*)((E*)a.o + base + (size_t)tr * D + rows.col_of(lane, j)) = x;
+    }
+    return;
+  }
+
+  // merged heads: the first pass carries fp32 rows, the second merges them
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
     const float lsum = group4_sum(l_run[G]);
@@ -459,11 +485,7 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
         *(V4*)(O + 16 * d + 4 * lg) = to_x4<E>(c4 * s0 + acc[G][d] * s1);
       }
       if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
-      continue;
     }
-#pragma unroll
-    for (int d = 0; d < ND; ++d) *(V4*)(O + 16 * d + 4 * lg) = to_x4<E>(acc[G][d] * inv);
-    if (lg == 0) a.lse[row] = lse2 * kLn2;
   }
 }
 
