@@ -108,12 +108,17 @@ struct Blob {
 // own L2.  Items are grouped by the inputs they share, groups are assigned to
 // XCDs longest-first (balancing total cost), each XCD's queue runs longest
 // first, and queue x fills workgroup ids x, x + kXcds, ...  Short queues are
-// padded with -1 (an empty item).
+// padded with -1 (an empty item).  Items that cost at most `short_cost` count
+// as equally long and keep their input order, so that short neighbours which
+// read the same blocks (adjacent key blocks of a window or of an l-block in
+// dk/dv) run at the same time and share the XCD's L2, instead of being
+// separated by a sort on their small cost differences.
 constexpr int kXcds = 8;
 // Aim for at least this many groups so that every XCD gets several.
 constexpr int kMinGroups = 64;
 
-std::vector<int> xcd_order(const std::vector<int64_t>& cost, const std::vector<int64_t>& group) {
+std::vector<int> xcd_order(const std::vector<int64_t>& cost, const std::vector<int64_t>& group,
+                           int64_t short_cost = 0) {
   const size_t n = cost.size();
   std::map<int64_t, int64_t> gcost;
   for (size_t i = 0; i < n; ++i) gcost[group[i]] += cost[i];
@@ -130,7 +135,8 @@ std::vector<int> xcd_order(const std::vector<int64_t>& cost, const std::vector<i
   for (size_t i = 0; i < n; ++i) q[gxcd[group[i]]].push_back((int)i);
   size_t maxlen = 0;
   for (auto& v : q) {
-    std::stable_sort(v.begin(), v.end(), [&](int x, int y) { return cost[x] > cost[y]; });
+    std::stable_sort(v.begin(), v.end(),
+                     [&](int x, int y) { return std::max(cost[x], short_cost) > std::max(cost[y], short_cost); });
     maxlen = std::max(maxlen, v.size());
   }
   std::vector<int> order(kXcds * maxlen, -1);
@@ -368,7 +374,9 @@ int build_plan(const PlanKey& key, Plan* plan) {
         hp[p].red.push_back({kb, bh, slot0, slots - slot0, kind, 0, 0, 0});
       }
     }
-    for (int i : xcd_order(dcost, dgroup))
+    // (an item's cost is its row-block count + 1; up to 4 the order is the
+    // key-block order)
+    for (int i : xcd_order(dcost, dgroup, 4))
       hp[p].dkdv.push_back(i < 0 ? DkdvItem{-1, -1, 0, 0, -1, 0, 0, 0} : dkdv[i]);
     max_slots = std::max(max_slots, slots);
   }

@@ -471,7 +471,8 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
   const int mlo = row_live ? lo : -(1 << 30);
   const uint32_t mspan = row_live ? (uint32_t)(hi - lo) : 0u;
   // Delta_O = dO_t . O_t: each of the row's four lanes holds a quarter of the
-  // row of dO (the MFMA operand) and loads the same quarter of O
+  // row of dO (the MFMA operand) and loads the same quarter of O (O is read
+  // nowhere else in the backward: a non-temporal load)
   const Rsrc ro = make_rsrc((const E*)a.o + base, head_bytes);
   V8 qop[NQ], gop[NQ];
   float dpart = 0.f;
@@ -480,7 +481,7 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
     const uint32_t off = t >= 0 ? (uint32_t)(t * D + 32 * s + 8 * lg) * 2 : kOutOfRange;
     qop[s] = __builtin_bit_cast(V8, buf_load16(rq, off));
     gop[s] = __builtin_bit_cast(V8, buf_load16(rg, off));
-    const V8 o8 = __builtin_bit_cast(V8, buf_load16(ro, off));
+    const V8 o8 = __builtin_bit_cast(V8, buf_load16_nt(ro, off));
 #pragma unroll
     for (int i = 0; i < 8; ++i) dpart = fmaf((float)gop[s][i], (float)o8[i], dpart);
   }

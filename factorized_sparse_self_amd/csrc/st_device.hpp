@@ -222,6 +222,11 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+// The same, non-temporal (cache policy nt): for data read once and not again
+// in the step, so that it does not displace lines that are.
+__device__ __forceinline__ uint4 buf_load16_nt(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
 __device__ __forceinline__ float buf_load_f32(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
