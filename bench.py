@@ -160,7 +160,7 @@ def accounting(w):
 # than about ORACLE_BUDGET_S seconds, every slice is timed on an evenly spaced
 # subset of its rows instead (and only those rows' FLOP are counted).
 ORACLE_BUDGET_S = 20.0
-# Worker processes: the host's cores, at most this many (a GPU machine's CPU share).
+# Worker processes: the host's cores, at most this many (the CPU share of one GPU on a shared node).
 ORACLE_MAX_WORKERS = 16
 
 
@@ -313,8 +313,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the sparse attention path is built and timed on a single "
-              "MI355X; runs on more than one GPU are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU: the sparse attention path runs and is timed on a single MI355X "
+              "(heads are independent, so several GPUs would each run their own share of the heads); "
+              "--gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

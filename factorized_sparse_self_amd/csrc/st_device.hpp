@@ -112,12 +112,13 @@ __device__ __forceinline__ typename Vec<E>::x4 lds_read_tr(const E* p) {
 
 __device__ __forceinline__ bool wave_any(bool v) { return __ballot(v) != 0ull; }
 
-// Output rows are written as whole 128-byte lines, 16 bytes per lane.  Rows
-// written once and not read again in the step (dq, dk, dv, and the zero dk /
-// dv rows of keys nobody attends) use non-temporal stores: streamed past the
-// caches, they do not evict the lines of Q, K, V and dO still being read.  A
-// non-temporal store of part of a line costs more than an ordinary one, so
-// only whole lines take them.
+// Output rows are written 16 bytes per lane, D/8 consecutive lanes per row,
+// so that one instruction writes whole 128-byte lines (one row at D = 64, two
+// adjacent rows at D = 32).  Rows written once and not read again in the step
+// (dq, dk, dv, and the zero dk / dv rows of keys nobody attends) use
+// non-temporal stores: streamed past the caches, they do not evict the lines
+// of Q, K, V and dO still being read.  Non-temporal stores of 8-byte pieces of
+// lines were slower than ordinary ones, so the pieces go through LDS first.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_zero16_nt(void* p) {
   __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, (u32x4*)p);
