@@ -30,7 +30,7 @@ namespace {
 // (summary heads) split at kDkdvSplit; launches with many more items than the
 // GPU holds (full attention, long sequences) are balanced by the schedule alone
 // and split nothing, which spares the partials' workspace and traffic.
-constexpr int kDkdvSplit = 32;
+constexpr int kDkdvSplit = 24;
 constexpr int64_t kDkdvSlots = 2048;
 
 struct PlanKey {
