@@ -684,7 +684,7 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   Plan* plan = nullptr;
   rc = get_plan({device, pattern, T, l, c, B, H, canonical_summary(pattern, l, c, summary)}, &plan, !static_ws);
   if (rc != ST_OK) return rc;
-  // workspace: Delta, lse2, split partials, for merged heads the first pass's
+  // workspace: -Delta (fp32 path) or (lse2, -Delta) row pairs (16-bit path), split partials, for merged heads the first pass's
   // fp32 dq, dk, dv, and the pre-pass Delta
   const size_t rows = (size_t)B * H * T;
   const size_t delta_bytes = align_up(rows * sizeof(float), 256);
@@ -714,8 +714,8 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.ndelta = (float*)wb;
-  a.lse2 = (float*)(wb + delta_bytes);
+  a.ndelta = (float*)wb;   // fp32 path
+  a.rowvals = (float*)wb;  // 16-bit path: 8 bytes per row, the first two delta_bytes slots
   a.partial = (float*)(wb + 2 * delta_bytes);
   a.carry_dq = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes) : nullptr;
   a.carry_dk = carry_bytes ? (float*)(wb + 2 * delta_bytes + partial_bytes + carry_bytes) : nullptr;

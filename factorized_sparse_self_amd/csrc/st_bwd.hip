@@ -633,11 +633,12 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
     // runs after every dq pass: the first pass of a merged head writes them,
     // its second adds its own keys' sum to the rows it holds
     if (t >= 0 && lg == 0) {
+      float* rv = a.rowvals + 2 * ((size_t)bh * a.T + t);
       if (a.out_mode != OUT_MERGE) {
-        a.ndelta[(size_t)bh * a.T + t] = -(delta + dsum_row);
-        a.lse2[(size_t)bh * a.T + t] = lse2;
+        rv[0] = lse2;
+        rv[1] = -(delta + dsum_row);
       } else if (row_live) {
-        a.ndelta[(size_t)bh * a.T + t] -= dsum_row;
+        rv[1] -= dsum_row;
       }
     }
     // keys nobody attends (positions outside a summary head's key map) get
@@ -697,8 +698,7 @@ template <int D>
 struct DkdvStage {
   unsigned char q[TileShape<D>::BYTES];
   unsigned char g[TileShape<D>::BYTES];
-  float lse2[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 16)
-  float ndelta[4 * 64];  // -Delta
+  float vals[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 32): lse*log2(e) of each, then -Delta
   int lo[kBlock];       // masking base of each row
   int span[kBlock];     // masking span (unsigned)
 };
@@ -708,7 +708,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   using S = TileShape<D>;
   typedef typename Vec<E>::x8 V8;
   constexpr int NQ = D / 32, ND = D / 16;
-  constexpr int PER_TILE = 2 * S::NI + 2;  // loads per wave per row block: Q, dO, lse2, Delta
+  constexpr int PER_TILE = 2 * S::NI + 1;  // loads per wave per row block: Q, dO, and lse2 with Delta
   using Stage = DkdvStage<D>;
   const int kb = item.kb, bh = item.bh;
   const KindDev kd = load_uniform(&a.kinds[item.kind]);
@@ -719,8 +719,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   const Rsrc rk = make_rsrc((const E*)a.k + base, head_bytes);
   const Rsrc rv = make_rsrc((const E*)a.v + base, head_bytes);
   const Rsrc rg = make_rsrc((const E*)a.dout + base, head_bytes);
-  const Rsrc rl = make_rsrc(a.lse2 + (size_t)bh * a.T, (uint32_t)a.T * 4);
-  const Rsrc rd = make_rsrc(a.ndelta + (size_t)bh * a.T, (uint32_t)a.T * 4);
+  const Rsrc rvals = make_rsrc(a.rowvals + 2 * (size_t)bh * a.T, (uint32_t)a.T * 8);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
@@ -742,12 +741,10 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   const StageRows<1, kBlock> stage_own(g, false, 16 * wave + li);  // this lane's row, lanes 0..15
   const cptr<uint32_t> entries = as_const(kd.csc_entry);
   // LDS addresses, in stage 0, of this wave's 16 Q rows (dO follows at
-  // +BYTES) and of its lse2 slot (Delta follows at +DELTA); stage s at
-  // +s*sizeof(Stage)
-  constexpr uint32_t DELTA = offsetof(Stage, ndelta) - offsetof(Stage, lse2);
+  // +BYTES) and of its row values; stage s at +s*sizeof(Stage)
   static_assert(offsetof(Stage, g) - offsetof(Stage, q) == S::BYTES, "stage layout");
   const uint32_t lds_rows = lds_address(&ring[0].q[16 * wave * S::RB]);
-  const uint32_t lds_vals = lds_address(&ring[0].lse2[64 * wave]);
+  const uint32_t lds_vals = lds_address(&ring[0].vals[64 * wave]);
   auto issue = [&](int e, int stg) {
     const int qb = (int)(entries[e] & ~kFullBit);
     const uint32_t so = stg * (uint32_t)sizeof(Stage);
@@ -760,8 +757,11 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     int lo = 1, hi = 0;
     if (tp[0] >= 0) row_interval(g, qb * kBlock + 16 * wave + li, tp[0], lo, hi);
     const bool live = lo <= hi;
-    stage_row_values(rl, lds_vals + so, lane, live ? tp[0] : -1);
-    stage_row_values(rd, lds_vals + so + DELTA, lane, live ? tp[0] : -1);
+    // one load for both values: lanes 0-15 fetch lse*log2(e) of row li,
+    // lanes 16-31 its -Delta (the pair is adjacent in the workspace), the
+    // other lanes write zeros
+    lds_dma<4>(rvals, lds_vals + so,
+               (lane < 32 && live) ? (uint32_t)tp[0] * 8 + (lane >= 16 ? 4u : 0u) : kOutOfRange);
     if (lane < 16) {
       ring[stg].lo[16 * wave + lane] = live ? lo : -(1 << 30);
       ring[stg].span[16 * wave + lane] = live ? hi - lo : 0;
@@ -813,7 +813,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
       for (int j = 0; j < NB; ++j) {
         const int b = gi * NB + j;
         sc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        dp[j] = *(const f32x4*)(&st.ndelta[64 * b + 4 * lg]);
+        dp[j] = *(const f32x4*)(&st.vals[64 * b + 16 + 4 * lg]);
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
           sc[j] = mfma16(*(const V8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[j]);
@@ -824,7 +824,7 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int b = gi * NB + j;
-        const float4 l2 = *(const float4*)(&st.lse2[64 * b + 4 * lg]);
+        const float4 l2 = *(const float4*)(&st.vals[64 * b + 4 * lg]);
         sc[j][0] = fast_exp2(fmaf(sc[j][0], sl2, -l2.x));
         sc[j][1] = fast_exp2(fmaf(sc[j][1], sl2, -l2.y));
         sc[j][2] = fast_exp2(fmaf(sc[j][2], sl2, -l2.z));

@@ -109,9 +109,9 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* ndelta;   // [B*H*T] workspace: -Delta for the dk/dv pass (exact)
+  float* ndelta;   // [B*H*T] workspace, fp32 path: -Delta for the dq and dk/dv passes
   float* ndelta_pre;  // [B*H*T] workspace: -Delta of ROW_PRE rows, from the delta pre-pass
-  float* lse2;     // [B*H*T] workspace: lse * log2(e) (16-bit path; written by dq)
+  float* rowvals;  // [B*H*T][2] workspace, 16-bit path: lse * log2(e) and -Delta (exact) of each row, from dq
   float* partial;  // [slots][2][64][D] workspace: split dK / dV sums
   int BH, H, T;
   const KindDev* kinds;

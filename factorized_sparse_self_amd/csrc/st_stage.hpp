@@ -83,14 +83,6 @@ __device__ __forceinline__ void stage_rows(Rsrc src, uint32_t rows, int row0, in
   }
 }
 
-// Stage one fp32 value per row for 16 rows: `vals` is the wave-uniform LDS
-// address of a 64-float slot; lane j < 16 fetches position pos (or zero when
-// pos < 0) into slot word j, lanes 16..63 write zeros into the rest.
-__device__ __forceinline__ void stage_row_values(Rsrc src, uint32_t vals, int lane, int pos) {
-  const uint32_t off = (lane < 16 && pos >= 0) ? (uint32_t)pos * 4 : kOutOfRange;
-  lds_dma<4>(src, vals, off);
-}
-
 // Wait until at most n vector-memory loads of this wave are outstanding
 // (loads complete in issue order).  n is a compile-time constant.
 template <int N>
