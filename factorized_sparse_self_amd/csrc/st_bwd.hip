@@ -746,7 +746,8 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   const uint32_t lds_rows = lds_address(&ring[0].q[16 * wave * S::RB]);
   const uint32_t lds_vals = lds_address(&ring[0].vals[64 * wave]);
   auto issue = [&](int e, int stg) {
-    const int qb = (int)(entries[e] & ~kFullBit);
+    const uint32_t ent = entries[e];
+    const int qb = (int)(ent & ~kFullBit);
     const uint32_t so = stg * (uint32_t)sizeof(Stage);
     int p[S::NI];
     stage.positions(g, false, qb, p);
@@ -754,18 +755,23 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     stage_rows<D>(rg, lds_rows + so + S::BYTES, 16 * wave, lane, p);
     int tp[1];
     stage_own.positions(g, false, qb, tp);
-    int lo = 1, hi = 0;
-    if (tp[0] >= 0) row_interval(g, qb * kBlock + 16 * wave + li, tp[0], lo, hi);
-    const bool live = lo <= hi;
+    // a FULL block's rows are all real and attend every key of the block: no
+    // key runs to form or store (its step applies no mask)
+    bool live = true;
+    if (!(ent & kFullBit)) {
+      int lo = 1, hi = 0;
+      if (tp[0] >= 0) row_interval(g, qb * kBlock + 16 * wave + li, tp[0], lo, hi);
+      live = lo <= hi;
+      if (lane < 16) {
+        ring[stg].lo[16 * wave + lane] = live ? lo : -(1 << 30);
+        ring[stg].span[16 * wave + lane] = live ? hi - lo : 0;
+      }
+    }
     // one load for both values: lanes 0-15 fetch lse*log2(e) of row li,
     // lanes 16-31 its -Delta (the pair is adjacent in the workspace), the
     // other lanes write zeros
     lds_dma<4>(rvals, lds_vals + so,
                (lane < 32 && live) ? (uint32_t)tp[0] * 8 + (lane >= 16 ? 4u : 0u) : kOutOfRange);
-    if (lane < 16) {
-      ring[stg].lo[16 * wave + lane] = live ? lo : -(1 << 30);
-      ring[stg].span[16 * wave + lane] = live ? hi - lo : 0;
-    }
   };
 
   // The key block's K and V rows go through the last ring stage (free until
