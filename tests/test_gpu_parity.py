@@ -402,7 +402,7 @@ def test_exact_special_rows(dtype):
                          ids=lambda p: inputs.PATTERN_NAMES[p])
 def test_results_repeat_bit_for_bit(pattern):
     """The same inputs give the same bits on every call, also from another stream: the
-    split key blocks (T = 4096 gives key columns of up to 64 row blocks, split at 32)
+    split key blocks (T = 4096 gives key columns of up to 64 row blocks, split at 24)
     are summed in slot order, and nothing depends on the order workgroups finish."""
     from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
     B, H, T, D, l, c = 1, 4, 4096, 64, 128, 8
@@ -426,6 +426,55 @@ def test_results_repeat_bit_for_bit(pattern):
         bits = torch.int32 if a.dtype == torch.float32 else torch.int16
         assert torch.equal(a.view(bits), b.view(bits)), f"{name}: second call differs"
         assert torch.equal(a.view(bits), o.view(bits)), f"{name}: call on another stream differs"
+
+
+GUARD_CASES = [
+    # (pattern, dtype, D, T, l, c): ragged T; a strided T whose classes straddle 64-blocks;
+    # a merged head; fp32
+    (inputs.STRIDED, "bf16", 64, 395, 33, 0),
+    (inputs.FIXED, "bf16", 64, 1000, 96, 8),
+    (inputs.FIXED, "f16", 32, 300, 20, 3),
+    (inputs.DENSE, "bf16", 128, 200, 16, 0),
+    (inputs.FIXED_UNION, "bf16", 64, 333, 20, 4),
+    (inputs.STRIDED_UNION, "f16", 64, 250, 16, 0),
+    (inputs.STRIDED, "f32", 64, 250, 16, 0),
+]
+
+
+@pytest.mark.parametrize("case", GUARD_CASES,
+                         ids=lambda c: f"{inputs.PATTERN_NAMES[c[0]]}_{c[1]}_D{c[2]}_T{c[3]}_l{c[4]}")
+def test_outputs_stay_inside_their_tensors(case):
+    """Outputs carved out of larger buffers: every byte before and after them keeps its
+    sentinel (the whole-line row stores and the zero fill write only rows of the tensor),
+    and the results equal, bit for bit, those written into plain tensors."""
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    pattern, dtype, D, T, l, c = case
+    B, H, G = 1, 3, 32768  # G: a whole row block of fp32 rows at D = 128
+    log(f"guard: pattern {inputs.PATTERN_NAMES[pattern]} {dtype} B{B} H{H} T{T} D{D} l{l} c{c}")
+    td = TORCH_DTYPE[dtype]
+    g = torch.Generator().manual_seed(515)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g).to(td).cuda() for _ in range(4))
+
+    def guarded(shape, dt):
+        n = math.prod(shape)
+        big = torch.full((n + 2 * G,), -3.0, dtype=dt, device="cuda")
+        return big, big[G:G + n].view(shape)
+
+    bufs = {name: guarded((B, H, T, D), td) for name in ("out", "dq", "dk", "dv")}
+    bufs["lse"] = guarded((B, H, T), torch.float32)
+    st_sparse_attn_fwd(q, k, v, pattern, l, c, out=bufs["out"][1], lse=bufs["lse"][1])
+    st_sparse_attn_bwd(q, k, v, bufs["out"][1], bufs["lse"][1], do, pattern, l, c,
+                       dq=bufs["dq"][1], dk=bufs["dk"][1], dv=bufs["dv"][1])
+    out, lse = st_sparse_attn_fwd(q, k, v, pattern, l, c)
+    dq, dk, dv = st_sparse_attn_bwd(q, k, v, out, lse, do, pattern, l, c)
+    torch.cuda.synchronize()
+    for name, ref in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        big, view = bufs[name]
+        n = view.numel()
+        assert bool((big[:G] == -3.0).all()), f"{name}: written before the tensor"
+        assert bool((big[G + n:] == -3.0).all()), f"{name}: written after the tensor"
+        bits = torch.int32 if ref.dtype == torch.float32 else torch.int16
+        assert torch.equal(view.view(bits), ref.view(bits)), f"{name}: differs from a plain tensor's result"
 
 
 def test_two_streams_share_the_workspace_safely():
