@@ -415,13 +415,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
 // of this kernel (DQ_DELTA: no dQ product, no stores but Delta) computes it.
 enum DqMode : int { DQ_MAIN = 0, DQ_DELTA = 1 };
 
+// Threads of a 16-bit dq workgroup: eight waves over both row blocks of a pair,
+// or at D = 128 (181 VGPRs: one eight-wave workgroup per CU) four waves over one
+// row block of the pair, two workgroups per pair.
+template <int D>
+constexpr int dq_threads() { return D >= 128 ? 256 : kDqThreads; }
+
 template <typename E, int D, int NS, int KC, int MODE>
 __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem& item,
                                                 unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
   typedef typename Vec<E>::x8 V8;
   constexpr int NQ = D / 32, ND = D / 16, CH = D / 8;
-  constexpr int NW = kDqThreads / 64;  // waves
+  constexpr int NW = dq_threads<D>() / 64;  // waves
   // staging: SW waves each stage SR rows of every tile (SNI instructions)
   constexpr int SR = S::RPI <= kBlock / NW ? kBlock / NW : S::RPI;
   constexpr int SW = kBlock / SR, SNI = SR / S::RPI;
@@ -439,7 +445,8 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const int half = wave >> 2, sub = wave & 3;  // row block 2pb + half, rows 16 sub + li
+  // row block 2pb + half, rows 16 sub + li
+  const int half = NW == 8 ? (wave >> 2) : (int)((blockIdx.x >> 3) & 1), sub = wave & 3;
   const int qb = 2 * item.pb + half;
   const bool stager = wave % (NW / SW) == 0;
   const int swave = wave / (NW / SW);
@@ -659,7 +666,7 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
       // whole-line dq rows through LDS (free once every wave is past its last
       // block), non-temporal
       using Rows = RowStage<E, D, 16>;
-      static_assert(kDqThreads / 64 * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
+      static_assert(NW * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
       __syncthreads();
       Rows rows(&ring[0][0][0] + wave * Rows::BYTES);
       rows.template put<ND>(0, li, lg, acc, a.scale);
@@ -680,9 +687,11 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
 
 // One kernel per pattern and mode; each workgroup branches once on its head's kind.
 template <typename E, int D, int NS, int C0, int C1, int MODE>
-__global__ __launch_bounds__(kDqThreads) void bwd_dq_b16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(dq_threads<D>()) void bwd_dq_b16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
-  const PairItem item = load_uniform(&a.dq_pairs[blockIdx.x]);
+  // four-wave workgroups: the two of a pair are 8 ids apart, on the same XCD
+  const unsigned idx = dq_threads<D>() == kDqThreads ? blockIdx.x : ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
+  const PairItem item = load_uniform(&a.dq_pairs[idx]);
   if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
     bwd_dq_b16_body<E, D, NS, C0, MODE>(a, item, ring);
@@ -1007,7 +1016,7 @@ hipError_t launch_bwd_delta(const BwdArgs& a, int n_items, hipStream_t stream) {
     timing_begin(KID_DELTA, stream);
     const hipError_t err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
       hipLaunchKernelGGL((bwd_dq_b16_kernel<TE, D, kDqStages, decltype(c0)::value, decltype(c1)::value, DQ_DELTA>),
-                         dim3(n_items), dim3(kDqThreads), 0, stream, a);
+                         dim3(n_items * (kDqThreads / dq_threads<D>())), dim3(dq_threads<D>()), 0, stream, a);
       return hipGetLastError();
     });
     timing_end(KID_DELTA, stream);
@@ -1036,7 +1045,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int n_dq, hipStream_t stream) {
     if constexpr (Is16<TE>::value) {
       err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
         hipLaunchKernelGGL((bwd_dq_b16_kernel<TE, D, kDqStages, decltype(c0)::value, decltype(c1)::value, DQ_MAIN>),
-                           dim3(n_dq), dim3(kDqThreads), 0, stream, a);
+                           dim3(n_dq * (kDqThreads / dq_threads<D>())), dim3(dq_threads<D>()), 0, stream, a);
         return hipGetLastError();
       });
     } else {
