@@ -432,6 +432,8 @@ GUARD_CASES = [
     # (pattern, dtype, D, T, l, c): ragged T; a strided T whose classes straddle 64-blocks;
     # a merged head; fp32
     (inputs.STRIDED, "bf16", 64, 395, 33, 0),
+    (inputs.STRIDED, "bf16", 32, 395, 33, 0),
+    (inputs.FIXED, "bf16", 128, 1000, 96, 8),
     (inputs.FIXED, "bf16", 64, 1000, 96, 8),
     (inputs.FIXED, "f16", 32, 300, 20, 3),
     (inputs.DENSE, "bf16", 128, 200, 16, 0),

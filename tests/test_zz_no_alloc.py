@@ -33,6 +33,8 @@ def test_noalloc_matches_allocating_backward_twice_then_smaller():
     # merged heads and the fp32 path at a small size
     _case(inputs.STRIDED_UNION, 1, 2, 300, 64, 20, 0, torch.bfloat16, 7)
     _case(inputs.STRIDED, 1, 2, 256, 32, 16, 0, torch.float32, 8)
+    # D = 128 (four-wave dq workgroups) with split key columns
+    _case(inputs.FIXED, 1, 4, 4096, 128, 64, 8, torch.float16, 10)
 
 
 def test_noalloc_refuses_what_it_cannot_hold():
