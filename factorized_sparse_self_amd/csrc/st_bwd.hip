@@ -662,14 +662,25 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
           }
         }
     }
-    if (a.out_mode == OUT_FINAL) {
+    if (a.out_mode != OUT_CARRY) {
       // whole-line dq rows through LDS (free once every wave is past its last
-      // block), non-temporal
+      // block), non-temporal; a merged head's second pass adds the carried rows
       using Rows = RowStage<E, D, 16>;
       static_assert(NW * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
+      f32x4 y[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) y[d] = acc[d] * a.scale;
+      if (a.out_mode == OUT_MERGE && t >= 0) {
+        const float* c = a.carry_dq + ((size_t)bh * a.T + t) * D + 4 * lg;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const float4 cv = *(const float4*)(c + 16 * d);
+          y[d] += (f32x4){cv.x, cv.y, cv.z, cv.w};
+        }
+      }
       __syncthreads();
       Rows rows(&ring[0][0][0] + wave * Rows::BYTES);
-      rows.template put<ND>(0, li, lg, acc, a.scale);
+      rows.template put<ND>(0, li, lg, y, 1.f);
 #pragma unroll
       for (int j = 0; j < Rows::ROUNDS; ++j) {
         const int tr = block_position(g, false, qb, sub * 16 + rows.row_of(lane, j));
@@ -908,16 +919,33 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
 
-  if (item.slot < 0 && a.out_mode == OUT_FINAL) {
+  if (item.slot < 0 && a.out_mode != OUT_CARRY) {
     // whole-line dk and dv rows through LDS (free once every wave is past its
-    // last block), non-temporal
+    // last block), non-temporal; a merged head's second pass adds the carried
+    // rows (every key it holds was carried by the first pass)
     using Rows = RowStage<E, D, 16>;
     static_assert(4 * 2 * Rows::BYTES <= NS * sizeof(Stage), "row staging fits the ring");
+    f32x4 yk[ND], yv[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      yk[d] = dk[d] * a.scale;
+      yv[d] = dv[d];
+    }
+    if (a.out_mode == OUT_MERGE && kp >= 0) {
+      const size_t off = ((size_t)bh * a.T + kp) * D + 4 * lg;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const float4 ck = *(const float4*)(a.carry_dk + off + 16 * d);
+        const float4 cv = *(const float4*)(a.carry_dv + off + 16 * d);
+        yk[d] += (f32x4){ck.x, ck.y, ck.z, ck.w};
+        yv[d] += (f32x4){cv.x, cv.y, cv.z, cv.w};
+      }
+    }
     __syncthreads();
     unsigned char* wbuf = (unsigned char*)(void*)ring + wave * 2 * Rows::BYTES;
     Rows rk(wbuf), rv(wbuf + Rows::BYTES);
-    rk.template put<ND>(0, li, lg, dk, a.scale);
-    rv.template put<ND>(0, li, lg, dv, 1.f);
+    rk.template put<ND>(0, li, lg, yk, 1.f);
+    rv.template put<ND>(0, li, lg, yv, 1.f);
 #pragma unroll
     for (int j = 0; j < Rows::ROUNDS; ++j) {
       const int kr = block_position(g, true, kb, wave * 16 + rk.row_of(lane, j));

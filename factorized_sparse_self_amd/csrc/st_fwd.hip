@@ -243,7 +243,6 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
                                               unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
   typedef typename Vec<E>::x8 V8;
-  typedef typename Vec<E>::x4 V4;
   constexpr int NQ = D / 32;           // MFMA k-steps over D
   constexpr int ND = D / 16;           // 16-wide output column blocks
   constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
@@ -421,9 +420,12 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
 
-  if (!M || a.out_mode == OUT_FINAL) {
+  if (!M || a.out_mode != OUT_CARRY) {
     // whole-line output rows through LDS (free once every wave is past its
-    // last block); ordinary stores, since the backward reads O again
+    // last block); ordinary stores, since the backward reads O again.  The
+    // second pass of a merged head first combines its rows with the carried
+    // ones: softmax over both key sets, weights exp2(L_p - L) of the two
+    // passes' outputs, L = log2(2^L0 + 2^L1) (a pass with no keys has L_p = -inf)
     using Rows = RowStage<E, D, 32>;
     static_assert(4 * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
     __syncthreads();
@@ -433,9 +435,36 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
       const float lsum = group4_sum(l_run[G]);
       // the output is rounded to 16 bits, so the hardware reciprocal (1 ulp) suffices
       const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
-      rows.template put<ND>(G, li, lg, acc[G], inv);
-      if (t[G] >= 0 && lg == 0)
-        a.lse[(size_t)bh * a.T + t[G]] = (lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY) * kLn2;
+      const float lse2 = lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
+      bool merged = false;
+      if constexpr (M) merged = a.out_mode == OUT_MERGE;
+      if (merged) {
+        f32x4 y[ND];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) y[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (t[G] >= 0) {
+          const size_t row = (size_t)bh * a.T + t[G];
+          const float lse0 = a.carry_lse[row];
+          const float mx = fmaxf(lse0, lse2);
+          const float w0 = mx == -INFINITY ? 0.f : fast_exp2(lse0 - mx);
+          const float w1 = mx == -INFINITY ? 0.f : fast_exp2(lse2 - mx);
+          const float sw = w0 + w1;
+          const float isw = sw > 0.f ? __builtin_amdgcn_rcpf(sw) : 0.f;
+          const float s0 = w0 * isw, s1 = w1 * inv * isw;
+          const float* C = a.carry_o + row * D;
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const float4 c = *(const float4*)(C + 16 * d + 4 * lg);
+            const f32x4 c4 = {c.x, c.y, c.z, c.w};
+            y[d] = c4 * s0 + acc[G][d] * s1;
+          }
+          if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
+        }
+        rows.template put<ND>(G, li, lg, y, 1.f);
+      } else {
+        rows.template put<ND>(G, li, lg, acc[G], inv);
+        if (t[G] >= 0 && lg == 0) a.lse[(size_t)bh * a.T + t[G]] = lse2 * kLn2;
+      }
     }
 #pragma unroll
     for (int j = 0; j < Rows::ROUNDS; ++j) {
@@ -446,46 +475,21 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
     return;
   }
 
-  // merged heads: the first pass carries fp32 rows, the second merges them
+  // first pass of a merged head: keep the normalised fp32 output and lse
 #pragma unroll
   for (int G = 0; G < 2; ++G) {
     const float lsum = group4_sum(l_run[G]);
     if (t[G] < 0) continue;
-    // the output is rounded to 16 bits, so the hardware reciprocal (1 ulp) suffices
     const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
     const float lse2 = lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
     const size_t row = (size_t)bh * a.T + t[G];
-    if (M && a.out_mode == OUT_CARRY) {
-      // first pass of a merged head: keep the normalised fp32 output and lse
-      float* C = a.carry_o + row * D;
+    float* C = a.carry_o + row * D;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const f32x4 o = acc[G][d] * inv;
-        *(float4*)(C + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-      if (lg == 0) a.carry_lse[row] = lse2;
-      continue;
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 o = acc[G][d] * inv;
+      *(float4*)(C + 16 * d + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
     }
-    E* O = (E*)a.o + base + (size_t)t[G] * D;
-    if (M && a.out_mode == OUT_MERGE) {
-      // softmax over both key sets: weights exp2(L_p - L) of the two passes'
-      // outputs, L = log2(2^L0 + 2^L1) (a pass with no keys has L_p = -inf)
-      const float lse0 = a.carry_lse[row];
-      const float mx = fmaxf(lse0, lse2);
-      const float w0 = mx == -INFINITY ? 0.f : fast_exp2(lse0 - mx);
-      const float w1 = mx == -INFINITY ? 0.f : fast_exp2(lse2 - mx);
-      const float sw = w0 + w1;
-      const float isw = sw > 0.f ? __builtin_amdgcn_rcpf(sw) : 0.f;
-      const float s0 = w0 * isw, s1 = w1 * inv * isw;
-      const float* C = a.carry_o + row * D;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const float4 c = *(const float4*)(C + 16 * d + 4 * lg);
-        const f32x4 c4 = {c.x, c.y, c.z, c.w};
-        *(V4*)(O + 16 * d + 4 * lg) = to_x4<E>(c4 * s0 + acc[G][d] * s1);
-      }
-      if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
-    }
+    if (lg == 0) a.carry_lse[row] = lse2;
   }
 }
 
