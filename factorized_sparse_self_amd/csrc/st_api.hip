@@ -250,6 +250,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
   for (int kind = 0; kind < 2; ++kind) {
     row_flags[kind].assign(key.T, 0);
     for (int t = 0; t < key.T; ++t) {
+      if (!position_is_key(lay.kind[kind].geo, t)) row_flags[kind][t] = ROW_NOKEY;
       const int n = merged ? n_keys[0][t] + n_keys[1][t] : n_keys[kind][t];
       if (n == 0 || n > kDqLoKeys) continue;
       uint8_t f = ROW_LO;
@@ -257,7 +258,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
         f |= ROW_INBLOCK;
       else
         f |= ROW_PRE;
-      row_flags[kind][t] = f;
+      row_flags[kind][t] |= f;
     }
   }
   // kPairLo / kPairPre of the pair of row blocks (2pb, 2pb+1) of a kind: rows

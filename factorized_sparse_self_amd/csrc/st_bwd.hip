@@ -656,7 +656,8 @@ __device__ __forceinline__ void bwd_dq_b16_body(const BwdArgs& a, const PairItem
         for (int u = tid & 255; u < kBlock * CH; u += 256) {
           const int r = u / CH, ch = u % CH;
           const int tp = block_position(g, false, qb, r);
-          if (tp >= 0 && !position_is_key(g, tp)) {
+          // (an explicit summary set: one byte per position instead of a search of the set)
+          if (tp >= 0 && (g.sigma ? (kd.row_flags[tp] & ROW_NOKEY) != 0 : !position_is_key(g, tp))) {
             store_zero16_nt((E*)a.dk + base + (size_t)tp * D + ch * 8);
             store_zero16_nt((E*)a.dv + base + (size_t)tp * D + ch * 8);
           }

@@ -74,8 +74,11 @@ constexpr int kPairLo = 1, kPairPre = 2;
 // so the dq pass gives them an exact Delta and dS as hi + lo.  ROW_INBLOCK:
 // the row's keys lie in one 64-key block, so the dq pass computes its exact
 // Delta inside that block; ROW_PRE: the delta pre-pass computes it.
+// ROW_NOKEY: the position is no key of the kind (nobody attends it, so its dk
+// and dv are zero); the dq pass of a summary kind with an explicit summary set
+// reads it instead of searching the set.
 constexpr int kDqLoKeys = 32;
-enum RowFlag : uint8_t { ROW_LO = 1, ROW_INBLOCK = 2, ROW_PRE = 4 };
+enum RowFlag : uint8_t { ROW_LO = 1, ROW_INBLOCK = 2, ROW_PRE = 4, ROW_NOKEY = 8 };
 
 // Reduction of a split key block: partial slots [slot0, slot0 + nsplit).
 struct ReduceItem {
