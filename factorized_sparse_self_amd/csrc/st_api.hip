@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -33,6 +34,11 @@ namespace {
 constexpr int kDkdvSplit = 24;
 constexpr int64_t kDkdvSlots = 2048;
 
+// Keys per wave of the 16-bit dK/dV kernel: 0 = by launch (32 for launches
+// whose items far outnumber the GPU's slots, 16 otherwise), or 16 / 32 for
+// every launch (st_set_dkdv_keys_per_wave).
+std::atomic<int> g_dkdv_keys_per_wave{0};
+
 struct PlanKey {
   int device, pattern, T, l, c, B, H;
   std::vector<int32_t> summary;  // canonical summary set (empty: the last c offsets)
@@ -52,6 +58,7 @@ struct PassItems {
   DkdvItem* dkdv_items = nullptr;
   ReduceItem* red_items = nullptr;
   int n_row_items = 0, n_pair_items = 0, n_pre_items = 0, n_dkdv_items = 0, n_red_items = 0;
+  bool dkdv_long = false;  // dK/dV items far outnumber the GPU's slots (no key block split)
 };
 
 struct Plan {
@@ -287,6 +294,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
     std::vector<PairItem> pairs, pre;
     std::vector<DkdvItem> dkdv;
     std::vector<ReduceItem> red;
+    bool dkdv_long = false;
   } hp[2];
   int max_slots = 0;
   for (int p = 0; p < n_pass; ++p) {
@@ -347,6 +355,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
     const int64_t avg = (dwork + kDkdvSlots - 1) / kDkdvSlots;
     const int64_t avg_up = (avg + kDkdvSplit - 1) / kDkdvSplit * kDkdvSplit;  // a multiple of kDkdvSplit
     const int split = (int)std::min<int64_t>(std::max<int64_t>(kDkdvSplit, avg_up), 1 << 30);
+    hp[p].dkdv_long = split > kDkdvSplit;
     std::vector<DkdvItem> dkdv;
     std::vector<int64_t> dcost, dgroup;
     int slots = 0;
@@ -453,6 +462,7 @@ int build_plan(const PlanKey& key, Plan* plan) {
     P.n_pre_items = (int)hp[p].pre.size();
     P.n_dkdv_items = (int)hp[p].dkdv.size();
     P.n_red_items = (int)hp[p].red.size();
+    P.dkdv_long = hp[p].dkdv_long;
   }
   plan->n_slots = max_slots;
   return ST_OK;
@@ -765,12 +775,14 @@ int attn_bwd(const char* fn, const void* q, const void* k, const void* v, const 
                   : launch_bwd_dq<TE, 128>(a, n_dq, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
+  const int kpw_set = g_dkdv_keys_per_wave.load(std::memory_order_relaxed);
   for (int p = 0; p < plan->n_pass; ++p) {
     set_pass(p);
     const PassItems& P = plan->pass[p];
-    e = D == 32 ? launch_bwd_dkdv<TE, 32>(a, P.n_dkdv_items, P.n_red_items, s)
-        : D == 64 ? launch_bwd_dkdv<TE, 64>(a, P.n_dkdv_items, P.n_red_items, s)
-                  : launch_bwd_dkdv<TE, 128>(a, P.n_dkdv_items, P.n_red_items, s);
+    const int kpw = kpw_set ? kpw_set : P.dkdv_long ? 32 : 16;
+    e = D == 32 ? launch_bwd_dkdv<TE, 32>(a, P.n_dkdv_items, P.n_red_items, kpw, s)
+        : D == 64 ? launch_bwd_dkdv<TE, 64>(a, P.n_dkdv_items, P.n_red_items, kpw, s)
+                  : launch_bwd_dkdv<TE, 128>(a, P.n_dkdv_items, P.n_red_items, kpw, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   return static_ws ? ST_OK : workspace_done(device, s);
@@ -931,6 +943,15 @@ int st_sparse_attn_bwd_noalloc(int dtype, const void* q, const void* k, const vo
                              true);
     default: set_error(std::string(fn) + ": unknown dtype " + std::to_string(dtype)); return ST_ERR_INVALID;
   }
+}
+
+int st_set_dkdv_keys_per_wave(int keys) {
+  if (keys != 0 && keys != 16 && keys != 32) {
+    set_error("st_set_dkdv_keys_per_wave: keys must be 0, 16 or 32, got " + std::to_string(keys));
+    return ST_ERR_INVALID;
+  }
+  g_dkdv_keys_per_wave.store(keys, std::memory_order_relaxed);
+  return ST_OK;
 }
 
 int st_timing_enable(int on) {

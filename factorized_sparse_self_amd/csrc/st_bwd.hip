@@ -714,23 +714,33 @@ __global__ __launch_bounds__(dq_threads<D>()) void bwd_dq_b16_kernel(BwdArgs a) 
 // dk/dv: Q and dO blocks with their lse*log2(e) and Delta are staged by
 // direct global->LDS loads into a ring of NS stages (st_stage.hpp), so the
 // loads of NS-1 row blocks are in flight while one is computed; each row's
-// key run (for masks) is computed and stored next to them.
-template <int D>
+// key run (for masks) is computed and stored next to them.  A workgroup holds
+// one 64-key block; each of its 4/KT waves holds 16*KT keys.  With KT = 2 a
+// wave reads every Q and dO operand from LDS once for two 16-key tiles, which
+// halves the LDS reads per key against KT = 1, at twice the accumulators and
+// half the waves.  That pays where items are long and the CUs stay full
+// (launches with many more items than the GPU holds); where short items and
+// latency set the time, KT = 1's four waves do better.  The launcher picks.
+template <int D, int KT>
 struct DkdvStage {
   unsigned char q[TileShape<D>::BYTES];
   unsigned char g[TileShape<D>::BYTES];
-  float vals[4 * 64];   // wave w's 16 rows at [64 w, 64 w + 32): lse*log2(e) of each, then -Delta
+  // 16-row sub-block b at [VS b, VS b + 32): lse*log2(e) of each row, then
+  // -Delta; VS = 64 / KT (with KT = 1 the second half of each slot is unused)
+  float vals[4 * 64 / KT];
   int lo[kBlock];       // masking base of each row
   int span[kBlock];     // masking span (unsigned)
 };
 
-template <typename E, int D, int NS, int KC>
-__device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvItem& item, DkdvStage<D>* ring) {
+template <typename E, int D, int NS, int KC, int KT>
+__device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvItem& item, DkdvStage<D, KT>* ring) {
   using S = TileShape<D>;
   typedef typename Vec<E>::x8 V8;
   constexpr int NQ = D / 32, ND = D / 16;
-  constexpr int PER_TILE = 2 * S::NI + 1;  // loads per wave per row block: Q, dO, and lse2 with Delta
-  using Stage = DkdvStage<D>;
+  constexpr int WR = 16 * KT;                   // rows staged, and keys held, per wave
+  constexpr int VS = 64 / KT;                   // row-value slot stride of a 16-row sub-block
+  constexpr int PER_TILE = 2 * KT * S::NI + 1;  // loads per wave per row block: Q, dO, and lse2 with Delta
+  using Stage = DkdvStage<D, KT>;
   const int kb = item.kb, bh = item.bh;
   const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const GeoC<KC> g{kd.geo};
@@ -744,36 +754,47 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const int Kw0 = kb * kBlock + wave * 16;
-  const int Kl = Kw0 + li;
-  const int kp = block_position(g, true, kb, wave * 16 + li);
-  V8 kop[NQ], vop[NQ];  // this wave's 16 keys as MFMA B operands (from LDS, first block)
+  int Kl[KT], kp[KT];  // kernel key and position of this lane's key in each 16-key tile
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    Kl[kt] = kb * kBlock + wave * WR + 16 * kt + li;
+    kp[kt] = block_position(g, true, kb, wave * WR + 16 * kt + li);
+  }
+  V8 kop[KT][NQ], vop[KT][NQ];  // this wave's keys as MFMA B operands (from LDS, first block)
   int a_off[NQ], t_off[ND];
 #pragma unroll
   for (int k = 0; k < NQ; ++k) a_off[k] = S::phys(li, 4 * k + lg);
 #pragma unroll
   for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
-  f32x4 dk[ND], dv[ND];
+  f32x4 dk[KT][ND], dv[KT][ND];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) dk[d] = dv[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dk[kt][d] = dv[kt][d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
 
-  const StageRows<S::NI, S::RPI> stage(g, false, 16 * wave + lane / S::CH);
-  const StageRows<1, kBlock> stage_own(g, false, 16 * wave + li);  // this lane's row, lanes 0..15
+  // The row whose values (and key run) this lane fetches: lanes 32 h + i and
+  // 32 h + 16 + i both take row i of the wave's sub-block h (the first its
+  // lse*log2(e), the second its -Delta); with KT = 1 lanes 32..63 repeat 0..31.
+  const int vh = (lane >> 5) % KT;
+  const bool vlane = (lane >> 5) < KT;
+  const int vrow = WR * wave + 16 * vh + li;
+  const StageRows<KT * S::NI, S::RPI> stage(g, false, WR * wave + lane / S::CH);
+  const StageRows<1, kBlock> stage_own(g, false, vrow);
   const cptr<uint32_t> entries = as_const(kd.csc_entry);
-  // LDS addresses, in stage 0, of this wave's 16 Q rows (dO follows at
-  // +BYTES) and of its row values; stage s at +s*sizeof(Stage)
+  // LDS addresses, in stage 0, of this wave's Q rows (dO follows at +BYTES)
+  // and of its row values; stage s at +s*sizeof(Stage)
   static_assert(offsetof(Stage, g) - offsetof(Stage, q) == S::BYTES, "stage layout");
-  const uint32_t lds_rows = lds_address(&ring[0].q[16 * wave * S::RB]);
-  const uint32_t lds_vals = lds_address(&ring[0].vals[64 * wave]);
+  const uint32_t lds_rows = lds_address(&ring[0].q[WR * wave * S::RB]);
+  const uint32_t lds_vals = lds_address(&ring[0].vals[VS * KT * wave]);
   auto issue = [&](int e, int stg) {
     const uint32_t ent = entries[e];
     const int qb = (int)(ent & ~kFullBit);
     const uint32_t so = stg * (uint32_t)sizeof(Stage);
-    int p[S::NI];
+    int p[KT * S::NI];
     stage.positions(g, false, qb, p);
-    stage_rows<D>(rq, lds_rows + so, 16 * wave, lane, p);
-    stage_rows<D>(rg, lds_rows + so + S::BYTES, 16 * wave, lane, p);
+    stage_rows<D>(rq, lds_rows + so, WR * wave, lane, p);
+    stage_rows<D>(rg, lds_rows + so + S::BYTES, WR * wave, lane, p);
     int tp[1];
     stage_own.positions(g, false, qb, tp);
     // a FULL block's rows are all real and attend every key of the block: no
@@ -781,29 +802,27 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     bool live = true;
     if (!(ent & kFullBit)) {
       int lo = 1, hi = 0;
-      if (tp[0] >= 0) row_interval(g, qb * kBlock + 16 * wave + li, tp[0], lo, hi);
+      if (tp[0] >= 0) row_interval(g, qb * kBlock + vrow, tp[0], lo, hi);
       live = lo <= hi;
-      if (lane < 16) {
-        ring[stg].lo[16 * wave + lane] = live ? lo : -(1 << 30);
-        ring[stg].span[16 * wave + lane] = live ? hi - lo : 0;
+      if (vlane && !(lane & 16)) {
+        ring[stg].lo[vrow] = live ? lo : -(1 << 30);
+        ring[stg].span[vrow] = live ? hi - lo : 0;
       }
     }
-    // one load for both values: lanes 0-15 fetch lse*log2(e) of row li,
-    // lanes 16-31 its -Delta (the pair is adjacent in the workspace), the
-    // other lanes write zeros
-    lds_dma<4>(rvals, lds_vals + so,
-               (lane < 32 && live) ? (uint32_t)tp[0] * 8 + (lane >= 16 ? 4u : 0u) : kOutOfRange);
+    // one load for both values (adjacent in the workspace); lanes without a
+    // row write zeros
+    lds_dma<4>(rvals, lds_vals + so, (vlane && live) ? (uint32_t)tp[0] * 8 + ((lane & 16) ? 4u : 0u) : kOutOfRange);
   };
 
   // The key block's K and V rows go through the last ring stage (free until
   // the first iteration refills it), ahead of the first NS-1 row blocks, so
   // every global load of the kernel is a ring DMA.
   if (item.e0 < item.e1) {
-    const StageRows<S::NI, S::RPI> kstage(g, true, 16 * wave + lane / S::CH);
-    int p[S::NI];
+    const StageRows<KT * S::NI, S::RPI> kstage(g, true, WR * wave + lane / S::CH);
+    int p[KT * S::NI];
     kstage.positions(g, true, kb, p);
-    stage_rows<D>(rk, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage), 16 * wave, lane, p);
-    stage_rows<D>(rv, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage) + S::BYTES, 16 * wave, lane, p);
+    stage_rows<D>(rk, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage), WR * wave, lane, p);
+    stage_rows<D>(rv, lds_rows + (NS - 1) * (uint32_t)sizeof(Stage) + S::BYTES, WR * wave, lane, p);
   }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
@@ -816,46 +835,61 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     wait_tiles_left<PER_TILE, NS - 2>(imin(NS - 2, item.e1 - 1 - e));
     __syncthreads();
     if (e == item.e0) {
-      // this wave's 16 K/V rows (its own DMA, complete with the first block)
+      // this wave's K/V rows (its own DMA, complete with the first block)
 #pragma unroll
-      for (int k = 0; k < NQ; ++k) {
-        kop[k] = *(const V8*)(ring[NS - 1].q + 16 * wave * S::RB + a_off[k]);
-        vop[k] = *(const V8*)(ring[NS - 1].g + 16 * wave * S::RB + a_off[k]);
-      }
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+          kop[kt][k] = *(const V8*)(ring[NS - 1].q + (WR * wave + 16 * kt) * S::RB + a_off[k]);
+          vop[kt][k] = *(const V8*)(ring[NS - 1].g + (WR * wave + 16 * kt) * S::RB + a_off[k]);
+        }
       // the reads must land before the DMA below refills that stage
       wait_lgkmcnt0();
     }
     if (e + NS - 1 < item.e1) issue(e + NS - 1, stg == 0 ? NS - 1 : stg - 1);
     const Stage& st = ring[stg];
     // The block's 64 rows as NG groups of 16-row sub-blocks: one group with
-    // P and dS in the input type; two with their low parts too, so that the
-    // extra operands fit the same registers.
-    constexpr int NG = LO ? 2 : 1, NB = 4 / NG;
+    // P and dS in the input type; two with their low parts too, or with two
+    // key tiles, so that the operands fit the registers.
+    constexpr int NG = (LO || KT > 1) ? 2 : 1, NB = 4 / NG;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       // S = Q K^T, and dP - Delta = dO V^T - Delta with the accumulators
-      // starting at -Delta of rows 16b + 4lg + i
-      f32x4 sc[NB], dp[NB];
+      // starting at -Delta of rows 16b + 4lg + i; each Q and dO operand read
+      // serves every key tile
+      f32x4 sc[KT][NB], dp[KT][NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int b = gi * NB + j;
-        sc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        dp[j] = *(const f32x4*)(&st.vals[64 * b + 16 + 4 * lg]);
+        const f32x4 nd = *(const f32x4*)(&st.vals[VS * b + 16 + 4 * lg]);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          sc[kt][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          dp[kt][j] = nd;
+        }
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
-          sc[j] = mfma16(*(const V8*)(st.q + 16 * b * S::RB + a_off[k]), kop[k], sc[j]);
-          dp[j] = mfma16(*(const V8*)(st.g + 16 * b * S::RB + a_off[k]), vop[k], dp[j]);
+          const V8 qa = *(const V8*)(st.q + 16 * b * S::RB + a_off[k]);
+          const V8 ga = *(const V8*)(st.g + 16 * b * S::RB + a_off[k]);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            sc[kt][j] = mfma16(qa, kop[kt][k], sc[kt][j]);
+            dp[kt][j] = mfma16(ga, vop[kt][k], dp[kt][j]);
+          }
         }
       }
       // rows 16b + 4lg + i of this lane's values
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int b = gi * NB + j;
-        const float4 l2 = *(const float4*)(&st.vals[64 * b + 4 * lg]);
-        sc[j][0] = fast_exp2(fmaf(sc[j][0], sl2, -l2.x));
-        sc[j][1] = fast_exp2(fmaf(sc[j][1], sl2, -l2.y));
-        sc[j][2] = fast_exp2(fmaf(sc[j][2], sl2, -l2.z));
-        sc[j][3] = fast_exp2(fmaf(sc[j][3], sl2, -l2.w));
+        const float4 l2 = *(const float4*)(&st.vals[VS * b + 4 * lg]);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          sc[kt][j][0] = fast_exp2(fmaf(sc[kt][j][0], sl2, -l2.x));
+          sc[kt][j][1] = fast_exp2(fmaf(sc[kt][j][1], sl2, -l2.y));
+          sc[kt][j][2] = fast_exp2(fmaf(sc[kt][j][2], sl2, -l2.z));
+          sc[kt][j][3] = fast_exp2(fmaf(sc[kt][j][3], sl2, -l2.w));
+        }
       }
       if (!full) {
 #pragma unroll
@@ -863,31 +897,39 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
           const int b = gi * NB + j;
           const int4 lo4 = *(const int4*)(&st.lo[16 * b + 4 * lg]);
           const int4 sp4 = *(const int4*)(&st.span[16 * b + 4 * lg]);
-          if ((uint32_t)(Kl - lo4.x) > (uint32_t)sp4.x) sc[j][0] = 0.f;
-          if ((uint32_t)(Kl - lo4.y) > (uint32_t)sp4.y) sc[j][1] = 0.f;
-          if ((uint32_t)(Kl - lo4.z) > (uint32_t)sp4.z) sc[j][2] = 0.f;
-          if ((uint32_t)(Kl - lo4.w) > (uint32_t)sp4.w) sc[j][3] = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            if ((uint32_t)(Kl[kt] - lo4.x) > (uint32_t)sp4.x) sc[kt][j][0] = 0.f;
+            if ((uint32_t)(Kl[kt] - lo4.y) > (uint32_t)sp4.y) sc[kt][j][1] = 0.f;
+            if ((uint32_t)(Kl[kt] - lo4.z) > (uint32_t)sp4.z) sc[kt][j][2] = 0.f;
+            if ((uint32_t)(Kl[kt] - lo4.w) > (uint32_t)sp4.w) sc[kt][j][3] = 0.f;
+          }
         }
       }
 #pragma unroll
-      for (int j = 0; j < NB; ++j) dp[j] *= sc[j];
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) dp[kt][j] *= sc[kt][j];
 #pragma unroll
       for (int jj = 0; jj < NB / 2; ++jj) {
         const int kk = gi * (NB / 2) + jj;  // 32-row step
-        const V8 p8 = pack_b_operand<E>(sc[2 * jj], sc[2 * jj + 1]);
-        const V8 ds8 = pack_b_operand<E>(dp[2 * jj], dp[2 * jj + 1]);
-        V8 p8lo{}, ds8lo{};
-        if constexpr (LO) {
-          f32x4 r0, r1, u0, u1;
+        V8 p8[KT], ds8[KT], p8lo[KT], ds8lo[KT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            r0[i] = sc[2 * jj][i] - (float)p8[i];
-            r1[i] = sc[2 * jj + 1][i] - (float)p8[4 + i];
-            u0[i] = dp[2 * jj][i] - (float)ds8[i];
-            u1[i] = dp[2 * jj + 1][i] - (float)ds8[4 + i];
+        for (int kt = 0; kt < KT; ++kt) {
+          p8[kt] = pack_b_operand<E>(sc[kt][2 * jj], sc[kt][2 * jj + 1]);
+          ds8[kt] = pack_b_operand<E>(dp[kt][2 * jj], dp[kt][2 * jj + 1]);
+          if constexpr (LO) {
+            f32x4 r0, r1, u0, u1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              r0[i] = sc[kt][2 * jj][i] - (float)p8[kt][i];
+              r1[i] = sc[kt][2 * jj + 1][i] - (float)p8[kt][4 + i];
+              u0[i] = dp[kt][2 * jj][i] - (float)ds8[kt][i];
+              u1[i] = dp[kt][2 * jj + 1][i] - (float)ds8[kt][4 + i];
+            }
+            p8lo[kt] = pack_b_operand<E>(r0, r1);
+            ds8lo[kt] = pack_b_operand<E>(u0, u1);
           }
-          p8lo = pack_b_operand<E>(r0, r1);
-          ds8lo = pack_b_operand<E>(u0, u1);
         }
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
@@ -895,10 +937,13 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
           const unsigned char* rq0 = st.q + 32 * kk * S::RB + t_off[d];
           const V8 ag = concat(lds_read_tr<E>((const E*)rg0), lds_read_tr<E>((const E*)(rg0 + 16 * S::RB)));
           const V8 aq = concat(lds_read_tr<E>((const E*)rq0), lds_read_tr<E>((const E*)(rq0 + 16 * S::RB)));
-          dv[d] = mfma16(ag, p8, dv[d]);
-          if constexpr (LO) dv[d] = mfma16(ag, p8lo, dv[d]);
-          dk[d] = mfma16(aq, ds8, dk[d]);
-          if constexpr (LO) dk[d] = mfma16(aq, ds8lo, dk[d]);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            dv[kt][d] = mfma16(ag, p8[kt], dv[kt][d]);
+            if constexpr (LO) dv[kt][d] = mfma16(ag, p8lo[kt], dv[kt][d]);
+            dk[kt][d] = mfma16(aq, ds8[kt], dk[kt][d]);
+            if constexpr (LO) dk[kt][d] = mfma16(aq, ds8lo[kt], dk[kt][d]);
+          }
         }
       }
     }
@@ -924,32 +969,41 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     // whole-line dk and dv rows through LDS (free once every wave is past its
     // last block), non-temporal; a merged head's second pass adds the carried
     // rows (every key it holds was carried by the first pass)
-    using Rows = RowStage<E, D, 16>;
-    static_assert(4 * 2 * Rows::BYTES <= NS * sizeof(Stage), "row staging fits the ring");
-    f32x4 yk[ND], yv[ND];
+    using Rows = RowStage<E, D, WR>;
+    static_assert((4 / KT) * 2 * Rows::BYTES <= NS * sizeof(Stage), "row staging fits the ring");
+    f32x4 yk[KT][ND], yv[KT][ND];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      yk[d] = dk[d] * a.scale;
-      yv[d] = dv[d];
-    }
-    if (a.out_mode == OUT_MERGE && kp >= 0) {
-      const size_t off = ((size_t)bh * a.T + kp) * D + 4 * lg;
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        const float4 ck = *(const float4*)(a.carry_dk + off + 16 * d);
-        const float4 cv = *(const float4*)(a.carry_dv + off + 16 * d);
-        yk[d] += (f32x4){ck.x, ck.y, ck.z, ck.w};
-        yv[d] += (f32x4){cv.x, cv.y, cv.z, cv.w};
+        yk[kt][d] = dk[kt][d] * a.scale;
+        yv[kt][d] = dv[kt][d];
+      }
+    if (a.out_mode == OUT_MERGE) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kp[kt] < 0) continue;
+        const size_t off = ((size_t)bh * a.T + kp[kt]) * D + 4 * lg;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const float4 ck = *(const float4*)(a.carry_dk + off + 16 * d);
+          const float4 cv = *(const float4*)(a.carry_dv + off + 16 * d);
+          yk[kt][d] += (f32x4){ck.x, ck.y, ck.z, ck.w};
+          yv[kt][d] += (f32x4){cv.x, cv.y, cv.z, cv.w};
+        }
       }
     }
     __syncthreads();
     unsigned char* wbuf = (unsigned char*)(void*)ring + wave * 2 * Rows::BYTES;
     Rows rk(wbuf), rv(wbuf + Rows::BYTES);
-    rk.template put<ND>(0, li, lg, yk, 1.f);
-    rv.template put<ND>(0, li, lg, yv, 1.f);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      rk.template put<ND>(kt, li, lg, yk[kt], 1.f);
+      rv.template put<ND>(kt, li, lg, yv[kt], 1.f);
+    }
 #pragma unroll
     for (int j = 0; j < Rows::ROUNDS; ++j) {
-      const int kr = block_position(g, true, kb, wave * 16 + rk.row_of(lane, j));
+      const int kr = block_position(g, true, kb, wave * WR + rk.row_of(lane, j));
       const u32x4 xk = rk.get(lane, j), xv = rv.get(lane, j);
       if (kr >= 0) {
         const size_t off = base + (size_t)kr * D + rk.col_of(lane, j);
@@ -960,35 +1014,42 @@ __device__ __forceinline__ void bwd_dkdv_b16_body(const BwdArgs& a, const DkdvIt
     return;
   }
   if (item.slot < 0) {
-    if (kp < 0) return;
-    const int mode = key_out_mode(a, kp);
-    const size_t off = ((size_t)bh * a.T + kp) * D + 4 * lg;
-    store_grad_row<ND>(mode, a.carry_dk + off, (E*)a.dk + off, dk, a.scale);
-    store_grad_row<ND>(mode, a.carry_dv + off, (E*)a.dv + off, dv, 1.f);
-  } else {
-    float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * 16 + li) * D;
-    float* pv = pk + kBlock * D;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      const f32x4 x = dk[d] * a.scale;
-      *(float4*)(pk + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
-      *(float4*)(pv + 16 * d + 4 * lg) = make_float4(dv[d][0], dv[d][1], dv[d][2], dv[d][3]);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kp[kt] < 0) continue;
+      const int mode = key_out_mode(a, kp[kt]);
+      const size_t off = ((size_t)bh * a.T + kp[kt]) * D + 4 * lg;
+      store_grad_row<ND>(mode, a.carry_dk + off, (E*)a.dk + off, dk[kt], a.scale);
+      store_grad_row<ND>(mode, a.carry_dv + off, (E*)a.dv + off, dv[kt], 1.f);
+    }
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      float* pk = a.partial + ((size_t)item.slot * 2) * kBlock * D + (wave * WR + 16 * kt + li) * D;
+      float* pv = pk + kBlock * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const f32x4 x = dk[kt][d] * a.scale;
+        *(float4*)(pk + 16 * d + 4 * lg) = make_float4(x[0], x[1], x[2], x[3]);
+        *(float4*)(pv + 16 * d + 4 * lg) = make_float4(dv[kt][d][0], dv[kt][d][1], dv[kt][d][2], dv[kt][d][3]);
+      }
     }
   }
 }
 
-// At least three waves per SIMD (at most 168 VGPRs), which beat two waves with
-// deeper prefetch; at D <= 64 the kernel needs about 120, so four fit.
-template <typename E, int D, int NS, int C0, int C1>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_dkdv_b16_kernel(
+// At least three waves per SIMD (at most 168 VGPRs) with one key tile per
+// wave (about 120 VGPRs at D <= 64, so four fit), two with two tiles (about
+// 200; the LDS ring allows four workgroups per CU either way).
+template <typename E, int D, int NS, int C0, int C1, int KT>
+__global__ __launch_bounds__(256 / KT) __attribute__((amdgpu_waves_per_eu(KT == 1 ? 3 : 2, 8))) void bwd_dkdv_b16_kernel(
     BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) DkdvStage<D> ring[NS];
+  __shared__ __attribute__((aligned(16))) DkdvStage<D, KT> ring[NS];
   const DkdvItem item = load_uniform(&a.dkdv_items[blockIdx.x]);
   if (item.kb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    bwd_dkdv_b16_body<E, D, NS, C0>(a, item, ring);
+    bwd_dkdv_b16_body<E, D, NS, C0, KT>(a, item, ring);
   else
-    bwd_dkdv_b16_body<E, D, NS, C1>(a, item, ring);
+    bwd_dkdv_b16_body<E, D, NS, C1, KT>(a, item, ring);
 }
 
 // ---------------------------------------------------------------------------
@@ -1088,14 +1149,22 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int n_dq, hipStream_t stream) {
 }
 
 template <typename TE, int D>
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, int keys_per_wave, hipStream_t stream) {
   hipError_t err = hipSuccess;
   if (n_dkdv > 0) {
     timing_begin(KID_DKDV, stream);
     if constexpr (Is16<TE>::value) {
       err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto) {
-        hipLaunchKernelGGL((bwd_dkdv_b16_kernel<TE, D, kDkdvStages, decltype(c0)::value, decltype(c1)::value>),
-                           dim3(n_dkdv), dim3(kThreads), 0, stream, a);
+        constexpr int C0 = decltype(c0)::value, C1 = decltype(c1)::value;
+        if constexpr (D <= 64) {
+          if (keys_per_wave == 32) {
+            hipLaunchKernelGGL((bwd_dkdv_b16_kernel<TE, D, kDkdvStages, C0, C1, 2>), dim3(n_dkdv), dim3(128), 0,
+                               stream, a);
+            return hipGetLastError();
+          }
+        }
+        hipLaunchKernelGGL((bwd_dkdv_b16_kernel<TE, D, kDkdvStages, C0, C1, 1>), dim3(n_dkdv), dim3(kThreads), 0,
+                           stream, a);
         return hipGetLastError();
       });
     } else {
@@ -1118,30 +1187,30 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, hipStream_t 
 
 template hipError_t launch_bwd_delta<bf16, 32>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<bf16, 32>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<bf16, 32>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<bf16, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<bf16, 64>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<bf16, 64>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<bf16, 64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<bf16, 64>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<bf16, 128>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<bf16, 128>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<bf16, 128>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<bf16, 128>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<f16, 32>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<f16, 32>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<f16, 32>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<f16, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<f16, 64>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<f16, 64>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<f16, 64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<f16, 64>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<f16, 128>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<f16, 128>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<f16, 128>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<f16, 128>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<float, 32>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<float, 32>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<float, 32>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<float, 32>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<float, 64>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<float, 64>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<float, 64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<float, 64>(const BwdArgs&, int, int, int, hipStream_t);
 template hipError_t launch_bwd_delta<float, 128>(const BwdArgs&, int, hipStream_t);
 template hipError_t launch_bwd_dq<float, 128>(const BwdArgs&, int, hipStream_t);
-template hipError_t launch_bwd_dkdv<float, 128>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_dkdv<float, 128>(const BwdArgs&, int, int, int, hipStream_t);
 
 }  // namespace st

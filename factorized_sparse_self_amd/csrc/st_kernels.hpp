@@ -148,7 +148,9 @@ template <typename TE, int D>
 hipError_t launch_bwd_delta(const BwdArgs& a, int n_items, hipStream_t stream);  // 16-bit only
 template <typename TE, int D>
 hipError_t launch_bwd_dq(const BwdArgs& a, int n_dq, hipStream_t stream);
+// keys_per_wave: 32 selects the two-tile dk/dv kernel (16-bit inputs, D <= 64
+// only); any other value, and every other case, the one-tile kernel.
 template <typename TE, int D>
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int n_dkdv, int n_red, int keys_per_wave, hipStream_t stream);
 
 }  // namespace st

@@ -251,6 +251,20 @@ int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const vo
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Kernel shape (performance only; not part of the computation).  The 16-bit
+ * dK/dV kernel at D <= 64 comes in two shapes: 16 keys per wave (four waves
+ * per 64-key block) or 32 (two waves, each reading its Q and dO operands once
+ * for two 16-key tiles).  Both sum every product in the same order, so dq, dk
+ * and dv are bitwise identical under either.  keys = 0 (the default) picks
+ * per launch: 32 where the dK/dV items far outnumber what the GPU holds at
+ * once (full attention, very long sequences), 16 otherwise; 16 or 32 forces
+ * that shape for every later backward call in the process (fp32 inputs and
+ * D = 128 always use 16).  Other values give ST_ERR_INVALID.  Takes effect at
+ * the next call; calls already enqueued are unaffected.
+ * ------------------------------------------------------------------------- */
+int st_set_dkdv_keys_per_wave(int keys);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing (diagnostics; not part of the computation).  While enabled,
  * every kernel the library launches is bracketed by two HIP events recorded
  * on its launch stream.  st_timing_read() waits for those events and returns,

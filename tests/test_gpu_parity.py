@@ -428,6 +428,52 @@ def test_results_repeat_bit_for_bit(pattern):
         assert torch.equal(a.view(bits), o.view(bits)), f"{name}: call on another stream differs"
 
 
+DKDV_SHAPE_CASES = [
+    # (pattern, dtype, D, B, H, T, l, c): split summary columns (T > 24 row blocks), merged
+    # heads (carry and merge passes), residue classes straddling 64-blocks at D = 32, a
+    # general summary set, full attention; D = 128 and fp32 always take 16 keys per wave
+    (inputs.FIXED, "bf16", 64, 1, 2, 3000, 64, 4),
+    (inputs.FIXED_UNION, "bf16", 64, 1, 2, 2500, 100, 5),
+    (inputs.FIXED_R1, "f16", 32, 2, 2, 2300, 50, 3),
+    (inputs.FIXED, "bf16", 64, 1, 3, 2200, 96, (0, 40, 95)),
+    (inputs.STRIDED, "bf16", 32, 1, 2, 395, 33, 0),
+    (inputs.STRIDED_UNION, "f16", 64, 2, 2, 700, 20, 0),
+    (inputs.DENSE, "bf16", 64, 1, 2, 1000, 16, 0),
+    (inputs.FIXED, "bf16", 128, 1, 2, 1000, 96, 8),
+    (inputs.FIXED, "f32", 64, 1, 2, 700, 32, 4),
+]
+
+
+@pytest.mark.parametrize("case", DKDV_SHAPE_CASES,
+                         ids=lambda c: f"{inputs.PATTERN_NAMES[c[0]]}_{c[1]}_D{c[2]}_T{c[5]}_l{c[6]}")
+def test_dkdv_kernel_shapes_agree_bit_for_bit(case):
+    """The dK/dV kernel's two shapes (16 or 32 keys per wave; the library picks 32 only
+    for long launches) sum the same products in the same order: forced either way, the
+    backward returns the same bits, and the 32-key result meets the oracle's bound."""
+    from factorized_sparse_self_amd import st_set_dkdv_keys_per_wave, st_sparse_attn_bwd
+    pattern, dtype, D, B, H, T, l, c = case
+    log(f"dkdv shapes {case}")
+    q, k, v, do = (x.cuda() for x in inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=T + 3 * l, n=4))
+    out, lse = run_fwd(q, k, v, pattern, l, c)
+    res = {}
+    try:
+        for keys in (16, 32):
+            st_set_dkdv_keys_per_wave(keys)
+            res[keys] = [t.clone() for t in st_sparse_attn_bwd(q, k, v, out, lse, do, pattern, l, c)]
+            torch.cuda.synchronize()
+    finally:
+        st_set_dkdv_keys_per_wave(0)
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    for name, a, b in zip(("dq", "dk", "dv"), res[16], res[32]):
+        assert torch.equal(a.view(bits), b.view(bits)), f"{name}: 16 and 32 keys per wave differ"
+    qn, kn, vn, don = (f64(x) for x in (q, k, v, do))
+    rq, rk, rv = oracle.backward(qn, kn, vn, don, pattern, l, c)
+    dq, dk, dv = res[32]
+    assert_close(f64(dq), rq, dtype, "dq")
+    assert_close(f64(dk), rk, dtype, "dk")
+    assert_close(f64(dv), rv, dtype, "dv")
+
+
 GUARD_CASES = [
     # (pattern, dtype, D, T, l, c): ragged T; a strided T whose classes straddle 64-blocks;
     # a merged head; fp32
