@@ -50,6 +50,7 @@ _SIG = {
     "st_sparse_attn_fwd_ex": (_I, [_I] + [_P] * 5 + [_I] * 7 + [_P, _P]),
     "st_sparse_attn_bwd_ex": (_I, [_I] + [_P] * 9 + [_I] * 7 + [_P, _P]),
     "st_sparse_attn_bwd_noalloc": (_I, [_I] + [_P] * 9 + [_I] * 7 + [_P, _P]),
+    "st_set_fwd_rows_per_wave": (_I, [_I]),
     "st_set_dkdv_keys_per_wave": (_I, [_I]),
     "st_timing_enable": (_I, [_I]),
     "st_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
@@ -151,6 +152,11 @@ def st_release() -> None:
 
 
 KERNEL_NAMES = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv", "bwd_reduce", "bwd_delta")
+
+
+def st_set_fwd_rows_per_wave(rows: int) -> None:
+    """Shape of the 16-bit forward: 0 = chosen per launch, 16 or 32 = forced (results are identical)."""
+    _check("st_set_fwd_rows_per_wave", lib().st_set_fwd_rows_per_wave(int(rows)))
 
 
 def st_set_dkdv_keys_per_wave(keys: int) -> None:

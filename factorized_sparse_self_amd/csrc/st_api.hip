@@ -39,6 +39,15 @@ constexpr int64_t kDkdvSlots = 2048;
 // every launch (st_set_dkdv_keys_per_wave).
 std::atomic<int> g_dkdv_keys_per_wave{0};
 
+// Rows per wave of the 16-bit forward: 0 = by launch (16, the eight-wave
+// form, for launches of at most kFwdShortItems pair items, 32 otherwise), or
+// 16 / 32 for every launch (st_set_fwd_rows_per_wave).  kFwdShortItems is one
+// and a half rounds of the four-wave form on MI355X (256 CUs x 4 workgroups):
+// at that size or less the eight-wave form, three workgroups per CU, hides
+// more of each item's latency than it loses to its extra LDS reads.
+constexpr int kFwdShortItems = 1536;
+std::atomic<int> g_fwd_rows_per_wave{0};
+
 struct PlanKey {
   int device, pattern, T, l, c, B, H;
   std::vector<int32_t> summary;  // canonical summary set (empty: the last c offsets)
@@ -667,9 +676,11 @@ int attn_fwd(const char* fn, const void* q, const void* k, const void* v, void* 
     a.pairs = P.pair_items;
     const int n_items = k16 ? P.n_pair_items : P.n_row_items;
     if (plan->n_pass == 2) a.out_mode = p == 0 ? OUT_CARRY : OUT_MERGE;
-    e = D == 32 ? launch_fwd<TE, 32>(a, n_items, s)
-        : D == 64 ? launch_fwd<TE, 64>(a, n_items, s)
-                  : launch_fwd<TE, 128>(a, n_items, s);
+    const int rpw_set = g_fwd_rows_per_wave.load(std::memory_order_relaxed);
+    const int rpw = rpw_set ? rpw_set : n_items <= kFwdShortItems ? 16 : 32;
+    e = D == 32 ? launch_fwd<TE, 32>(a, n_items, rpw, s)
+        : D == 64 ? launch_fwd<TE, 64>(a, n_items, rpw, s)
+                  : launch_fwd<TE, 128>(a, n_items, rpw, s);
     if (e != hipSuccess) return hip_fail(fn, e);
   }
   if (plan->n_pass == 2) return workspace_done(device, s);
@@ -943,6 +954,15 @@ int st_sparse_attn_bwd_noalloc(int dtype, const void* q, const void* k, const vo
                              true);
     default: set_error(std::string(fn) + ": unknown dtype " + std::to_string(dtype)); return ST_ERR_INVALID;
   }
+}
+
+int st_set_fwd_rows_per_wave(int rows) {
+  if (rows != 0 && rows != 16 && rows != 32) {
+    set_error("st_set_fwd_rows_per_wave: rows must be 0, 16 or 32, got " + std::to_string(rows));
+    return ST_ERR_INVALID;
+  }
+  g_fwd_rows_per_wave.store(rows, std::memory_order_relaxed);
+  return ST_OK;
 }
 
 int st_set_dkdv_keys_per_wave(int keys) {

@@ -222,10 +222,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // 16-bit (bf16 or fp16) forward.
 //  * Work item = a pair of 64-row LUT blocks (128 kernel rows) of one head; it
-//    walks the union of the two blocks' key-block lists.  Waves 0-1 own the
-//    first block, waves 2-3 the second; a wave owns 32 rows as two MFMA
-//    groups of 16, which share every K and V operand read from LDS, and skips
-//    the key blocks its own row block does not visit.
+//    walks the union of the two blocks' key-block lists.  The first half of
+//    the waves own the first block, the second half the second; a wave owns
+//    GW MFMA groups of 16 rows (two in four-wave workgroups, which share every
+//    K and V operand read from LDS; one in eight-wave ones), and skips the key
+//    blocks its own row block does not visit.
 //  * K and V blocks are staged by direct global->LDS loads into a ring of NS
 //    LDS stages (st_stage.hpp): the loads of the next NS-1 blocks are in
 //    flight while a block is computed, and no registers hold them.  Padding
@@ -238,14 +239,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 //    when a logit exceeds it by more than 2^8 in exp2 units; blocks where no
 //    lane of the wave needs that skip the cross-lane max and the rescale.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int NS, int KC, bool M>
+template <typename E, int D, int NS, int KC, bool M, int GW>
 __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& item,
                                               unsigned char (*ring)[2][TileShape<D>::BYTES]) {
   using S = TileShape<D>;
   typedef typename Vec<E>::x8 V8;
   constexpr int NQ = D / 32;           // MFMA k-steps over D
   constexpr int ND = D / 16;           // 16-wide output column blocks
-  constexpr int PER_TILE = 2 * S::NI;  // loads per wave per block (K and V)
+  constexpr int NW = 8 / GW;  // waves: NW/2 per row block, 16*GW rows each
+  // staging: SW waves each stage SR rows of every tile (SNI instructions)
+  constexpr int SR = S::RPI <= kBlock / NW ? kBlock / NW : S::RPI;
+  constexpr int SW = kBlock / SR, SNI = SR / S::RPI;
+  constexpr int PER_TILE = 2 * SNI;  // loads per staging wave per block (K and V)
   const int pb = item.pb, bh = item.bh;
   const KindDev kd = load_uniform(&a.kinds[item.kind]);
   const GeoC<KC> g{kd.geo};
@@ -258,15 +263,19 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  // Waves 0-1 take row block 2pb, waves 2-3 row block 2pb+1; a wave owns 32
-  // rows, two MFMA groups of 16 (G = 0, 1) that share every K and V operand.
-  const int half = wave >> 1;
+  // The first NW/2 waves take row block 2pb, the others 2pb+1; a wave owns
+  // 16*GW rows, GW MFMA groups of 16 that share every K and V operand.
+  // (unsigned: a signed division here costs the four-wave form 10-16 VGPRs)
+  const unsigned uw = (unsigned)wave;
+  const int half = (int)(uw / (NW / 2));
   const int qb = 2 * pb + half;
-  const int r0 = (wave & 1) * 32;
-  int t[2], mlo[2];
-  uint32_t mspan[2];
+  const int r0 = (int)(uw % (NW / 2)) * 16 * GW;
+  const bool stager = uw % (NW / SW) == 0;
+  const int swave = (int)(uw / (NW / SW));
+  int t[GW], mlo[GW];
+  uint32_t mspan[GW];
 #pragma unroll
-  for (int G = 0; G < 2; ++G) {
+  for (int G = 0; G < GW; ++G) {
     const int r = r0 + 16 * G + li;
     t[G] = block_position(g, false, qb, r);
     int lo = 1, hi = 0;
@@ -283,27 +292,33 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
 #pragma unroll
   for (int d = 0; d < ND; ++d) t_off[d] = S::phys(4 * lg + (li >> 2), 2 * d + ((li & 3) >> 1)) + 8 * (li & 1);
 
-  V8 qop[2][NQ];  // the two groups' query rows as MFMA B operands (from LDS, first block)
-  f32x4 acc[2][ND];
+  V8 qop[GW][NQ];  // the groups' query rows as MFMA B operands (from LDS, first block)
+  f32x4 acc[GW][ND];
 #pragma unroll
-  for (int G = 0; G < 2; ++G)
+  for (int G = 0; G < GW; ++G)
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[G][d] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.sl2;
   const float headroom = 8.0f / sl2;  // raw-logit growth allowed before a rescale
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[GW], l_run[GW];
+#pragma unroll
+  for (int G = 0; G < GW; ++G) {
+    m_run[G] = -INFINITY;
+    l_run[G] = 0.f;
+  }
 
-  const StageRows<S::NI, S::RPI> stage(g, true, 16 * wave + lane / S::CH);
+  const StageRows<SNI, S::RPI> stage(g, true, SR * swave + lane / S::CH);
   const cptr<uint32_t> entries = as_const(kd.pair_entry);
   // LDS address of this wave's 16 staging rows in stage 0's K tile (V follows
   // at +BYTES, stage s at +s*STAGE)
   constexpr uint32_t STAGE = 2 * S::BYTES;
-  const uint32_t lds_rows = lds_address(&ring[0][0][16 * wave * S::RB]);
+  const uint32_t lds_rows = lds_address(&ring[0][0][SR * swave * S::RB]);
   auto issue = [&](uint32_t entry, int stg) {
-    int p[S::NI];
+    if (!stager) return;
+    int p[SNI];
     stage.positions(g, true, (int)(entry & kPairBlockMask), p);
-    stage_rows<D>(rk, lds_rows + stg * STAGE, 16 * wave, lane, p);
-    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, 16 * wave, lane, p);
+    stage_rows<D>(rk, lds_rows + stg * STAGE, SR * swave, lane, p);
+    stage_rows<D>(rv, lds_rows + stg * STAGE + S::BYTES, SR * swave, lane, p);
   };
 
   const int e0 = item.e0, e1 = item.e1;
@@ -311,13 +326,13 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
   // first iteration refills it: row block 2pb in the K tile, 2pb+1 in the V
   // tile), ahead of the first NS-1 key blocks, so every global load of the
   // loop is a ring DMA.
-  if (e0 < e1) {
-    const StageRows<S::NI, S::RPI> qstage(g, false, 16 * wave + lane / S::CH);
+  if (e0 < e1 && stager) {
+    const StageRows<SNI, S::RPI> qstage(g, false, SR * swave + lane / S::CH);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      int p[S::NI];
+      int p[SNI];
       qstage.positions(g, false, 2 * pb + hb, p);
-      stage_rows<D>(rq, lds_rows + (NS - 1) * STAGE + hb * S::BYTES, 16 * wave, lane, p);
+      stage_rows<D>(rq, lds_rows + (NS - 1) * STAGE + hb * S::BYTES, SR * swave, lane, p);
     }
   }
 #pragma unroll
@@ -333,7 +348,7 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
       // the wave's own rows, staged by all four waves: complete after the barrier
       const unsigned char* qt = ring[NS - 1][half] + r0 * S::RB;
 #pragma unroll
-      for (int G = 0; G < 2; ++G)
+      for (int G = 0; G < GW; ++G)
 #pragma unroll
         for (int k = 0; k < NQ; ++k) qop[G][k] = *(const V8*)(qt + 16 * G * S::RB + a_off[k]);
       // every wave's reads must land before any wave's DMA below refills
@@ -347,22 +362,23 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
     const unsigned char* Vt = ring[stg][1];
 
     // S^T = K Q^T for both groups: each K operand read serves two MFMAs
-    f32x4 sc[2][4];
+    f32x4 sc[GW][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      sc[0][b] = sc[1][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int G = 0; G < GW; ++G) sc[G][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NQ; ++k) {
         const V8 ka = *(const V8*)(Kt + 16 * b * S::RB + a_off[k]);
-        sc[0][b] = mfma16(ka, qop[0][k], sc[0][b]);
-        sc[1][b] = mfma16(ka, qop[1][k], sc[1][b]);
+#pragma unroll
+        for (int G = 0; G < GW; ++G) sc[G][b] = mfma16(ka, qop[G][k], sc[G][b]);
       }
     }
     if (!(hbits & kPairFull)) {
       // key k0 + 16b + 4lg + i is outside the row's run when
       // (unsigned)(key - mlo) > mspan
 #pragma unroll
-      for (int G = 0; G < 2; ++G) {
+      for (int G = 0; G < GW; ++G) {
         const int m0 = k0 + 4 * lg - mlo[G];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -371,17 +387,20 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
             if ((uint32_t)(m0 + 16 * b + i) > mspan[G]) sc[G][b][i] = -INFINITY;
       }
     }
-    float lm[2];
+    float lm[GW];
 #pragma unroll
-    for (int G = 0; G < 2; ++G) {
+    for (int G = 0; G < GW; ++G) {
       lm[G] = fmaxf(fmaxf(sc[G][0][0], sc[G][0][1]), fmaxf(sc[G][0][2], sc[G][0][3]));
 #pragma unroll
       for (int b = 1; b < 4; ++b)
         lm[G] = fmaxf(fmaxf(lm[G], fmaxf(sc[G][b][0], sc[G][b][1])), fmaxf(sc[G][b][2], sc[G][b][3]));
     }
-    if (wave_any(lm[0] > m_run[0] + headroom || lm[1] > m_run[1] + headroom)) {
+    bool need = lm[0] > m_run[0] + headroom;
 #pragma unroll
-      for (int G = 0; G < 2; ++G) {
+    for (int G = 1; G < GW; ++G) need = need || lm[G] > m_run[G] + headroom;
+    if (wave_any(need)) {
+#pragma unroll
+      for (int G = 0; G < GW; ++G) {
         const float mt = group4_max(lm[G]);
         const bool raise = mt > m_run[G] + headroom;
         // raising rows scale by exp2((old - new) max), 0 when the old max is
@@ -393,9 +412,9 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
         m_run[G] = raise ? mt : m_run[G];
       }
     }
-    V8 pb8[2][2];
+    V8 pb8[GW][2];
 #pragma unroll
-    for (int G = 0; G < 2; ++G) {
+    for (int G = 0; G < GW; ++G) {
       const float mb = (m_run[G] == -INFINITY) ? 0.f : m_run[G] * sl2;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -414,8 +433,8 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
       for (int d = 0; d < ND; ++d) {
         const unsigned char* r = Vt + 32 * kk * S::RB + t_off[d];
         const V8 av = concat(lds_read_tr<E>((const E*)r), lds_read_tr<E>((const E*)(r + 16 * S::RB)));
-        acc[0][d] = mfma16(av, pb8[0][kk], acc[0][d]);
-        acc[1][d] = mfma16(av, pb8[1][kk], acc[1][d]);
+#pragma unroll
+        for (int G = 0; G < GW; ++G) acc[G][d] = mfma16(av, pb8[G][kk], acc[G][d]);
       }
   }
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup ends
@@ -426,16 +445,16 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
     // second pass of a merged head first combines its rows with the carried
     // ones: softmax over both key sets, weights exp2(L_p - L) of the two
     // passes' outputs, L = log2(2^L0 + 2^L1) (a pass with no keys has L_p = -inf)
-    using Rows = RowStage<E, D, 32>;
-    static_assert(4 * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
+    using Rows = RowStage<E, D, 16 * GW>;
+    static_assert(NW * Rows::BYTES <= NS * 2 * S::BYTES, "row staging fits the ring");
     __syncthreads();
     Rows rows(&ring[0][0][0] + wave * Rows::BYTES);
 #pragma unroll
-    for (int G = 0; G < 2; ++G) {
+    for (int G = 0; G < GW; ++G) {
       const float lsum = group4_sum(l_run[G]);
       // the output is rounded to 16 bits, so the hardware reciprocal (1 ulp) suffices
       const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
-      const float lse2 = lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
+      const float lse2 = lsum > 0.f ? fmaf(m_run[G], sl2, fast_log2(lsum)) : -INFINITY;  // log2 units
       bool merged = false;
       if constexpr (M) merged = a.out_mode == OUT_MERGE;
       if (merged) {
@@ -456,7 +475,11 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
           for (int d = 0; d < ND; ++d) {
             const float4 c = *(const float4*)(C + 16 * d + 4 * lg);
             const f32x4 c4 = {c.x, c.y, c.z, c.w};
-            y[d] = c4 * s0 + acc[G][d] * s1;
+            // explicit fma: the same operations in every instantiation of
+            // the kernel (the compiler may contract a * b + c * d either way)
+            const f32x4 c0 = c4 * s0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[d][i] = fmaf(acc[G][d][i], s1, c0[i]);
           }
           if (lg == 0) a.lse[row] = (sw > 0.f ? mx + fast_log2(sw) : -INFINITY) * kLn2;
         }
@@ -477,11 +500,11 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
 
   // first pass of a merged head: keep the normalised fp32 output and lse
 #pragma unroll
-  for (int G = 0; G < 2; ++G) {
+  for (int G = 0; G < GW; ++G) {
     const float lsum = group4_sum(l_run[G]);
     if (t[G] < 0) continue;
     const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
-    const float lse2 = lsum > 0.f ? m_run[G] * sl2 + fast_log2(lsum) : -INFINITY;  // log2 units
+    const float lse2 = lsum > 0.f ? fmaf(m_run[G], sl2, fast_log2(lsum)) : -INFINITY;  // log2 units
     const size_t row = (size_t)bh * a.T + t[G];
     float* C = a.carry_o + row * D;
 #pragma unroll
@@ -499,27 +522,41 @@ __device__ __forceinline__ void fwd_b16_body(const FwdArgs& a, const PairItem& i
 // kind codes, and each workgroup branches once, uniformly, on its head's kind.
 // M: merged heads (the epilogue carries or merges; plain patterns compile
 // without those stores).
-template <typename E, int D, int NS, int C0, int C1, bool M>
-__global__ __launch_bounds__(kThreads) void fwd_b16_kernel(FwdArgs a) {
+// GW: 16-row groups per wave.  GW = 2: four waves, each two groups that share
+// every K and V operand read (about 120 VGPRs, four workgroups per CU).  GW =
+// 1: eight waves of one group (76 VGPRs; six waves per SIMD, three workgroups
+// per CU), twice the LDS reads per row but more waves to hide latency, which
+// pays in launches too short to fill the GPU more than once or twice.
+template <typename E, int D, int NS, int C0, int C1, bool M, int GW>
+__global__ __launch_bounds__(512 / GW) __attribute__((amdgpu_waves_per_eu(GW == 1 ? 6 : 1))) void fwd_b16_kernel(
+    FwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][TileShape<D>::BYTES];
   const PairItem item = load_uniform(&a.pairs[blockIdx.x]);
   if (item.pb < 0) return;  // schedule padding
   if (C0 == C1 || item.kind == 0)
-    fwd_b16_body<E, D, NS, C0, M>(a, item, ring);
+    fwd_b16_body<E, D, NS, C0, M, GW>(a, item, ring);
   else
-    fwd_b16_body<E, D, NS, C1, M>(a, item, ring);
+    fwd_b16_body<E, D, NS, C1, M, GW>(a, item, ring);
 }
 
 template <typename TE, int D>
-hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int n_items, int rows_per_wave, hipStream_t stream) {
   if (n_items == 0) return hipSuccess;
   timing_begin(KID_FWD, stream);
   hipError_t err;
   if constexpr (Is16<TE>::value) {
     err = with_kind_codes(a.pattern, [&](auto c0, auto c1, auto m) {
-      hipLaunchKernelGGL(
-          (fwd_b16_kernel<TE, D, kFwdStages, decltype(c0)::value, decltype(c1)::value, decltype(m)::value>),
-          dim3(n_items), dim3(kThreads), 0, stream, a);
+      constexpr int C0 = decltype(c0)::value, C1 = decltype(c1)::value;
+      constexpr bool M = decltype(m)::value;
+      if constexpr (D <= 64) {
+        if (rows_per_wave == 16) {
+          hipLaunchKernelGGL((fwd_b16_kernel<TE, D, kFwdStages, C0, C1, M, 1>), dim3(n_items), dim3(512), 0, stream,
+                             a);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((fwd_b16_kernel<TE, D, kFwdStages, C0, C1, M, 2>), dim3(n_items), dim3(kThreads), 0, stream,
+                         a);
       return hipGetLastError();
     });
   } else {
@@ -530,14 +567,14 @@ hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream) {
   return err;
 }
 
-template hipError_t launch_fwd<bf16, 32>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<bf16, 64>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<bf16, 128>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<f16, 32>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<f16, 64>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<f16, 128>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<float, 32>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<float, 64>(const FwdArgs&, int, hipStream_t);
-template hipError_t launch_fwd<float, 128>(const FwdArgs&, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 32>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 64>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<bf16, 128>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<f16, 32>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<f16, 64>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<f16, 128>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 32>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 64>(const FwdArgs&, int, int, hipStream_t);
+template hipError_t launch_fwd<float, 128>(const FwdArgs&, int, int, hipStream_t);
 
 }  // namespace st

@@ -139,8 +139,11 @@ extern const char* const kKernelNames[KID_COUNT];
 void timing_begin(int kid, hipStream_t stream);
 void timing_end(int kid, hipStream_t stream);
 
+// rows_per_wave: 16 selects the eight-wave forward (16-bit inputs, D <= 64
+// only); any other value, and every other case, the four-wave one (32 rows per
+// wave).
 template <typename TE, int D>
-hipError_t launch_fwd(const FwdArgs& a, int n_items, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int n_items, int rows_per_wave, hipStream_t stream);
 
 // The backward in two stages: Delta (fp32) and dq, then dk / dv and the
 // reduction of split key blocks, which read the Delta the first stage wrote.

@@ -251,17 +251,26 @@ int st_sparse_attn_bwd_f32(const void* q, const void* k, const void* v, const vo
                            int B, int H, int T, int D, int pattern, int l, int c, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Kernel shape (performance only; not part of the computation).  The 16-bit
- * dK/dV kernel at D <= 64 comes in two shapes: 16 keys per wave (four waves
- * per 64-key block) or 32 (two waves, each reading its Q and dO operands once
- * for two 16-key tiles).  Both sum every product in the same order, so dq, dk
- * and dv are bitwise identical under either.  keys = 0 (the default) picks
- * per launch: 32 where the dK/dV items far outnumber what the GPU holds at
- * once (full attention, very long sequences), 16 otherwise; 16 or 32 forces
- * that shape for every later backward call in the process (fp32 inputs and
- * D = 128 always use 16).  Other values give ST_ERR_INVALID.  Takes effect at
- * the next call; calls already enqueued are unaffected.
+ * Kernel shapes (performance only; not part of the computation).  Two 16-bit
+ * kernels at D <= 64 come in two shapes each, which compute every output
+ * element with the same operations in the same order, so the results are
+ * bitwise identical under either:
+ *   - the forward: 32 rows per wave (four waves per pair of 64-row blocks,
+ *     each reading its K and V operands once for two 16-row groups) or 16
+ *     (eight waves, more of them resident per CU);
+ *   - the dK/dV pass: 16 keys per wave (four waves per 64-key block) or 32
+ *     (two waves, each reading its Q and dO operands once for two 16-key
+ *     tiles).
+ * 0 (the default) picks per launch: the forward takes 16 rows per wave for
+ * launches of at most 1536 work items (too short to fill the GPU more than
+ * about one and a half times), 32 otherwise; dK/dV takes 32 keys per wave
+ * where its items far outnumber what the GPU holds at once (full attention,
+ * very long sequences), 16 otherwise.  16 or 32 forces that shape for every
+ * later call in the process (fp32 inputs and D = 128 always use the four-wave
+ * forward and 16 keys per wave).  Other values give ST_ERR_INVALID.  A setting
+ * takes effect at the next call; calls already enqueued are unaffected.
  * ------------------------------------------------------------------------- */
+int st_set_fwd_rows_per_wave(int rows);
 int st_set_dkdv_keys_per_wave(int keys);
 
 /* ---------------------------------------------------------------------------

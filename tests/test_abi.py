@@ -49,16 +49,21 @@ def test_status_strings_and_block_size():
     assert L.st_status_string(-2) == b"unsupported configuration"
 
 
-def test_dkdv_shape_setting_accepts_only_its_values():
-    from factorized_sparse_self_amd import StError, lib, st_set_dkdv_keys_per_wave
+def test_kernel_shape_settings_accept_only_their_values():
+    from factorized_sparse_self_amd import StError, lib, st_set_dkdv_keys_per_wave, st_set_fwd_rows_per_wave
     L = lib()
     for bad in (-1, 1, 8, 24, 64):
         assert L.st_set_dkdv_keys_per_wave(bad) == -1
         assert b"keys must be 0, 16 or 32" in L.st_last_error()
+        assert L.st_set_fwd_rows_per_wave(bad) == -1
+        assert b"rows must be 0, 16 or 32" in L.st_last_error()
     with pytest.raises(StError):
         st_set_dkdv_keys_per_wave(48)
+    with pytest.raises(StError):
+        st_set_fwd_rows_per_wave(48)
     for good in (16, 32, 0):
         st_set_dkdv_keys_per_wave(good)
+        st_set_fwd_rows_per_wave(good)
 
 
 def _call_fwd(name, ptr, B=1, H=2, T=64, D=64, pattern=0, l=8, c=0):

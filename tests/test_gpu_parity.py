@@ -428,6 +428,48 @@ def test_results_repeat_bit_for_bit(pattern):
         assert torch.equal(a.view(bits), o.view(bits)), f"{name}: call on another stream differs"
 
 
+FWD_SHAPE_CASES = [
+    # (pattern, dtype, D, B, H, T, l, c): ragged T, residue classes straddling 64-blocks at
+    # D = 32, merged heads (carry and merge passes), a general summary set, full attention;
+    # D = 128 and fp32 always take the four-wave forward
+    (inputs.FIXED, "bf16", 64, 2, 3, 1000, 96, 8),
+    (inputs.STRIDED, "bf16", 32, 1, 2, 395, 33, 0),
+    (inputs.FIXED_UNION, "bf16", 64, 1, 2, 333, 20, 4),
+    (inputs.STRIDED_UNION, "f16", 64, 2, 2, 700, 20, 0),
+    (inputs.FIXED_R1, "f16", 32, 1, 3, 900, 64, (1, 30, 63)),
+    (inputs.DENSE, "f16", 32, 1, 2, 300, 16, 0),
+    (inputs.FIXED, "bf16", 128, 1, 2, 500, 96, 8),
+    (inputs.STRIDED, "f32", 64, 1, 2, 300, 17, 0),
+]
+
+
+@pytest.mark.parametrize("case", FWD_SHAPE_CASES,
+                         ids=lambda c: f"{inputs.PATTERN_NAMES[c[0]]}_{c[1]}_D{c[2]}_T{c[5]}_l{c[6]}")
+def test_forward_kernel_shapes_agree_bit_for_bit(case):
+    """The forward's two shapes (16 or 32 rows per wave; the library picks 16 only for
+    short launches) compute every row with the same operations in the same order: forced
+    either way, out and lse are the same bits, and the 32-row result meets the oracle's
+    bound."""
+    from factorized_sparse_self_amd import st_set_fwd_rows_per_wave, st_sparse_attn_fwd
+    pattern, dtype, D, B, H, T, l, c = case
+    log(f"forward shapes {case}")
+    q, k, v = (x.cuda() for x in inputs.draw(B, H, T, D, dtype=TORCH_DTYPE[dtype], seed=2 * T + l, n=3))
+    res = {}
+    try:
+        for rows in (16, 32):
+            st_set_fwd_rows_per_wave(rows)
+            res[rows] = [t.clone() for t in st_sparse_attn_fwd(q, k, v, pattern, l, c)]
+            torch.cuda.synchronize()
+    finally:
+        st_set_fwd_rows_per_wave(0)
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(res[16][0].view(bits), res[32][0].view(bits)), "out: 16 and 32 rows per wave differ"
+    assert torch.equal(res[16][1].view(torch.int32), res[32][1].view(torch.int32)), "lse: the shapes differ"
+    O, L = oracle.forward(f64(q), f64(k), f64(v), pattern, l, c)
+    assert_close(f64(res[32][0]), O, dtype, "out")
+    assert_close(f64(res[32][1]), L, "f32", "lse")
+
+
 DKDV_SHAPE_CASES = [
     # (pattern, dtype, D, B, H, T, l, c): split summary columns (T > 24 row blocks), merged
     # heads (carry and merge passes), residue classes straddling 64-blocks at D = 32, a
