@@ -596,6 +596,54 @@ def test_two_streams_share_the_workspace_safely():
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} of call {i} differs"
 
 
+def test_calls_from_two_host_threads():
+    """Forward and backward called from two host threads at once, each on its own
+    stream and with its own problem, give the bits of the same calls made one after
+    the other (the library serialises its host state with a lock and orders its
+    shared workspace across the streams)."""
+    import threading
+
+    from factorized_sparse_self_amd import st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, T, D, l, c = 1, 8, 3000, 64, 64, 4
+    log(f"two threads: fixed B{B} H{H} T{T} D{D} l{l} c{c}")
+    problems = [tuple(x.cuda() for x in inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=s, n=4)) for s in (91, 92)]
+    torch.cuda.synchronize()
+
+    def run(p):
+        q, k, v, do = p
+        out, lse = st_sparse_attn_fwd(q, k, v, inputs.FIXED, l, c)
+        return [out, lse] + list(st_sparse_attn_bwd(q, k, v, out, lse, do, inputs.FIXED, l, c))
+
+    serial = [[t.clone() for t in run(p)] for p in problems]
+    torch.cuda.synchronize()
+    results = [[None] * 4 for _ in problems]
+    errors = []
+
+    def worker(i):
+        try:
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.default_stream())
+            with torch.cuda.stream(s_):
+                for rep in range(4):
+                    results[i][rep] = run(problems[i])
+            s_.synchronize()
+        except Exception as exc:  # reported in the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(problems))]
+    for t_ in threads:
+        t_.start()
+    for t_ in threads:
+        t_.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, reps in enumerate(results):
+        for rep, got in enumerate(reps):
+            for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), serial[i], got):
+                bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+                assert torch.equal(a.view(bits), b.view(bits)), f"{name} of thread {i}, call {rep} differs"
+
+
 class DeviceRows:
     """A GPU tensor [B, H, T, ...] seen by the oracle as an array: indexing [b, h, t] or
     [b, h, positions] copies only those rows to the host, as float64.  Lets the oracle
