@@ -53,3 +53,47 @@ def test_noalloc_refuses_what_it_cannot_hold():
     with pytest.raises(StError, match="static scratch holds"):
         st_sparse_attn_bwd_noalloc(big, big, big, big, lse_big, big, inputs.FIXED_UNION, 128, 8)
     torch.cuda.synchronize()
+
+
+def test_noalloc_backward_replays_in_a_graph():
+    """The callers the entry point is for: a HIP graph captures the forward and the
+    allocation-free backward once (plan cached and scratch looked up beforehand), and
+    every replay -- with new input values copied in, the outputs poisoned, and the
+    library's allocating and allocation-free calls run eagerly on other problems
+    between replays -- gives the bits of eager calls on the same values."""
+    B, H, T, D, l, c = 1, 4, 2048, 64, 128, 8
+    pattern = inputs.FIXED
+    print(f"graph replay: fixed B{B} H{H} T{T} D{D} l{l} c{c} bf16", flush=True)
+    sets = [tuple(x.cuda() for x in inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=s, n=4)) for s in (21, 22, 23)]
+    q, k, v, do = (x.clone() for x in sets[0])  # the graph's static inputs
+    out, lse = torch.empty_like(q), torch.empty(B, H, T, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    st_sparse_attn_fwd(q, k, v, pattern, l, c, out=out, lse=lse)
+    st_sparse_attn_bwd_noalloc(q, k, v, out, lse, do, pattern, l, c, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st_sparse_attn_fwd(q, k, v, pattern, l, c, out=out, lse=lse)
+        st_sparse_attn_bwd_noalloc(q, k, v, out, lse, do, pattern, l, c, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        src = sets[rep % 3]
+        for dst, x in zip((q, k, v, do), src):
+            dst.copy_(x)
+        for t in (out, lse, dq, dk, dv):
+            t.fill_(float("nan"))  # a replay that leaves anything unwritten fails
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (out, lse, dq, dk, dv)]
+        # eager work between replays: the allocating entry points on the same values
+        # (the reference), then an allocation-free call on other values, which leaves
+        # its own contents in the static scratch
+        e_out, e_lse = st_sparse_attn_fwd(*src[:3], pattern, l, c)
+        ref = [e_out, e_lse, *st_sparse_attn_bwd(*src[:3], e_out, e_lse, src[3], pattern, l, c)]
+        other = sets[(rep + 1) % 3]
+        o_out, o_lse = st_sparse_attn_fwd(*other[:3], pattern, l, c)
+        st_sparse_attn_bwd_noalloc(*other[:3], o_out, o_lse, other[3], pattern, l, c)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), ref, got):
+            bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+            assert torch.equal(a.view(bits), b.view(bits)), f"replay {rep}: {name} differs from eager calls"
