@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <set>
 #include <memory>
 #include <mutex>
 #include <string>
@@ -1019,6 +1020,15 @@ void st_release(void) {
   std::lock_guard<std::mutex> lock(g_mutex);
   int current = 0;
   const bool have_device = hipGetDevice(&current) == hipSuccess;
+  // kernels still queued may read a plan or the workspace: every device the
+  // library holds memory on finishes its work before anything is freed
+  if (have_device) {
+    std::set<int> devices;
+    for (const auto& kv : g_plans) devices.insert(kv.first.device);
+    for (const auto& kv : g_workspace) devices.insert(kv.first);
+    for (int d : devices)
+      if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
+  }
   for (auto& kv : g_plans) {
     if (have_device) (void)hipSetDevice(kv.first.device);
     kv.second.reset();

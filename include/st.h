@@ -292,7 +292,10 @@ void st_timing_reset(void);
 int st_block_size(void);                 /* block size of the LUTs (64)              */
 const char* st_status_string(int status); /* static text for a status code           */
 const char* st_last_error(void);         /* last failure message on this thread       */
-void st_release(void);                   /* free LUT caches and workspaces (all GPUs) */
+/* Free the LUT caches and workspaces on every GPU, after waiting for each GPU's
+ * queued work (a blocking call).  Later calls rebuild what they need.  It takes
+ * the library's lock, so calls from other host threads run before or after it. */
+void st_release(void);
 
 #ifdef __cplusplus
 }

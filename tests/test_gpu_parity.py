@@ -644,6 +644,45 @@ def test_calls_from_two_host_threads():
                 assert torch.equal(a.view(bits), b.view(bits)), f"{name} of thread {i}, call {rep} differs"
 
 
+def test_evicted_and_released_plans_rebuild_to_the_same_bits():
+    """More shapes than the plan cache holds (64), launched back to back without
+    waiting, so that plans are dropped while earlier calls' kernels may still be
+    queued; then the same calls again (their plans rebuilt), and again after
+    st_release() freed every plan and workspace.  Every repeat gives the first
+    pass's bits, and sampled problems agree with the oracle."""
+    from factorized_sparse_self_amd import st_release, st_sparse_attn_bwd, st_sparse_attn_fwd
+    B, H, D, l, c = 1, 2, 32, 16, 2
+    Ts = list(range(100, 100 + 3 * 80, 3))  # 80 distinct shapes
+    log(f"plan cache: fixed B{B} H{H} D{D} l{l} c{c}, {len(Ts)} lengths")
+    probs = [tuple(x.cuda() for x in inputs.draw(B, H, T, D, dtype=torch.bfloat16, seed=T, n=4)) for T in Ts]
+
+    def run_all(idx):
+        res = []
+        for i in idx:
+            q, k, v, do = probs[i]
+            out, lse = st_sparse_attn_fwd(q, k, v, inputs.FIXED, l, c)
+            res.append([out, lse, *st_sparse_attn_bwd(q, k, v, out, lse, do, inputs.FIXED, l, c)])
+        torch.cuda.synchronize()
+        return res
+
+    first = run_all(range(len(Ts)))
+    for i in (0, 37, len(Ts) - 1):
+        q, k, v, do = (f64(x) for x in probs[i])
+        O, L = oracle.forward(q, k, v, inputs.FIXED, l, c)
+        rq, rk, rv = oracle.backward(q, k, v, do, inputs.FIXED, l, c)
+        for name, got, ref, dt in zip(("out", "lse", "dq", "dk", "dv"), first[i], (O, L, rq, rk, rv),
+                                      ("bf16", "f32", "bf16", "bf16", "bf16")):
+            assert_close(f64(got), ref, dt, f"T={Ts[i]} {name}")
+    again = run_all(range(len(Ts)))
+    st_release()
+    after = run_all(range(0, len(Ts), 7))
+    for label, res, idx in (("rebuilt", again, range(len(Ts))), ("after release", after, range(0, len(Ts), 7))):
+        for r, i in zip(res, idx):
+            for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), first[i], r):
+                bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+                assert torch.equal(a.view(bits), b.view(bits)), f"{label}: T={Ts[i]} {name} differs"
+
+
 class DeviceRows:
     """A GPU tensor [B, H, T, ...] seen by the oracle as an array: indexing [b, h, t] or
     [b, h, positions] copies only those rows to the host, as float64.  Lets the oracle
