@@ -1,0 +1,68 @@
+"""The benchmark's work accounting (bench.accounting) against the oracle.
+
+The headline throughput is useful FLOP over step time, with the useful FLOP
+counted from the attended (query, key) pairs; the roofline divides
+algorithmic bytes, counted from the rows with a non-empty key set and the
+keys some query attends, by kernel time.  Here those counts are recomputed by
+enumerating the oracle's key sets (pattern definitions: llm-arch-kb "Sparse
+Transformer" §2 and the §3 mask sketch; nlp-lineage "The idea").  CPU only:
+the accounting reads the host-side layout builder of libst.so.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from factorized_sparse_self_amd import inputs
+
+
+def _passes(pattern):
+    """(oracle set part, bench kind) of each pass over a head of kind h mod 2."""
+    if pattern in (inputs.STRIDED_UNION, inputs.FIXED_UNION):
+        return lambda h: [0, 1]
+    return lambda h: [h % 2]
+
+
+def _sets(pattern, part, T, l, c):
+    return [oracle.part_key_set(pattern, part, t, T, l, c) for t in range(T)]
+
+
+@pytest.mark.parametrize("w", [w for w in inputs.WORKLOADS + inputs.EXTRA_WORKLOADS if w.T <= 65536],
+                         ids=lambda w: w.name)
+def test_useful_pairs_match_the_oracle(w):
+    acct = bench.accounting(w)
+    per_part = {}
+    total = 0
+    for h in range(w.H):
+        for part in _passes(w.pattern)(h):
+            if part not in per_part:
+                per_part[part] = sum(s.size for s in _sets(w.pattern, part, w.T, w.l, w.c))
+            total += per_part[part]
+    assert acct["pairs"] == w.B * total
+    assert acct["useful_flops"] == (14 if w.backward else 4) * w.D * w.B * total
+
+
+def _small(w, T):
+    return dataclasses.replace(w, T=T)
+
+
+@pytest.mark.parametrize("T", [1000, 1003])
+@pytest.mark.parametrize("w", inputs.WORKLOADS + inputs.EXTRA_WORKLOADS, ids=lambda w: w.name)
+def test_rows_and_keys_of_the_byte_count_match_the_oracle(w, T):
+    """bench.active_rows / attended_keys / second_pass_keys, the closed forms behind
+    the algorithmic bytes, against enumeration, at the workload's pattern, l and c."""
+    l = min(w.l, 200)
+    c = w.c if isinstance(w.c, int) else tuple(o for o in w.c if o < l)
+    for part in (0, 1):
+        S = _sets(w.pattern, part, T, l, c)
+        rows = sum(1 for s in S if s.size)
+        keys = np.unique(np.concatenate([s for s in S if s.size])).size if rows else 0
+        assert bench.active_rows(w.pattern, part, T, l, c) == rows, (part, "rows")
+        assert bench.attended_keys(w.pattern, part, T, l, c) == keys, (part, "keys")
+        if w.pattern in (inputs.STRIDED_UNION, inputs.FIXED_UNION) and part == 1:
+            # the keys the second pass holds (whose first-pass gradients are carried):
+            # every position its kernel key map covers, attended in that pass or not
+            _, key_pos = oracle.kernel_maps(w.pattern, 1, T, l, c, 64)
+            assert bench.second_pass_keys(w.pattern, T, l, c) == int((key_pos >= 0).sum())
