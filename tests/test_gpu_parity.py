@@ -273,12 +273,20 @@ def test_small_head_dim_128(case, dtype):
 
 
 def test_edge_shapes():
-    """T = 1, T < l, l = 1, c = l, a single row block, odd H."""
+    """T = 1 (every pattern, every head dimension), T < l, l = 1, c = l, a single row
+    block and one more row, odd H."""
     cases = [
         (inputs.STRIDED, 1, 2, 1, 64, 4, 0), (inputs.FIXED, 1, 2, 1, 64, 4, 2),
         (inputs.STRIDED, 1, 3, 10, 64, 16, 0), (inputs.FIXED, 1, 3, 10, 64, 16, 3),
         (inputs.STRIDED, 2, 2, 70, 32, 1, 0), (inputs.FIXED, 1, 2, 70, 64, 1, 1),
         (inputs.FIXED, 1, 5, 130, 64, 8, 8), (inputs.DENSE, 1, 1, 65, 64, 1, 0),
+        # every pattern at T = 1, and the other head dimensions at T = 1 and at one block plus one row
+        (inputs.FIXED_R1, 1, 2, 1, 64, 4, 2), (inputs.DENSE, 1, 2, 1, 64, 4, 0),
+        (inputs.STRIDED_UNION, 1, 2, 1, 64, 4, 0), (inputs.FIXED_UNION, 1, 2, 1, 64, 4, 2),
+        (inputs.STRIDED, 1, 2, 1, 32, 4, 0), (inputs.FIXED, 1, 2, 1, 128, 4, 2),
+        (inputs.FIXED_R1, 1, 3, 65, 32, 16, 16), (inputs.STRIDED, 1, 2, 65, 128, 8, 0),
+        # l larger than T for the merged heads (the second pass of the fixed head attends nothing)
+        (inputs.FIXED_UNION, 1, 2, 40, 64, 64, 4), (inputs.STRIDED_UNION, 1, 2, 40, 64, 64, 0),
     ]
     for dtype in ("bf16", "f16", "f32"):
         tdt = TORCH_DTYPE[dtype]
