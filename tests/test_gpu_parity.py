@@ -365,6 +365,31 @@ def test_random_shapes(case):
     _check_random(case)
 
 
+def _random_medium_cases(n, seed):
+    """n seeded random problems between the small sweep and the split-column lengths
+    (T from 420 to 2100), every pattern, dtype and head dimension."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        pattern = int(rng.integers(0, 6))
+        dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
+        D = [32, 64, 128][int(rng.integers(0, 3))]
+        T = int(rng.integers(420, 2100))
+        l = int(rng.integers(1, 300))
+        c = 0
+        if pattern in (inputs.FIXED, inputs.FIXED_R1, inputs.FIXED_UNION):
+            c = int(rng.integers(1, l + 1))
+        cases.append((pattern, 1, int(rng.integers(1, 4)), T, D, l, c, dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_medium_cases(30, 2718),
+                         ids=lambda c: f"p{c[0]}_H{c[2]}T{c[3]}D{c[4]}l{c[5]}c{c[6]}_{c[7]}")
+def test_random_medium_shapes(case):
+    """As test_random_shapes, at lengths of several to thirty row-block pairs."""
+    _check_random(case)
+
+
 def _check_random(case):
     pattern, B, H, T, D, l, c, dtype = case
     log(f"random shape {case}")
