@@ -66,3 +66,16 @@ def test_rows_and_keys_of_the_byte_count_match_the_oracle(w, T):
             # every position its kernel key map covers, attended in that pass or not
             _, key_pos = oracle.kernel_maps(w.pattern, 1, T, l, c, 64)
             assert bench.second_pass_keys(w.pattern, T, l, c) == int((key_pos >= 0).sum())
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with a message saying so
+    (checked before anything touches a GPU)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus must be 1" in r.stderr
